@@ -1,0 +1,206 @@
+"""Benchmark: chunked GRPO log-prob + loss forward/backward on one MI355X.
+
+A step is one pass of the whole path over one synthetic batch: group advantages,
+then grpo_loss_fwd_bwd (token index, target logits, per chunk the logits GEMM with
+online log-sum-exp, the merge with the GRPO per-token terms, the recompute GEMM
+writing probabilities and the dH GEMM; finally the fp64 loss sum).  Inputs are
+resident in HBM before the timed region.  The default workload is the
+Qwen3-8B-shaped long-context stream (D=4096, V=151936, 2 x 55000 tokens,
+chunks of 8192 tokens).
+
+Prints one JSON line: whole-step tokens/s, the roofline of the dominant kernel
+(algorithmic flops over its event-timed launches inside the timed region) and the
+fp64 oracle timed on the host cores on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "GRPO logp+loss fwd+bwd tokens/s at 1 GPU; % of bf16 MFMA peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--chunk", type=int, default=0, help="override the workload's chunk tokens")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (for HBM counter scaling)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
+
+
+def cpu_baseline(case, n_tokens):
+    """The fp64 oracle, as it stands, on the first n_tokens tokens of the workload."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    n = min(n_tokens, case.T)
+    H = oracle.widen(case.H[:n], case.dtype)
+    W = oracle.widen(case.W, case.dtype)
+    y = case.targets[:n]
+    cu = np.array([0, n], dtype=np.int64)
+    old = np.zeros(n)
+    ref = np.zeros(n)
+    adv = np.array([1.0])
+    t0 = time.perf_counter()
+    oracle.grpo_loss_and_grad(H, W, y, cu, np.ones(n, np.uint8), old, ref, adv)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {n} tokens of the workload, full fwd+bwd (logp, loss, dH) in fp64 numpy; "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this path runs on a single MI355X and has no multi-GPU mode "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    from rl_fine_tuning_amd import Timer, grpo_advantages, grpo_logp_fwd, grpo_loss_fwd_bwd, grpo_workspace_bytes
+    from synth import CONFIGS, make_config
+
+    cfg = args.config
+    spec = CONFIGS[cfg]
+    t_gen = time.perf_counter()
+    case = make_config(cfg)
+    C = args.chunk or case.chunk
+    T, D, V, S, G = case.T, case.D, case.V, case.S, case.G
+    log(f"config {cfg}: T={T} D={D} V={V} S={S} chunk={C}; inputs drawn in {time.perf_counter() - t_gen:.1f} s")
+    dev = torch.device("cuda:0")
+    if case.dtype == "bf16":
+        mat = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        mat = lambda x: torch.from_numpy(x).to(dev)
+    H, W = mat(case.H), mat(case.W)
+    targets = torch.from_numpy(case.targets).to(dev)
+    rewards = torch.from_numpy(case.rewards).to(dev)
+    # old / reference policy log-probs: the current policy's logp plus the workload's noise
+    # (input preparation, outside the timed region)
+    logp0 = grpo_logp_fwd(H, W, targets, C)
+    old = (logp0.double() + torch.from_numpy(case.noise_old).to(dev)).float()
+    ref = (logp0.double() + torch.from_numpy(case.noise_ref).to(dev)).float()
+    del logp0
+    ws_bytes = grpo_workspace_bytes(T, D, V, C, 0 if case.dtype == "bf16" else 1, num_seqs=S)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    dH = torch.empty_like(H)
+    adv = torch.empty(S, dtype=torch.float32, device=dev)
+    cu = case.cu
+
+    def step(timer=None):
+        grpo_advantages(rewards, G, out=adv)
+        return grpo_loss_fwd_bwd(H, W, targets, cu, old, ref, adv, C, dH=dH, workspace=ws, timer=timer,
+                                 want_logp=False, want_token_loss=False)
+
+    torch.cuda.synchronize()
+    base_mem = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+    timer = Timer(16384)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        out = step(timer)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    log(f"timed {args.steps} steps in {elapsed:.3f} s")
+    peak_extra = torch.cuda.max_memory_allocated() - base_mem
+    loss = float(out["loss"].cpu()[0])
+
+    ms_step = 1e3 * elapsed / args.steps
+    tokens_per_s = T * args.steps / elapsed
+    flops_step = 6.0 * T * D * V
+    nchunks = (T + C - 1) // C
+    rows = [min(C, T - k * C) for k in range(nchunks)]
+    gemm_flops = {"logits_lse": sum(2.0 * r * D * V for r in rows),
+                  "probs": sum(2.0 * r * D * V for r in rows),
+                  "dh_gemm": sum(2.0 * r * D * V for r in rows)}
+    kernels = {}
+    for k in ("target_logit", "logits_lse", "merge", "probs", "dh_gemm", "dh_reduce", "token_index",
+              "loss_finalize"):
+        ms, n, dropped = timer.read(k)
+        kernels[k] = {"ms_total": ms, "launches": n}
+    dominant = max(gemm_flops, key=lambda k: kernels[k]["ms_total"])
+    dk = kernels[dominant]
+    achieved = gemm_flops[dominant] * args.steps / (dk["ms_total"] * 1e-3) / 1e12
+    for k in gemm_flops:
+        kk = kernels[k]
+        kk["tflops"] = gemm_flops[k] * args.steps / (kk["ms_total"] * 1e-3) / 1e12 if kk["ms_total"] else None
+    result = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if case.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": spec["workload"], "T": T, "D": D, "V": V, "chunk_tokens": C,
+                   "sequences": S, "group_size": G},
+        "mfma_frac_step": flops_step / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+        "roofline": {"bound": "mfma", "kernel": dominant, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "avg_launch_ms": dk["ms_total"] / max(1, dk["launches"]),
+                     "flops_per_launch_avg": gemm_flops[dominant] / nchunks},
+        "kernels": kernels,
+        "workspace_bytes": ws_bytes,
+        "peak_extra_bytes": peak_extra,
+        "loss": loss,
+    }
+    timer.close()
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on the host")
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_sample_tokens)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,190 @@
+/*
+ * grpo.h - C ABI of the MI355X (gfx950) chunked GRPO log-probability and loss library.
+ *
+ * The library computes, from a model's final hidden states H[T, D] and the lm_head
+ * weight W[V, D], the per-token log-probability of each target token, the GRPO
+ * per-token objective and its gradient with respect to H, chunk by chunk over the
+ * flattened token stream, so that the [T, V] logit tensor never exists in memory.
+ *
+ * Sources (page titles as printed on the pages):
+ *  [P4] "Reinforcement Learning GRPO mit 7x laengerem Kontext" (Unsloth docs):
+ *       section "Chunking der abgeflachten Sequenzlaenge" (Eq. 1-3: the batch and
+ *       context axes are flattened and cut into chunks, logit memory bounded by one
+ *       chunk), the call of chunked_hidden_states_selective_log_softmax (hidden
+ *       states, lm_head, completion ids, temperature; chunked logits upcast to
+ *       float32), and section "Auslagern von Aktivierungen fuer Log-Softmax" (the
+ *       forward keeps no logits; the backward recomputes the chunk and
+ *       back-propagates the incoming gradient).
+ *  [P2] "Unsloth internals", section "The relationship to TRL": group-relative
+ *       advantages, clipped surrogate objective, KL-to-reference term.
+ *  [P3] "You can now train reasoning models with 5GB VRAM thanks to Unsloth",
+ *       section "Under the Hood": reverse KL; ratio exp(q - q_old) times the
+ *       advantage broadcast over the tokens of a sequence.
+ *  [P1] "Unsloth GRPO Implementation: How It Accelerates Reinforcement Learning
+ *       Training", section "Corrected Hyperparameters for GRPO Stability":
+ *       beta = 0.001.
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers are device pointers unless marked [host].  `stream` is a
+ *    hipStream_t passed as void* (NULL = the null stream).  Every call only
+ *    enqueues work on `stream`; none synchronizes the host (except the timer
+ *    read-out), none allocates device memory, and none keeps a pointer after it
+ *    returns.  The caller owns every buffer, including the workspace.
+ *  - Row-major layouts: H[T, D], W[V, D] (the nn.Linear [out, in] layout), dH[T, D].
+ *    Row t of H predicts targets[t]; the caller applies any causal shift.
+ *  - Sequences are contiguous runs of the flattened stream given by cu_seqlens;
+ *    groups are consecutive runs of `group_size` sequences (prompt-major).
+ *  - Every host-checkable error is reported before anything is enqueued and leaves
+ *    every output untouched.  A failed launch returns GRPO_E_HIP.
+ *  - A target outside [0, V) yields NaN logp / token_loss for that token (and a
+ *    NaN loss if its weight is non-zero), a zero dH row, and no out-of-bounds access.
+ *  - Calls keep no global state and may run concurrently on different streams with
+ *    different workspaces.
+ */
+#ifndef GRPO_MI355X_H
+#define GRPO_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GRPO_OK = 0,
+  GRPO_E_NULL = 1,        /* a required pointer is NULL */
+  GRPO_E_SHAPE = 2,       /* a size is out of range or cu_seqlens is inconsistent */
+  GRPO_E_VALUE = 3,       /* a scalar is out of range or not finite */
+  GRPO_E_WORKSPACE = 4,   /* workspace missing, too small or misaligned */
+  GRPO_E_UNSUPPORTED = 5, /* dtype, alignment or divisibility this build does not handle */
+  GRPO_E_HIP = 6          /* the HIP runtime reported an error */
+} grpo_status;
+
+typedef enum { GRPO_BF16 = 0, GRPO_F32 = 1 } grpo_dtype;            /* element type of H, W, dH */
+typedef enum { GRPO_AGG_SEQ_MEAN = 0, GRPO_AGG_TOKEN_MEAN = 1 } grpo_agg;
+typedef enum { GRPO_STD_UNBIASED = 0, GRPO_STD_POPULATION = 1 } grpo_std;
+
+/* Problem shape.  T >= 0 tokens, D >= 1 hidden size (multiple of 8 for bf16, of 4 for
+ * fp32), V >= 1 vocabulary size, chunk_tokens >= 1 tokens per chunk.  T, V and
+ * chunk_tokens are below 2^31.  temperature > 0 and finite: logits are
+ * (H . W[v]) / temperature ([P4], call arguments). */
+typedef struct {
+  int64_t T;
+  int64_t D;
+  int64_t V;
+  int64_t chunk_tokens;
+  int32_t dtype;       /* grpo_dtype */
+  float temperature;
+} grpo_shape;
+
+/* GRPO objective parameters ([P2], [P3], [P1]).  The ratio is clipped to
+ * [1 - clip_eps_low, 1 + clip_eps_high]; 0 <= clip_eps_low < 1, clip_eps_high >= 0;
+ * beta >= 0 weights the k3 reverse-KL term; agg is a grpo_agg. */
+typedef struct {
+  float clip_eps_low;
+  float clip_eps_high;
+  float beta;
+  int32_t agg;
+} grpo_loss_params;
+
+/* Kernel classes that a grpo_timer can time (events around each launch). */
+typedef enum {
+  GRPO_K_TARGET_LOGIT = 0, /* z[t, y_t] by a row dot product */
+  GRPO_K_LOGITS_LSE = 1,   /* MFMA logits GEMM with online max / sum-exp epilogue */
+  GRPO_K_MERGE = 2,        /* merge of the vocabulary tiles' partials; GRPO per-token terms */
+  GRPO_K_PROBS = 3,        /* recompute GEMM writing softmax probabilities */
+  GRPO_K_DH_GEMM = 4,      /* MFMA GEMM dH = (g/tau) (W[y] - P W) */
+  GRPO_K_DH_REDUCE = 5,    /* fixed-order sum of split-vocabulary dH partials */
+  GRPO_K_TOKEN_INDEX = 6,  /* sequence index, per-sequence token counts and weights */
+  GRPO_K_LOSS_FINALIZE = 7,/* fixed-order fp64 sum of the per-token loss terms */
+  GRPO_K_ADVANTAGES = 8,
+  GRPO_K_COUNT = 9
+} grpo_kernel_id;
+
+typedef struct grpo_timer grpo_timer; /* opaque, owned by the caller */
+
+/* Bytes of workspace that grpo_logp_fwd (with_backward = 0) or grpo_loss_fwd_bwd
+ * (with_backward = 1) needs for this shape and num_seqs sequences.  Returns 0 for an
+ * invalid shape.  Bounded by chunk_tokens * V * 4 (one chunk's fp32 logits) plus
+ * O(T + chunk_tokens * (V / 256 + D)) bytes of per-token state. */
+size_t grpo_workspace_bytes(const grpo_shape* shape, int64_t num_seqs, int with_backward);
+
+/* Per-token log-probabilities of the targets ([P4]: chunked hidden-state selective
+ * log-softmax): logp[t] = z[t, y_t] - logsumexp_v z[t, v], z = H W^T / temperature,
+ * fp32 accumulation of bf16 (or fp32) products.
+ *   H [T, D], W [V, D] of shape->dtype, 16-byte aligned; targets int32 [T];
+ *   logp fp32 [T] (written); lse fp32 [T] (written when not NULL);
+ *   workspace of grpo_workspace_bytes(shape, 1, 0) bytes, 256-byte aligned;
+ *   timer may be NULL.
+ * logp is bitwise independent of chunk_tokens and equal to the logp that
+ * grpo_loss_fwd_bwd computes for the same inputs. */
+grpo_status grpo_logp_fwd(const grpo_shape* shape, const void* H, const void* W,
+                          const int32_t* targets, float* logp, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream, grpo_timer* timer);
+
+/* Group-relative advantages ([P2]): for group k = sequences [k G, (k + 1) G),
+ * adv[i] = (r_i - mean) / (std + eps), std unbiased or population per std_mode;
+ * a group of size 1, or whose rewards are all equal, gets 0.  Computed in fp64.
+ *   rewards fp32 [num_seqs]; adv fp32 [num_seqs] (written).
+ * num_seqs must be a positive multiple of group_size; eps >= 0 and finite. */
+grpo_status grpo_advantages(const float* rewards, int64_t num_seqs, int64_t group_size,
+                            int32_t std_mode, float eps, float* adv, void* stream);
+
+/* GRPO loss over the flattened stream and its gradient with respect to H
+ * ([P2], [P3], [P4] "Auslagern von Aktivierungen fuer Log-Softmax"):
+ *   rho_t  = exp(logp_t - old_logp_t)
+ *   surr_t = min(rho_t A_s(t), clip(rho_t, 1 - eps_low, 1 + eps_high) A_s(t))
+ *   d_t    = ref_logp_t - logp_t,  k3_t = exp(d_t) - d_t - 1
+ *   l_t    = -(surr_t - beta k3_t)
+ *   loss   = sum_t w_t l_t   with w_t = mask_t / (S * L_s(t)) (seq mean; L_i = unmasked
+ *            tokens of sequence i) or w_t = mask_t / sum(mask) (token mean)
+ *   dH_t   = (g_t / temperature) (W[y_t] - sum_v softmax(z_t)_v W[v]),
+ *            g_t = w_t (-(rho A if rho A <= clip(rho) A else 0) + beta (1 - exp(d_t)))
+ * Arguments:
+ *   cu_seqlens [host] int32 [num_seqs + 1]: cu[0] = 0, non-decreasing, cu[S] = T.
+ *   mask uint8 [T] (NULL = every token counts); old_logp, ref_logp fp32 [T]
+ *   (ref_logp may be NULL only when beta == 0); adv fp32 [num_seqs].
+ *   loss fp64 [1] (written); logp, token_loss fp32 [T] (written when not NULL;
+ *   token_loss holds l_t, unweighted); dH [T, D] of shape->dtype (overwritten;
+ *   masked tokens get +0 rows); workspace of grpo_workspace_bytes(shape, S, 1) bytes.
+ * The loss is summed in fp64 in a fixed token order, so it is bitwise independent
+ * of chunk_tokens, as are logp and token_loss. */
+grpo_status grpo_loss_fwd_bwd(const grpo_shape* shape, const grpo_loss_params* params,
+                              const void* H, const void* W, const int32_t* targets,
+                              const int32_t* cu_seqlens, int64_t num_seqs, const uint8_t* mask,
+                              const float* old_logp, const float* ref_logp, const float* adv,
+                              double* loss, float* logp, float* token_loss, void* dH,
+                              void* workspace, size_t workspace_bytes, void* stream,
+                              grpo_timer* timer);
+
+/* Human-readable name of a status code (static storage). */
+const char* grpo_status_string(grpo_status status);
+
+/* Test hook: the per-token sequence id, chunk id (t / chunk_tokens) and position within
+ * the sequence, exactly as the loss kernels derive them.  cu_seqlens [host] as for
+ * grpo_loss_fwd_bwd; seq_id, chunk_id, pos int32 [T] device outputs; the workspace
+ * needs (num_seqs + 1) * 4 bytes rounded up to 256. */
+grpo_status grpo_debug_token_index(const int32_t* cu_seqlens, int64_t num_seqs, int64_t T,
+                                   int64_t chunk_tokens, int32_t* seq_id, int32_t* chunk_id,
+                                   int32_t* pos, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/* Kernel timing for measurement.  A timer holds `capacity` event pairs; a call that
+ * receives a timer records an event pair around every kernel launch it makes until
+ * the timer is full (launches beyond capacity are counted in `dropped`).
+ * grpo_timer_read waits for the recorded events and returns the summed duration and
+ * launch count of one kernel class.  Timers are not thread-safe. */
+grpo_status grpo_timer_create(int32_t capacity, grpo_timer** out);
+grpo_status grpo_timer_destroy(grpo_timer* timer);
+grpo_status grpo_timer_reset(grpo_timer* timer);
+grpo_status grpo_timer_read(grpo_timer* timer, int32_t kernel_id, double* total_ms,
+                            int64_t* launches, int64_t* dropped);
+
+/* Library version string. */
+const char* grpo_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GRPO_MI355X_H */

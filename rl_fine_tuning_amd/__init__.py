@@ -1,0 +1,17 @@
+"""Chunked GRPO log-probabilities, loss and dL/dH on MI355X (gfx950).
+
+The computation lives in the HIP library built from ``csrc/`` (C ABI in
+include/grpo.h); ``grpo`` is its thin ctypes binding.
+"""
+from .grpo import (  # noqa: F401
+    GRPO_BF16,
+    GRPO_F32,
+    GrpoError,
+    Timer,
+    grpo_advantages,
+    grpo_debug_token_index,
+    grpo_logp_fwd,
+    grpo_loss_fwd_bwd,
+    grpo_workspace_bytes,
+    lib,
+)

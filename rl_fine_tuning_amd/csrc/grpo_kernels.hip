@@ -1,0 +1,1122 @@
+// gfx950 (MI355X) kernels and C-ABI entry points of the chunked GRPO path.
+//
+// What is computed follows the Unsloth pages:
+//  * "Reinforcement Learning GRPO mit 7x laengerem Kontext" (Unsloth docs), the call of
+//    chunked_hidden_states_selective_log_softmax: logits = hidden states x lm_head over
+//    a chunk of the flattened token stream, upcast to fp32, divided by the temperature,
+//    log-softmaxed and gathered at the target id; section "Auslagern von Aktivierungen
+//    fuer Log-Softmax": nothing but log-probabilities is kept from the forward and the
+//    backward recomputes the chunk's logits.
+//  * "Unsloth internals", section "The relationship to TRL": group-relative advantages,
+//    clipped surrogate, KL-to-reference term; "You can now train reasoning models with
+//    5GB VRAM thanks to Unsloth", section "Under the Hood": reverse KL, ratio
+//    exp(logp - old_logp) times the sequence's advantage.
+//
+// How it is laid out on the chip (not from the pages):
+//  * One GEMM kernel template, 256 threads (4 waves of 64), one 256 x 256 output tile
+//    per workgroup, v_mfma_f32_32x32x16_bf16 (v_mfma_f32_32x32x2f32 for fp32 inputs),
+//    each wave a 128 x 128 sub-tile held as 4 x 4 accumulator blocks in AGPRs.  K is
+//    staged through LDS in 128-byte rows (64 bf16 / 32 fp32), double buffered, with an
+//    XOR swizzle of the 16-byte chunks so that operand reads and staging writes avoid
+//    bank conflicts.
+//  * The logits GEMMs put the vocabulary on the MFMA row axis and tokens on the column
+//    axis, so a lane holds 64 vocabulary entries of 4 tokens: the per-token max and
+//    sum-exp need only in-lane work plus one cross-lane step, and probability rows are
+//    written as 4-element vectors.
+//  * The dH GEMM computes dH^T tiles (hidden x tokens) with K = vocabulary.  W [V, D] is
+//    read as its transpose by loading 8 x 8 blocks and transposing them in registers on
+//    the way into LDS, so no transposed copy of W is ever stored.
+//  * Workgroups are dispatched round-robin over the 8 XCDs; the tile map gives each XCD
+//    a contiguous share of one tile axis and walks the other in small groups, so the
+//    workgroups that run together on one XCD share operand tiles in its L2.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <type_traits>
+#include <vector>
+
+#include "grpo.h"
+#include "grpo_plan.h"
+
+struct grpo_timer {
+  int32_t capacity = 0;
+  int32_t used = 0;
+  int64_t dropped = 0;
+  std::vector<hipEvent_t> start, stop;
+  std::vector<int32_t> kid;
+};
+
+namespace grpo {
+namespace {
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kThreads = 256;
+constexpr int kRowBytes = 128;                   // one LDS tile row: 8 chunks of 16 bytes
+constexpr int kTileBytes = kTile * kRowBytes;    // one operand, one stage: 32 KB
+constexpr float kLog2e = 1.4426950408889634f;
+
+enum Kind { KIND_LSE = 0, KIND_PROBS = 1, KIND_DH = 2 };
+
+// Byte offset of 16-byte chunk c of row r inside a [256 rows x 8 chunks] LDS tile.
+__device__ __forceinline__ int lds_off(int r, int c) {
+  return r * kRowBytes + ((c ^ ((r & 7) ^ ((r >> 3) & 7))) << 4);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  __bf16 x = (__bf16)a, y = (__bf16)b;  // round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+__device__ __forceinline__ uint32_t u4get(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// Zero the elements [n, 16 / sizeof(T)) of a 16-byte chunk.
+template <typename T>
+__device__ __forceinline__ uint4 keep_first(uint4 x, int n) {
+  uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  if (sizeof(T) == 2) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (e >= n) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (e >= n) w[e] = 0;
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+struct GemmArgs {
+  const void* a;      // LSE / PROBS: W [V, D].  DH: W [V, D], read transposed
+  const void* b;      // LSE / PROBS: hidden-state chunk [rows, D].  DH: probabilities [rows, ldp]
+  int64_t lda, ldb;   // row strides (elements)
+  int a_rows;         // rows of the MFMA A operand: V (LSE / PROBS) or D (DH)
+  int b_rows;         // tokens in the chunk
+  int K;              // reduction length: D (LSE / PROBS) or V (DH)
+  int k_len;          // DH: vocabulary entries per split; otherwise K
+  int tiles_a_base;   // A tiles before the split factor
+  int tiles_a, tiles_b;
+  int xcd_axis;       // 0: tiles_a are shared out over XCDs; 1: tiles_b
+  int group_b;        // B tiles walked together
+  float inv_tau;
+  // LSE outputs: [tiles_a][b_rows]
+  float* pm;
+  float* ps;
+  // PROBS
+  const float* lse;   // [b_rows], chunk-local
+  void* p;            // [b_rows, ldp]
+  int64_t ldp;
+  int V;
+  // DH
+  const float* g;         // [b_rows]
+  const int32_t* targets; // [b_rows]
+  const void* w;          // W, for the W[y] term
+  void* dh;               // [b_rows, D] (ksplit == 1)
+  float* part;            // [ksplit][b_rows][D] (ksplit > 1)
+  int D;
+  int ksplit;
+};
+
+// Tile of this workgroup.  Workgroup i runs on XCD i % 8; each XCD owns a contiguous
+// share of one tile axis and walks the other axis group_b tiles at a time.
+__device__ __forceinline__ bool map_tile(const GemmArgs& g, int& ta, int& tb) {
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7;
+  const int local = bid >> 3;
+  int a_lo = 0, na = g.tiles_a, b_lo = 0, nb = g.tiles_b;
+  if (g.xcd_axis == 0) {
+    a_lo = (int)((int64_t)xcd * g.tiles_a / 8);
+    na = (int)((int64_t)(xcd + 1) * g.tiles_a / 8) - a_lo;
+  } else {
+    b_lo = (int)((int64_t)xcd * g.tiles_b / 8);
+    nb = (int)((int64_t)(xcd + 1) * g.tiles_b / 8) - b_lo;
+  }
+  if (local >= na * nb) return false;
+  const int gsz = g.group_b * na;
+  const int grp = local / gsz;
+  const int r = local - grp * gsz;
+  const int gb = min(g.group_b, nb - grp * g.group_b);
+  ta = a_lo + r / gb;
+  tb = b_lo + grp * g.group_b + r % gb;
+  return true;
+}
+
+// Row-major operand, k contiguous: rows [row0, row0 + 256), k in [k0, k0 + 128 bytes)
+// clipped to [.., kend).  Thread tid moves chunk tid % 8 of rows tid / 8 + 32 p.
+template <typename T>
+struct DirectTile {
+  uint4 v[8];
+  __device__ __forceinline__ void load(const T* __restrict__ base, int64_t ld, int row0, int nrows,
+                                       int k0, int kend, int tid) {
+    constexpr int VEC = 16 / sizeof(T);
+    const int kc = k0 + (tid & 7) * VEC;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int row = row0 + (tid >> 3) + 32 * p;
+      uint4 x = make_uint4(0u, 0u, 0u, 0u);
+      if (row < nrows && kc < kend) {
+        x = *reinterpret_cast<const uint4*>(base + (int64_t)row * ld + kc);
+        if (kc + VEC > kend) x = keep_first<T>(x, kend - kc);
+      }
+      v[p] = x;
+    }
+  }
+  __device__ __forceinline__ void store(char* lds, int tid) const {
+#pragma unroll
+    for (int p = 0; p < 8; ++p)
+      *reinterpret_cast<uint4*>(lds + lds_off((tid >> 3) + 32 * p, tid & 7)) = v[p];
+  }
+};
+
+// Transposed operand of the dH GEMM: LDS row d holds W[k0 .. k0 + 128 bytes, d0 + d].
+template <typename T>
+struct TransTile;
+
+template <>
+struct TransTile<__bf16> {
+  uint4 v[8];  // 8 vocabulary rows x 8 hidden columns
+  __device__ __forceinline__ void load(const __bf16* __restrict__ W, int64_t D, int d0, int k0,
+                                       int kend, int tid) {
+    const int d = d0 + 8 * (tid & 31);
+    const int k = k0 + 8 * (tid >> 5);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint4 x = make_uint4(0u, 0u, 0u, 0u);
+      if (d < D && k + e < kend) x = *reinterpret_cast<const uint4*>(W + (int64_t)(k + e) * D + d);
+      v[e] = x;
+    }
+  }
+  __device__ __forceinline__ void store(char* lds, int tid) const {
+    const int b = tid & 31, a = tid >> 5;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = u4get(v[2 * q], i >> 1), hi = u4get(v[2 * q + 1], i >> 1);
+        w[q] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+      }
+      *reinterpret_cast<uint4*>(lds + lds_off(8 * b + i, a)) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+};
+
+template <>
+struct TransTile<float> {
+  uint4 v[8];  // 4 vocabulary rows x 8 hidden columns (two chunks per row)
+  __device__ __forceinline__ void load(const float* __restrict__ W, int64_t D, int d0, int k0,
+                                       int kend, int tid) {
+    const int d = d0 + 8 * (tid & 31);
+    const int k = k0 + 4 * (tid >> 5);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint4 x0 = make_uint4(0u, 0u, 0u, 0u), x1 = x0;
+      if (k + e < kend) {
+        const float* row = W + (int64_t)(k + e) * D;
+        if (d < D) x0 = *reinterpret_cast<const uint4*>(row + d);
+        if (d + 4 < D) x1 = *reinterpret_cast<const uint4*>(row + d + 4);
+      }
+      v[2 * e] = x0;
+      v[2 * e + 1] = x1;
+    }
+  }
+  __device__ __forceinline__ void store(char* lds, int tid) const {
+    const int b = tid & 31, a = tid >> 5;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int h = i >> 2, c = i & 3;
+      *reinterpret_cast<uint4*>(lds + lds_off(8 * b + i, a)) =
+          make_uint4(u4get(v[h], c), u4get(v[2 + h], c), u4get(v[4 + h], c), u4get(v[6 + h], c));
+    }
+  }
+};
+
+// One LDS stage (128 bytes of K per row) of MFMA work for a wave's 128 x 128 sub-tile.
+// Lane l supplies row (l % 32) of each 32-row block and k = 8 (l / 32) + 0..7 of each
+// 16-wide k step, for both operands alike.
+template <typename T>
+struct Mma;
+
+template <>
+struct Mma<__bf16> {
+  __device__ __forceinline__ static void stage(const char* As, const char* Bs, floatx16 (&acc)[4][4],
+                                               int wm, int wn, int lane) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int c = 2 * kk + (lane >> 5);
+      bf16x8 a[4], b[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        a[f] = *reinterpret_cast<const bf16x8*>(As + lds_off(wm * 128 + f * 32 + (lane & 31), c));
+        b[f] = *reinterpret_cast<const bf16x8*>(Bs + lds_off(wn * 128 + f * 32 + (lane & 31), c));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+};
+
+template <>
+struct Mma<float> {
+  __device__ __forceinline__ static void stage(const char* As, const char* Bs, floatx16 (&acc)[4][4],
+                                               int wm, int wn, int lane) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int c = 4 * kk + 2 * (lane >> 5);
+      float4 a[4][2], b[4][2];
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          a[f][h] = *reinterpret_cast<const float4*>(As + lds_off(wm * 128 + f * 32 + (lane & 31), c + h));
+          b[f][h] = *reinterpret_cast<const float4*>(Bs + lds_off(wn * 128 + f * 32 + (lane & 31), c + h));
+        }
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float av = e < 4 ? a[i][0][e] : a[i][1][e - 4];
+            const float bv = e < 4 ? b[j][0][e] : b[j][1][e - 4];
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc[i][j], 0, 0, 0);
+          }
+    }
+  }
+};
+
+// Store 4 consecutive elements (fp32 values) to a row of T.
+__device__ __forceinline__ void store4(__bf16* dst, float a, float b, float c, float d) {
+  *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16(a, b), pack_bf16(c, d));
+}
+__device__ __forceinline__ void store4(float* dst, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ void load4(const __bf16* src, float (&o)[4]) {
+  const uint2 u = *reinterpret_cast<const uint2*>(src);
+  o[0] = bf16_lo(u.x); o[1] = bf16_hi(u.x); o[2] = bf16_lo(u.y); o[3] = bf16_hi(u.y);
+}
+__device__ __forceinline__ void load4(const float* src, float (&o)[4]) {
+  const float4 u = *reinterpret_cast<const float4*>(src);
+  o[0] = u.x; o[1] = u.y; o[2] = u.z; o[3] = u.w;
+}
+
+// Accumulator element (i, j, r) of lane l: A-row wm*128 + 32 i + 8 (r / 4) + 4 (l / 32) + r % 4,
+// B-row (token) wn*128 + 32 j + l % 32.
+template <typename T, int KIND>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_kernel(const GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * kTileBytes];
+  int ta, tb;
+  if (!map_tile(g, ta, tb)) return;
+  constexpr int BK = 128 / (int)sizeof(T);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  int ks = 0, tile_a = ta;
+  if (KIND == KIND_DH) {
+    ks = ta / g.tiles_a_base;
+    tile_a = ta - ks * g.tiles_a_base;
+  }
+  const int row_a0 = tile_a * kTile;
+  const int row_b0 = tb * kTile;
+  const int k_begin = ks * g.k_len;
+  const int k_end = min(g.K, k_begin + g.k_len);
+  const int nk = k_end > k_begin ? (k_end - k_begin + BK - 1) / BK : 0;
+
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const T* A = reinterpret_cast<const T*>(g.a);
+  const T* B = reinterpret_cast<const T*>(g.b);
+  // stage s: A operand at smem + s * 64 KB, B operand 32 KB after it
+
+  using ALoader = typename std::conditional<KIND == KIND_DH, TransTile<T>, DirectTile<T>>::type;
+  ALoader la;
+  DirectTile<T> lb;
+  if (nk > 0) {
+    if constexpr (KIND == KIND_DH) la.load(A, g.lda, row_a0, k_begin, k_end, tid);
+    else la.load(A, g.lda, row_a0, g.a_rows, k_begin, k_end, tid);
+    lb.load(B, g.ldb, row_b0, g.b_rows, k_begin, k_end, tid);
+    la.store(smem, tid);
+    lb.store(smem + kTileBytes, tid);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      const bool more = kt + 1 < nk;
+      if (more) {
+        const int k0 = k_begin + (kt + 1) * BK;
+        if constexpr (KIND == KIND_DH) la.load(A, g.lda, row_a0, k0, k_end, tid);
+        else la.load(A, g.lda, row_a0, g.a_rows, k0, k_end, tid);
+        lb.load(B, g.ldb, row_b0, g.b_rows, k0, k_end, tid);
+      }
+      char* sc = smem + cur * (2 * kTileBytes);
+      char* sn = smem + (cur ^ 1) * (2 * kTileBytes);
+      Mma<T>::stage(sc, sc + kTileBytes, acc, wm, wn, lane);
+      if (more) {
+        la.store(sn, tid);
+        lb.store(sn + kTileBytes, tid);
+      }
+      __syncthreads();
+    }
+  }
+
+  const int hi = lane >> 5;     // which 4-row half of each 8-row group this lane holds
+  const int col = lane & 31;
+
+  if constexpr (KIND == KIND_LSE) {
+    // Per token: max and sum of exp over this tile's vocabulary rows (those < V).
+    float* red_m = reinterpret_cast<float*>(smem);
+    float* red_s = red_m + 2 * kTile;
+    const bool full = row_a0 + kTile <= g.a_rows;
+    const int vbase = row_a0 + wm * 128 + 4 * hi;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int v = vbase + 32 * i + 8 * (r >> 2) + (r & 3);
+          if (full || v < g.a_rows) mx = fmaxf(mx, acc[i][j][r]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float zmax = mx * g.inv_tau;  // inv_tau > 0, so this is the max of z
+      float s = 0.0f;
+      if (mx > -INFINITY) {
+        const float c1 = g.inv_tau * kLog2e, c0 = -zmax * kLog2e;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int v = vbase + 32 * i + 8 * (r >> 2) + (r & 3);
+            if (full || v < g.a_rows) s += __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], c1, c0));
+          }
+      }
+      s += __shfl_xor(s, 32);
+      if (hi == 0) {
+        red_m[wm * kTile + wn * 128 + 32 * j + col] = zmax;
+        red_s[wm * kTile + wn * 128 + 32 * j + col] = s;
+      }
+    }
+    __syncthreads();
+    const int tok = row_b0 + tid;
+    if (tok < g.b_rows) {
+      const float m0 = red_m[tid], m1 = red_m[kTile + tid];
+      const float M = fmaxf(m0, m1);
+      float S = 0.0f;
+      if (m0 > -INFINITY) S += red_s[tid] * __builtin_amdgcn_exp2f((m0 - M) * kLog2e);
+      if (m1 > -INFINITY) S += red_s[kTile + tid] * __builtin_amdgcn_exp2f((m1 - M) * kLog2e);
+      g.pm[(int64_t)tile_a * g.b_rows + tok] = M;
+      g.ps[(int64_t)tile_a * g.b_rows + tok] = S;
+    }
+  } else if constexpr (KIND == KIND_PROBS) {
+    // P[token, v] = exp(z - lse[token]) for v < V, written as 4-element vectors.
+    T* P = reinterpret_cast<T*>(g.p);
+    const float c1 = g.inv_tau * kLog2e;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tok = row_b0 + wn * 128 + 32 * j + col;
+      if (tok >= g.b_rows) continue;
+      const float c0 = -g.lse[tok] * kLog2e;
+      T* prow = P + (int64_t)tok * g.ldp;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int v0 = row_a0 + wm * 128 + 32 * i + 8 * q + 4 * hi;
+          float e[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) e[u] = __builtin_amdgcn_exp2f(fmaf(acc[i][j][4 * q + u], c1, c0));
+          if (v0 + 4 <= g.V) {
+            store4(prow + v0, e[0], e[1], e[2], e[3]);
+          } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (v0 + u < g.V) prow[v0 + u] = (T)e[u];
+          }
+        }
+    }
+  } else {
+    // dH[token, d] = (g / tau) (W[y, d] - acc), or the raw fp32 partial when split.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tok = row_b0 + wn * 128 + 32 * j + col;
+      if (tok >= g.b_rows) continue;
+      if (g.ksplit > 1) {
+        float* dst = g.part + ((int64_t)ks * g.b_rows + tok) * g.D;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int d0 = row_a0 + wm * 128 + 32 * i + 8 * q + 4 * hi;
+            if (d0 < g.D)
+              *reinterpret_cast<float4*>(dst + d0) =
+                  make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          }
+        continue;
+      }
+      const float gt = g.g[tok];
+      const int y = g.targets[tok];
+      const bool live = gt != 0.0f && y >= 0 && y < g.V;
+      const float scale = gt * g.inv_tau;
+      const T* wrow = reinterpret_cast<const T*>(g.w) + (int64_t)(live ? y : 0) * g.D;
+      T* dst = reinterpret_cast<T*>(g.dh) + (int64_t)tok * g.D;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int d0 = row_a0 + wm * 128 + 32 * i + 8 * q + 4 * hi;
+          if (d0 >= g.D) continue;
+          float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+          if (live) {
+            float wv[4];
+            load4(wrow + d0, wv);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) o[u] = scale * (wv[u] - acc[i][j][4 * q + u]);
+          }
+          store4(dst + d0, o[0], o[1], o[2], o[3]);
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------- small kernels
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// z[t, y_t] = (H[t] . W[y_t]) / tau, one wave per token, fixed summation order.
+template <typename T>
+__global__ __launch_bounds__(256) void target_logit_kernel(const T* __restrict__ H, const T* __restrict__ W,
+                                                           const int32_t* __restrict__ targets, int ntok,
+                                                           int D, int V, float inv_tau, float* __restrict__ zy) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= ntok) return;
+  const int y = targets[t];
+  if (y < 0 || y >= V) {
+    if (lane == 0) zy[t] = __builtin_nanf("");
+    return;
+  }
+  constexpr int VEC = 16 / sizeof(T);
+  const T* h = H + (int64_t)t * D;
+  const T* w = W + (int64_t)y * D;
+  float s = 0.0f;
+  for (int c = lane * VEC; c < D; c += 64 * VEC) {
+    const uint4 hv = *reinterpret_cast<const uint4*>(h + c);
+    const uint4 wv = *reinterpret_cast<const uint4*>(w + c);
+    if (sizeof(T) == 2) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        s = fmaf(bf16_lo(u4get(hv, q)), bf16_lo(u4get(wv, q)), s);
+        s = fmaf(bf16_hi(u4get(hv, q)), bf16_hi(u4get(wv, q)), s);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s = fmaf(__uint_as_float(u4get(hv, q)), __uint_as_float(u4get(wv, q)), s);
+    }
+  }
+  s = wave_sum(s);
+  if (lane == 0) zy[t] = s * inv_tau;
+}
+
+struct MergeArgs {
+  const float* pm;
+  const float* ps;
+  int ntiles;
+  int rows;
+  int64_t t0;
+  const float* zy;      // [T]
+  float* lse;           // [T]
+  float* logp;          // [T] or NULL
+  int grpo;
+  const float* old_logp;
+  const float* ref_logp;  // NULL when beta == 0
+  const float* adv;
+  const int32_t* seq;
+  const uint8_t* mask;    // NULL = all tokens count
+  const double* wseq;     // per-sequence token weight
+  float eps_lo, eps_hi, beta;
+  float* token_loss;      // NULL allowed
+  float* g;
+  double* wl;
+};
+
+// Merge of the vocabulary tiles' (max, sum-exp) partials in tile order; then, for the
+// loss, the per-token GRPO terms.
+__global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= a.rows) return;
+  const int64_t t = a.t0 + j;
+  float M = -INFINITY;
+  for (int i = 0; i < a.ntiles; ++i) M = fmaxf(M, a.pm[(int64_t)i * a.rows + j]);
+  float S = 0.0f;
+  for (int i = 0; i < a.ntiles; ++i) {
+    const float m = a.pm[(int64_t)i * a.rows + j];
+    if (m > -INFINITY) S += a.ps[(int64_t)i * a.rows + j] * expf(m - M);
+  }
+  const float lse = M + logf(S);
+  const float lp = a.zy[t] - lse;
+  a.lse[t] = lse;
+  if (a.logp) a.logp[t] = lp;
+  if (!a.grpo) return;
+
+  const int s = a.seq[t];
+  const float A = a.adv[s];
+  const bool counted = a.mask == nullptr || a.mask[t] != 0;
+  const double w64 = counted ? a.wseq[s] : 0.0;
+  const float w = (float)w64;
+  float ell, dell;
+  if (lp != lp) {  // target outside the vocabulary
+    ell = __builtin_nanf("");
+    dell = __builtin_nanf("");
+  } else {
+    const float rho = expf(lp - a.old_logp[t]);
+    const float c = fminf(fmaxf(rho, 1.0f - a.eps_lo), 1.0f + a.eps_hi);
+    const float un = rho * A, cl = c * A;
+    const float surr = un <= cl ? un : cl;
+    const float dsurr = un <= cl ? un : 0.0f;
+    float k3 = 0.0f, dk3 = 0.0f;
+    if (a.ref_logp) {
+      const float d = a.ref_logp[t] - lp;
+      const float em1 = expm1f(d);
+      k3 = em1 - d;
+      dk3 = -em1;
+    }
+    ell = -(surr - a.beta * k3);
+    dell = -dsurr + a.beta * dk3;
+  }
+  if (a.token_loss) a.token_loss[t] = ell;
+  a.g[t] = counted ? w * dell : 0.0f;
+  a.wl[t] = w64 != 0.0 ? w64 * (double)ell : 0.0;
+}
+
+// Largest s in [0, S) with cu[s] <= t: the sequence of token t.
+__device__ __forceinline__ int seq_of(const int32_t* cu, int S, int t) {
+  int lo = 0, hi = S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(256) void token_index_kernel(const int32_t* __restrict__ cu, int S, int ntok,
+                                                          int chunk, int32_t* __restrict__ seq,
+                                                          int32_t* __restrict__ chunk_id,
+                                                          int32_t* __restrict__ pos) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= ntok) return;
+  const int s = seq_of(cu, S, t);
+  seq[t] = s;
+  if (chunk_id) chunk_id[t] = t / chunk;
+  if (pos) pos[t] = t - cu[s];
+}
+
+// Unmasked tokens per sequence; one workgroup per sequence.
+__global__ __launch_bounds__(256) void seq_count_kernel(const int32_t* __restrict__ cu,
+                                                        const uint8_t* __restrict__ mask,
+                                                        int32_t* __restrict__ cnt) {
+  __shared__ int part[4];
+  const int s = blockIdx.x;
+  const int b = cu[s], e = cu[s + 1];
+  int n = 0;
+  if (mask) {
+    for (int t = b + (int)threadIdx.x; t < e; t += 256) n += mask[t] != 0;
+  } else if (threadIdx.x == 0) {
+    n = e - b;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) n += __shfl_xor(n, m);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = n;
+  __syncthreads();
+  if (threadIdx.x == 0) cnt[s] = part[0] + part[1] + part[2] + part[3];
+}
+
+// Per-sequence token weight: 1 / (S L_i) (sequence mean) or 1 / sum(L) (token mean).
+__global__ __launch_bounds__(256) void seq_weight_kernel(const int32_t* __restrict__ cnt, int S, int agg,
+                                                         double* __restrict__ wseq) {
+  __shared__ long long part[4];
+  long long n = 0;
+  for (int s = threadIdx.x; s < S; s += 256) n += cnt[s];
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) n += __shfl_xor(n, m);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = n;
+  __syncthreads();
+  const long long total = part[0] + part[1] + part[2] + part[3];
+  for (int s = threadIdx.x; s < S; s += 256) {
+    double w = 0.0;
+    if (agg == GRPO_AGG_SEQ_MEAN) {
+      if (cnt[s] > 0) w = 1.0 / ((double)S * (double)cnt[s]);
+    } else if (total > 0) {
+      w = 1.0 / (double)total;
+    }
+    wseq[s] = w;
+  }
+}
+
+// loss = sum_t wl[t] in fp64: thread i adds tokens i, i + 1024, ...; then a fixed tree.
+__global__ __launch_bounds__(1024) void loss_finalize_kernel(const double* __restrict__ wl, int ntok,
+                                                             double* __restrict__ loss) {
+  __shared__ double sm[1024];
+  double s = 0.0;
+  for (int t = threadIdx.x; t < ntok; t += 1024) s += wl[t];
+  sm[threadIdx.x] = s;
+  for (int stride = 512; stride > 0; stride >>= 1) {
+    __syncthreads();
+    if ((int)threadIdx.x < stride) sm[threadIdx.x] += sm[threadIdx.x + stride];
+  }
+  if (threadIdx.x == 0) loss[0] = sm[0];
+}
+
+// Fixed-order sum of the split-vocabulary dH partials, then (g / tau) (W[y] - sum).
+template <typename T>
+__global__ __launch_bounds__(256) void dh_reduce_kernel(const float* __restrict__ part, int ksplit, int rows,
+                                                        int D, int V, float inv_tau,
+                                                        const float* __restrict__ g,
+                                                        const int32_t* __restrict__ targets,
+                                                        const T* __restrict__ W, T* __restrict__ dh) {
+  const int quads = D / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)rows * quads) return;
+  const int tok = (int)(idx / quads);
+  const int d0 = (int)(idx - (int64_t)tok * quads) * 4;
+  const float gt = g[tok];
+  const int y = targets[tok];
+  float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (gt != 0.0f && y >= 0 && y < V) {
+    float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k = 0; k < ksplit; ++k) {
+      const float4 p = *reinterpret_cast<const float4*>(part + ((int64_t)k * rows + tok) * D + d0);
+      s[0] += p.x; s[1] += p.y; s[2] += p.z; s[3] += p.w;
+    }
+    float wv[4];
+    load4(W + (int64_t)y * D + d0, wv);
+    const float scale = gt * inv_tau;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) o[u] = scale * (wv[u] - s[u]);
+  }
+  store4(dh + (int64_t)tok * D + d0, o[0], o[1], o[2], o[3]);
+}
+
+// Group-relative advantages in fp64, one thread per group.
+__global__ __launch_bounds__(256) void advantages_kernel(const float* __restrict__ r, int ngroups, int G,
+                                                         int std_mode, float eps, float* __restrict__ adv) {
+  const int grp = blockIdx.x * 256 + threadIdx.x;
+  if (grp >= ngroups) return;
+  const float* x = r + (int64_t)grp * G;
+  float* o = adv + (int64_t)grp * G;
+  bool same = true;
+  for (int i = 1; i < G; ++i) same = same && x[i] == x[0];
+  if (G == 1 || same) {
+    for (int i = 0; i < G; ++i) o[i] = 0.0f;
+    return;
+  }
+  double mu = 0.0;
+  for (int i = 0; i < G; ++i) mu += (double)x[i];
+  mu /= (double)G;
+  double ss = 0.0;
+  for (int i = 0; i < G; ++i) {
+    const double dv = (double)x[i] - mu;
+    ss += dv * dv;
+  }
+  const double sigma = sqrt(ss / (double)(std_mode == GRPO_STD_UNBIASED ? G - 1 : G));
+  for (int i = 0; i < G; ++i) o[i] = (float)(((double)x[i] - mu) / (sigma + (double)eps));
+}
+
+// ---------------------------------------------------------------------------- host side
+
+struct Launcher {
+  hipStream_t stream;
+  grpo_timer* timer;
+  template <typename F>
+  void run(int kid, F&& f) {
+    int slot = -1;
+    if (timer) {
+      if (timer->used < timer->capacity) slot = timer->used++;
+      else ++timer->dropped;
+    }
+    if (slot >= 0) {
+      timer->kid[slot] = kid;
+      (void)hipEventRecord(timer->start[slot], stream);
+    }
+    f();
+    if (slot >= 0) (void)hipEventRecord(timer->stop[slot], stream);
+  }
+};
+
+inline int grid1(int64_t n, int per) { return (int)((n + per - 1) / per); }
+
+template <typename T, int KIND>
+void launch_gemm(Launcher& L, int kid, const GemmArgs& g) {
+  int per_xcd;
+  if (g.xcd_axis == 0) per_xcd = (int)cdiv(g.tiles_a, 8) * g.tiles_b;
+  else per_xcd = g.tiles_a * (int)cdiv(g.tiles_b, 8);
+  const int blocks = 8 * per_xcd;
+  L.run(kid, [&] { hipLaunchKernelGGL((gemm_kernel<T, KIND>), dim3(blocks), dim3(kThreads), 0, L.stream, g); });
+}
+
+template <typename T>
+void enqueue_logits_lse(Launcher& L, const Plan& p, const T* W, const T* Hc, int rows, float inv_tau,
+                        float* pm, float* ps) {
+  GemmArgs g = {};
+  g.a = W;
+  g.b = Hc;
+  g.lda = p.D;
+  g.ldb = p.D;
+  g.a_rows = (int)p.V;
+  g.b_rows = rows;
+  g.K = (int)p.D;
+  g.k_len = (int)p.D;
+  g.tiles_a_base = (int)p.ntiles_v;
+  g.tiles_a = (int)p.ntiles_v;
+  g.tiles_b = (int)cdiv(rows, kTile);
+  g.xcd_axis = 0;
+  g.group_b = 8;
+  g.inv_tau = inv_tau;
+  g.pm = pm;
+  g.ps = ps;
+  g.V = (int)p.V;
+  g.D = (int)p.D;
+  g.ksplit = 1;
+  launch_gemm<T, KIND_LSE>(L, GRPO_K_LOGITS_LSE, g);
+}
+
+template <typename T>
+grpo_status logp_impl(const Plan& p, const grpo_shape* shape, const T* H, const T* W, const int32_t* targets,
+                      float* logp, float* lse_out, char* ws, Launcher& L) {
+  const float inv_tau = 1.0f / shape->temperature;
+  float* zy = reinterpret_cast<float*>(ws + p.off_zy);
+  float* lse = lse_out ? lse_out : reinterpret_cast<float*>(ws + p.off_lse);
+  float* pm = reinterpret_cast<float*>(ws + p.off_pm);
+  float* ps = reinterpret_cast<float*>(ws + p.off_ps);
+  L.run(GRPO_K_TARGET_LOGIT, [&] {
+    hipLaunchKernelGGL((target_logit_kernel<T>), dim3(grid1(p.T, 4)), dim3(256), 0, L.stream, H, W, targets,
+                       (int)p.T, (int)p.D, (int)p.V, inv_tau, zy);
+  });
+  for (int64_t k = 0; k < p.nchunks; ++k) {
+    const int64_t t0 = k * p.C;
+    const int rows = (int)(p.T - t0 < p.C ? p.T - t0 : p.C);
+    enqueue_logits_lse<T>(L, p, W, H + t0 * p.D, rows, inv_tau, pm, ps);
+    MergeArgs m = {};
+    m.pm = pm;
+    m.ps = ps;
+    m.ntiles = (int)p.ntiles_v;
+    m.rows = rows;
+    m.t0 = t0;
+    m.zy = zy;
+    m.lse = lse;
+    m.logp = logp;
+    L.run(GRPO_K_MERGE, [&] {
+      hipLaunchKernelGGL(merge_kernel, dim3(grid1(rows, 256)), dim3(256), 0, L.stream, m);
+    });
+  }
+  return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_E_HIP;
+}
+
+template <typename T>
+grpo_status loss_impl(const Plan& p, const grpo_shape* shape, const grpo_loss_params* prm, const T* H,
+                      const T* W, const int32_t* targets, const int32_t* cu_host, const uint8_t* mask,
+                      const float* old_logp, const float* ref_logp, const float* adv, double* loss,
+                      float* logp, float* token_loss, T* dH, char* ws, Launcher& L) {
+  const float inv_tau = 1.0f / shape->temperature;
+  float* zy = reinterpret_cast<float*>(ws + p.off_zy);
+  float* lse = reinterpret_cast<float*>(ws + p.off_lse);
+  float* pm = reinterpret_cast<float*>(ws + p.off_pm);
+  float* ps = reinterpret_cast<float*>(ws + p.off_ps);
+  float* gbuf = reinterpret_cast<float*>(ws + p.off_g);
+  double* wl = reinterpret_cast<double*>(ws + p.off_wl);
+  int32_t* seq = reinterpret_cast<int32_t*>(ws + p.off_seq);
+  int32_t* cu = reinterpret_cast<int32_t*>(ws + p.off_cu);
+  int32_t* cnt = reinterpret_cast<int32_t*>(ws + p.off_cnt);
+  double* wseq = reinterpret_cast<double*>(ws + p.off_wseq);
+  T* P = reinterpret_cast<T*>(ws + p.off_P);
+  float* part = reinterpret_cast<float*>(ws + p.off_part);
+  const int S = (int)p.S;
+
+  if (hipMemcpyAsync(cu, cu_host, sizeof(int32_t) * (S + 1), hipMemcpyHostToDevice, L.stream) != hipSuccess)
+    return GRPO_E_HIP;
+  L.run(GRPO_K_TOKEN_INDEX, [&] {
+    if (p.T > 0)
+      hipLaunchKernelGGL(token_index_kernel, dim3(grid1(p.T, 256)), dim3(256), 0, L.stream, cu, S, (int)p.T,
+                         (int)(p.C > 0 ? p.C : 1), seq, (int32_t*)nullptr, (int32_t*)nullptr);
+    hipLaunchKernelGGL(seq_count_kernel, dim3(S), dim3(256), 0, L.stream, cu, mask, cnt);
+    hipLaunchKernelGGL(seq_weight_kernel, dim3(1), dim3(256), 0, L.stream, cnt, S, (int)prm->agg, wseq);
+  });
+  if (p.T > 0) {
+    L.run(GRPO_K_TARGET_LOGIT, [&] {
+      hipLaunchKernelGGL((target_logit_kernel<T>), dim3(grid1(p.T, 4)), dim3(256), 0, L.stream, H, W, targets,
+                         (int)p.T, (int)p.D, (int)p.V, inv_tau, zy);
+    });
+  }
+  for (int64_t k = 0; k < p.nchunks; ++k) {
+    const int64_t t0 = k * p.C;
+    const int rows = (int)(p.T - t0 < p.C ? p.T - t0 : p.C);
+    const T* Hc = H + t0 * p.D;
+    enqueue_logits_lse<T>(L, p, W, Hc, rows, inv_tau, pm, ps);
+
+    MergeArgs m = {};
+    m.pm = pm;
+    m.ps = ps;
+    m.ntiles = (int)p.ntiles_v;
+    m.rows = rows;
+    m.t0 = t0;
+    m.zy = zy;
+    m.lse = lse;
+    m.logp = logp;
+    m.grpo = 1;
+    m.old_logp = old_logp;
+    m.ref_logp = ref_logp;
+    m.adv = adv;
+    m.seq = seq;
+    m.mask = mask;
+    m.wseq = wseq;
+    m.eps_lo = prm->clip_eps_low;
+    m.eps_hi = prm->clip_eps_high;
+    m.beta = prm->beta;
+    m.token_loss = token_loss;
+    m.g = gbuf;
+    m.wl = wl;
+    L.run(GRPO_K_MERGE, [&] {
+      hipLaunchKernelGGL(merge_kernel, dim3(grid1(rows, 256)), dim3(256), 0, L.stream, m);
+    });
+
+    // Recompute the chunk's logits and write its softmax probabilities.
+    GemmArgs gp = {};
+    gp.a = W;
+    gp.b = Hc;
+    gp.lda = p.D;
+    gp.ldb = p.D;
+    gp.a_rows = (int)p.V;
+    gp.b_rows = rows;
+    gp.K = (int)p.D;
+    gp.k_len = (int)p.D;
+    gp.tiles_a_base = (int)p.ntiles_v;
+    gp.tiles_a = (int)p.ntiles_v;
+    gp.tiles_b = (int)cdiv(rows, kTile);
+    gp.xcd_axis = 0;
+    gp.group_b = 8;
+    gp.inv_tau = inv_tau;
+    gp.lse = lse + t0;
+    gp.p = P;
+    gp.ldp = p.ldp;
+    gp.V = (int)p.V;
+    gp.D = (int)p.D;
+    gp.ksplit = 1;
+    launch_gemm<T, KIND_PROBS>(L, GRPO_K_PROBS, gp);
+
+    // dH^T tiles: hidden x tokens, K = vocabulary, split over the vocabulary if needed.
+    const int ks_plan = (k == p.nchunks - 1) ? p.ksplit_tail : p.ksplit_full;
+    const int k_len = (int)(cdiv(cdiv(p.V, ks_plan), p.bk) * p.bk);
+    const int ksplit = (int)cdiv(p.V, k_len);
+    GemmArgs gd = {};
+    gd.a = W;
+    gd.b = P;
+    gd.lda = p.D;
+    gd.ldb = p.ldp;
+    gd.a_rows = (int)p.D;
+    gd.b_rows = rows;
+    gd.K = (int)p.V;
+    gd.k_len = k_len;
+    gd.tiles_a_base = (int)cdiv(p.D, kTile);
+    gd.tiles_a = gd.tiles_a_base * ksplit;
+    gd.tiles_b = (int)cdiv(rows, kTile);
+    gd.xcd_axis = 1;
+    gd.group_b = 2;
+    gd.inv_tau = inv_tau;
+    gd.g = gbuf + t0;
+    gd.targets = targets + t0;
+    gd.w = W;
+    gd.dh = dH + t0 * p.D;
+    gd.part = part;
+    gd.V = (int)p.V;
+    gd.D = (int)p.D;
+    gd.ksplit = ksplit;
+    launch_gemm<T, KIND_DH>(L, GRPO_K_DH_GEMM, gd);
+    if (ksplit > 1) {
+      L.run(GRPO_K_DH_REDUCE, [&] {
+        hipLaunchKernelGGL((dh_reduce_kernel<T>), dim3(grid1((int64_t)rows * (p.D / 4), 256)), dim3(256), 0,
+                           L.stream, part, ksplit, rows, (int)p.D, (int)p.V, inv_tau, gbuf + t0, targets + t0, W,
+                           dH + t0 * p.D);
+      });
+    }
+  }
+  L.run(GRPO_K_LOSS_FINALIZE, [&] {
+    hipLaunchKernelGGL(loss_finalize_kernel, dim3(1), dim3(1024), 0, L.stream, wl, (int)p.T, loss);
+  });
+  return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_E_HIP;
+}
+
+bool ws_ok(const Plan& p, const void* ws, size_t bytes) {
+  if (p.total == 0) return true;
+  return ws != nullptr && bytes >= p.total && (reinterpret_cast<uintptr_t>(ws) % kAlign) == 0;
+}
+
+}  // namespace
+}  // namespace grpo
+
+using namespace grpo;
+
+extern "C" {
+
+grpo_status grpo_logp_fwd(const grpo_shape* shape, const void* H, const void* W, const int32_t* targets,
+                          float* logp, float* lse, void* workspace, size_t workspace_bytes, void* stream,
+                          grpo_timer* timer) {
+  Plan p;
+  grpo_status st = make_plan(shape, 1, false, &p);
+  if (st != GRPO_OK) return st;
+  if (p.T > 0 && (!H || !W || !targets || !logp)) return GRPO_E_NULL;
+  if (!W) return GRPO_E_NULL;
+  if (!aligned16(H) || !aligned16(W)) return GRPO_E_UNSUPPORTED;
+  if (!ws_ok(p, workspace, workspace_bytes)) return GRPO_E_WORKSPACE;
+  if (p.T == 0) return GRPO_OK;
+  (void)hipGetLastError();  // clear any stale error so that failures below are this call's
+  Launcher L{reinterpret_cast<hipStream_t>(stream), timer};
+  char* ws = reinterpret_cast<char*>(workspace);
+  if (p.dtype == GRPO_BF16)
+    return logp_impl<__bf16>(p, shape, (const __bf16*)H, (const __bf16*)W, targets, logp, lse, ws, L);
+  return logp_impl<float>(p, shape, (const float*)H, (const float*)W, targets, logp, lse, ws, L);
+}
+
+grpo_status grpo_advantages(const float* rewards, int64_t num_seqs, int64_t group_size, int32_t std_mode,
+                            float eps, float* adv, void* stream) {
+  if (!rewards || !adv) return GRPO_E_NULL;
+  if (num_seqs < 1 || group_size < 1 || num_seqs % group_size != 0 || num_seqs > INT32_MAX) return GRPO_E_SHAPE;
+  if (std_mode != GRPO_STD_UNBIASED && std_mode != GRPO_STD_POPULATION) return GRPO_E_VALUE;
+  if (!isfinite(eps) || eps < 0.0f) return GRPO_E_VALUE;
+  (void)hipGetLastError();
+  const int ngroups = (int)(num_seqs / group_size);
+  hipLaunchKernelGGL(advantages_kernel, dim3(grid1(ngroups, 256)), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), rewards, ngroups, (int)group_size, (int)std_mode, eps,
+                     adv);
+  return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_E_HIP;
+}
+
+grpo_status grpo_loss_fwd_bwd(const grpo_shape* shape, const grpo_loss_params* params, const void* H,
+                              const void* W, const int32_t* targets, const int32_t* cu_seqlens, int64_t num_seqs,
+                              const uint8_t* mask, const float* old_logp, const float* ref_logp, const float* adv,
+                              double* loss, float* logp, float* token_loss, void* dH, void* workspace,
+                              size_t workspace_bytes, void* stream, grpo_timer* timer) {
+  grpo_status st = validate_shape(shape);
+  if (st != GRPO_OK) return st;
+  st = validate_loss_params(params);
+  if (st != GRPO_OK) return st;
+  if (!loss || !adv || !W) return GRPO_E_NULL;
+  if (shape->T > 0 && (!H || !targets || !old_logp || !dH)) return GRPO_E_NULL;
+  if (params->beta != 0.0f && shape->T > 0 && !ref_logp) return GRPO_E_NULL;
+  st = validate_cu(cu_seqlens, num_seqs, shape->T);
+  if (st != GRPO_OK) return st;
+  if (!aligned16(H) || !aligned16(W) || !aligned16(dH)) return GRPO_E_UNSUPPORTED;
+  Plan p;
+  st = make_plan(shape, num_seqs, true, &p);
+  if (st != GRPO_OK) return st;
+  if (!ws_ok(p, workspace, workspace_bytes)) return GRPO_E_WORKSPACE;
+  (void)hipGetLastError();
+  Launcher L{reinterpret_cast<hipStream_t>(stream), timer};
+  char* ws = reinterpret_cast<char*>(workspace);
+  const float* ref = params->beta != 0.0f ? ref_logp : nullptr;
+  if (p.dtype == GRPO_BF16)
+    return loss_impl<__bf16>(p, shape, params, (const __bf16*)H, (const __bf16*)W, targets, cu_seqlens, mask,
+                             old_logp, ref, adv, loss, logp, token_loss, (__bf16*)dH, ws, L);
+  return loss_impl<float>(p, shape, params, (const float*)H, (const float*)W, targets, cu_seqlens, mask, old_logp,
+                          ref, adv, loss, logp, token_loss, (float*)dH, ws, L);
+}
+
+grpo_status grpo_debug_token_index(const int32_t* cu_seqlens, int64_t num_seqs, int64_t T, int64_t chunk_tokens,
+                                   int32_t* seq_id, int32_t* chunk_id, int32_t* pos, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (T < 0 || T > INT32_MAX || chunk_tokens < 1) return GRPO_E_SHAPE;
+  grpo_status st = validate_cu(cu_seqlens, num_seqs, T);
+  if (st != GRPO_OK) return st;
+  if (T > 0 && (!seq_id || !chunk_id || !pos)) return GRPO_E_NULL;
+  const size_t need = align_up((size_t)(num_seqs + 1) * 4);
+  if (!workspace || workspace_bytes < need) return GRPO_E_WORKSPACE;
+  if (T == 0) return GRPO_OK;
+  (void)hipGetLastError();
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int32_t* cu = reinterpret_cast<int32_t*>(workspace);
+  if (hipMemcpyAsync(cu, cu_seqlens, sizeof(int32_t) * (num_seqs + 1), hipMemcpyHostToDevice, s) != hipSuccess)
+    return GRPO_E_HIP;
+  hipLaunchKernelGGL(token_index_kernel, dim3(grid1(T, 256)), dim3(256), 0, s, cu, (int)num_seqs, (int)T,
+                     (int)(chunk_tokens > INT32_MAX ? INT32_MAX : chunk_tokens), seq_id, chunk_id, pos);
+  return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_E_HIP;
+}
+
+grpo_status grpo_timer_create(int32_t capacity, grpo_timer** out) {
+  if (!out) return GRPO_E_NULL;
+  if (capacity < 1 || capacity > (1 << 20)) return GRPO_E_VALUE;
+  grpo_timer* t = new grpo_timer();
+  t->capacity = capacity;
+  t->start.resize(capacity);
+  t->stop.resize(capacity);
+  t->kid.resize(capacity);
+  for (int32_t i = 0; i < capacity; ++i) {
+    if (hipEventCreate(&t->start[i]) != hipSuccess || hipEventCreate(&t->stop[i]) != hipSuccess) {
+      t->capacity = i;  // destroy what was created
+      grpo_timer_destroy(t);
+      return GRPO_E_HIP;
+    }
+  }
+  *out = t;
+  return GRPO_OK;
+}
+
+grpo_status grpo_timer_destroy(grpo_timer* t) {
+  if (!t) return GRPO_E_NULL;
+  for (int32_t i = 0; i < t->capacity; ++i) {
+    if (t->start[i]) (void)hipEventDestroy(t->start[i]);
+    if (t->stop[i]) (void)hipEventDestroy(t->stop[i]);
+  }
+  delete t;
+  return GRPO_OK;
+}
+
+grpo_status grpo_timer_reset(grpo_timer* t) {
+  if (!t) return GRPO_E_NULL;
+  t->used = 0;
+  t->dropped = 0;
+  return GRPO_OK;
+}
+
+grpo_status grpo_timer_read(grpo_timer* t, int32_t kernel_id, double* total_ms, int64_t* launches,
+                            int64_t* dropped) {
+  if (!t || !total_ms || !launches) return GRPO_E_NULL;
+  if (kernel_id < 0 || kernel_id >= GRPO_K_COUNT) return GRPO_E_VALUE;
+  double ms = 0.0;
+  int64_t n = 0;
+  for (int32_t i = 0; i < t->used; ++i) {
+    if (t->kid[i] != kernel_id) continue;
+    if (hipEventSynchronize(t->stop[i]) != hipSuccess) return GRPO_E_HIP;
+    float e = 0.0f;
+    if (hipEventElapsedTime(&e, t->start[i], t->stop[i]) != hipSuccess) return GRPO_E_HIP;
+    ms += e;
+    ++n;
+  }
+  *total_ms = ms;
+  *launches = n;
+  if (dropped) *dropped = t->dropped;
+  return GRPO_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,49 @@
+// Host-side validation and workspace planning shared by the entry points.
+// Pure C++: no HIP headers, so the checks run (and are tested) without a GPU.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "grpo.h"
+
+namespace grpo {
+
+// MFMA tile edge: a workgroup computes a 256 x 256 output tile (vocabulary x tokens for
+// the logits GEMMs, hidden x tokens for the dH GEMM).
+constexpr int kTile = 256;
+// MI355X compute units; sizes the vocabulary split of the dH GEMM for small chunks.
+constexpr int kNumCUs = 256;
+constexpr int kMaxKSplit = 8;
+constexpr size_t kAlign = 256;
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+
+// K-step of the GEMM main loop: one 128-byte LDS row per operand row.
+inline int k_step(int32_t dtype) { return dtype == GRPO_BF16 ? 64 : 32; }
+inline int elem_size(int32_t dtype) { return dtype == GRPO_BF16 ? 2 : 4; }
+
+struct Plan {
+  int64_t T = 0, D = 0, V = 0, C = 0, nchunks = 0, S = 0;
+  int32_t dtype = 0;
+  int esize = 0, bk = 0;
+  int64_t ntiles_v = 0;   // vocabulary tiles = (max, sum-exp) partials per token
+  int64_t ldp = 0;        // row stride (elements) of the chunk probability matrix
+  int ksplit_full = 1;    // dH vocabulary split for a full chunk
+  int ksplit_tail = 1;    // ... and for the last, shorter chunk
+  bool backward = false;
+  size_t off_zy = 0, off_lse = 0, off_pm = 0, off_ps = 0;
+  size_t off_g = 0, off_wl = 0, off_seq = 0, off_cu = 0, off_cnt = 0, off_wseq = 0;
+  size_t off_P = 0, off_part = 0;
+  size_t total = 0;
+};
+
+grpo_status validate_shape(const grpo_shape* s);
+grpo_status validate_loss_params(const grpo_loss_params* p);
+grpo_status validate_cu(const int32_t* cu, int64_t S, int64_t T);
+grpo_status make_plan(const grpo_shape* s, int64_t S, bool backward, Plan* out);
+int dh_ksplit(int64_t chunk_rows, int64_t D, int64_t V, int32_t dtype);
+bool aligned16(const void* p);
+
+}  // namespace grpo

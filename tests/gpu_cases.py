@@ -1,0 +1,123 @@
+"""Helpers shared by the GPU parity tests: seeded cases on the device, the oracle on
+the host, and the comparison bars.
+
+Bars (per the problem statement): per-token logp abs error <= 1e-3; loss error
+<= 1e-4 relative to max(|L|, sum_t |w_t l_t|) (the loss is a cancelling sum of
+zero-mean advantages, so its own magnitude is not a usable scale); dH relative L2
+error <= 1e-2; integer index work bit-exact.
+"""
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from synth import make_case
+
+LOGP_ATOL = 1e-3
+LOSS_RTOL = 1e-4
+DH_REL_L2 = 1e-2
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def dev_matrix(x, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+def host_matrix(t, dtype):
+    t = t.detach().cpu()
+    if dtype == "bf16":
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def f32(x):
+    return np.asarray(x, dtype=np.float64).astype(np.float32)
+
+
+def case(seed, *, D, V, lengths, G=2, dtype="bf16", chunk=256, rewards=("uniform",), w_std=0.02,
+         old_std=None, ref_std=None, mask_frac=0.0, tau=1.0, beta=0.001, eps_lo=0.2, eps_hi=0.2,
+         agg="seq_mean", bad_targets=()):
+    """A seeded case with every input fixed on the host, plus the oracle's full result."""
+    c = make_case(seed, D=D, V=V, G=G, lengths=lengths, dtype=dtype, rewards=rewards, chunk=chunk, w_std=w_std)
+    T = c.T
+    H64 = oracle.widen(c.H, dtype)
+    W64 = oracle.widen(c.W, dtype)
+    targets = c.targets.copy()
+    for t in bad_targets:
+        targets[t] = V if t % 2 == 0 else -1
+    mask = c.mask.copy()
+    if mask_frac > 0:
+        rng = np.random.default_rng(seed + 77)
+        mask[rng.random(T) < mask_frac] = 0
+    logp0, _ = oracle.selective_log_softmax(H64, W64, targets, tau)
+    base = np.where(np.isfinite(logp0), logp0, -np.log(V))
+    n_old = c.noise_old if old_std is None else c.noise_old * (old_std / 0.01)
+    n_ref = c.noise_ref if ref_std is None else c.noise_ref * (ref_std / 0.05)
+    old = f32(base + n_old)
+    ref = f32(base + n_ref)
+    adv = f32(oracle.group_advantages(c.rewards, G))
+    prm = dict(clip_eps_low=eps_lo, clip_eps_high=eps_hi, beta=beta, agg=agg)
+    out = oracle.grpo_loss_and_grad(H64, W64, targets, c.cu, mask, old.astype(np.float64),
+                                    ref.astype(np.float64), adv.astype(np.float64), tau, **prm)
+    w = oracle.token_weights(c.cu, mask, agg)
+    return dict(c=c, T=T, D=D, V=V, dtype=dtype, tau=tau, targets=targets, mask=mask, old=old, ref=ref,
+                adv=adv, prm=prm, oracle=out, w=w, H64=H64, W64=W64)
+
+
+def to_device(k):
+    c = k["c"]
+    return dict(H=dev_matrix(c.H, k["dtype"]), W=dev_matrix(c.W, k["dtype"]),
+                targets=torch.from_numpy(k["targets"]).cuda(), mask=torch.from_numpy(k["mask"]).cuda(),
+                old=torch.from_numpy(k["old"]).cuda(), ref=torch.from_numpy(k["ref"]).cuda(),
+                adv=torch.from_numpy(k["adv"]).cuda())
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    nb = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+def near_clip_boundary(logp, old, eps_lo, eps_hi, tol=1e-4):
+    rho = np.exp(np.asarray(logp, np.float64) - old)
+    return (np.abs(rho - (1 - eps_lo)) <= tol) | (np.abs(rho - (1 + eps_hi)) <= tol)
+
+
+def check_loss_outputs(k, got, *, rows=None):
+    """Compare the GPU's loss, logp, token_loss and dH with the oracle's."""
+    o = k["oracle"]
+    T = k["T"]
+    rows = np.arange(T) if rows is None else rows
+    logp = got["logp"].cpu().numpy().astype(np.float64)
+    tl = got["token_loss"].cpu().numpy().astype(np.float64)
+    ok = np.isfinite(o["logp"][rows])
+    assert np.array_equal(np.isfinite(logp[rows]), ok), "NaN pattern of logp differs"
+    err = np.abs(logp[rows][ok] - o["logp"][rows][ok])
+    assert err.max(initial=0) <= LOGP_ATOL, f"logp max abs err {err.max()}"
+    A_t = k["adv"].astype(np.float64)[oracle.sequence_of_token(k["c"].cu)][rows]
+    terr = np.abs(tl[rows][ok] - o["token_loss"][rows][ok])
+    assert np.all(terr <= LOGP_ATOL * (1 + np.abs(A_t[ok]))), f"token_loss max err {terr.max()}"
+    L = float(got["loss"].cpu().numpy()[0])
+    scale = max(abs(o["loss"]), float(np.nansum(np.abs(k["w"] * o["token_loss"]))))
+    if np.isnan(o["loss"]):
+        assert np.isnan(L)
+    else:
+        assert abs(L - o["loss"]) <= LOSS_RTOL * scale, f"loss {L} vs {o['loss']} (scale {scale})"
+    dH = host_matrix(got["dH"], k["dtype"])
+    dH = oracle.widen(dH[rows], k["dtype"])
+    ref = o["dH"][rows]
+    amb = near_clip_boundary(o["logp"][rows], k["old"][rows].astype(np.float64),
+                             k["prm"]["clip_eps_low"], k["prm"]["clip_eps_high"])
+    sel = ~amb
+    assert rel_l2(dH[sel], ref[sel]) <= DH_REL_L2, f"dH rel L2 {rel_l2(dH[sel], ref[sel])}"
+    zero_rows = (o["g"][rows] == 0) | ~ok
+    assert np.all(dH[zero_rows] == 0), "masked / invalid rows must be exactly zero"
+    return dict(logp_err=err.max(initial=0), dH_rel=rel_l2(dH[sel], ref[sel]), loss=L, loss_ref=o["loss"])

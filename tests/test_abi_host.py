@@ -1,0 +1,145 @@
+"""Host-side checks of the C ABI: the library loads, exports every function that
+include/grpo.h declares, and rejects bad arguments before any HIP call (so these
+run without a GPU)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from rl_fine_tuning_amd import grpo as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "grpo.h")
+
+FAKE = ctypes.c_void_p(1 << 20)  # never dereferenced: every case fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(grpo_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 11
+    lib = B.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.grpo_version().startswith(b"grpo-mi355x")
+
+
+def test_status_strings():
+    lib = B.lib()
+    for s in range(7):
+        assert lib.grpo_status_string(s)
+    assert lib.grpo_status_string(99) == b"unknown status"
+
+
+def shape(T=100, D=64, V=512, C=32, dtype=0, tau=1.0):
+    return B.make_shape(T, D, V, C, dtype, tau)
+
+
+def test_workspace_bound_one_chunk_of_logits():
+    # extra memory <= one chunk's fp32 logits + O(T + C (V / 256 + D)) per-token state
+    for (T, D, V, C, S) in [(110000, 4096, 151936, 8192, 2), (40960, 1536, 151936, 4096, 64),
+                            (20480, 4096, 128256, 2048, 4), (380000, 2880, 201088, 8192, 4),
+                            (128, 64, 512, 32, 4)]:
+        for dt in (0, 1):
+            n = B.grpo_workspace_bytes(T, D, V, C, dt, num_seqs=S)
+            bound = C * V * 4 + 64 * T + 64 * 2 ** 20 + 8 * C * (V // 256 + 1) + 32 * C * D
+            assert 0 < n <= bound, (T, D, V, C, dt, n, bound)
+    assert B.grpo_workspace_bytes(0, 64, 512, 32) > 0
+    assert B.grpo_workspace_bytes(10, 63, 512, 32) == 0  # D not a multiple of 8 for bf16
+
+
+def test_logp_fwd_validation():
+    lib = B.lib()
+    s = shape()
+    ws = ctypes.c_void_p(1 << 20)
+    f = lambda sh, H=FAKE, W=FAKE, y=FAKE, lp=FAKE, wsp=ws, n=1 << 40: lib.grpo_logp_fwd(
+        ctypes.byref(sh), H, W, y, lp, None, wsp, n, None, None)
+    assert lib.grpo_logp_fwd(None, FAKE, FAKE, FAKE, FAKE, None, ws, 1 << 40, None, None) == 1
+    assert f(s, H=None) == 1
+    assert f(s, lp=None) == 1
+    assert f(shape(tau=0.0)) == 3
+    assert f(shape(tau=float("nan"))) == 3
+    assert f(shape(tau=-1.0)) == 3
+    assert f(shape(D=60)) == 5  # bf16 rows must be 16-byte multiples
+    assert f(shape(dtype=7)) == 5
+    assert f(shape(C=0)) == 2
+    assert f(shape(V=0)) == 2
+    assert f(shape(T=-1)) == 2
+    assert f(s, H=ctypes.c_void_p((1 << 20) + 2)) == 5  # misaligned
+    assert f(s, n=16) == 4
+    assert f(s, wsp=None) == 4
+    assert f(s, wsp=ctypes.c_void_p((1 << 20) + 16)) == 4  # workspace must be 256-byte aligned
+    # T = 0: nothing to do, nothing touched
+    assert f(shape(T=0), H=None, y=None, lp=None) == 0
+
+
+def test_loss_validation():
+    lib = B.lib()
+    T = 100
+    cu = np.array([0, 30, 60, 100], dtype=np.int32)
+    cup = cu.ctypes.data_as(ctypes.c_void_p)
+    good = B.GrpoLossParams(0.2, 0.2, 0.001, 0)
+
+    def call(sh=None, prm=good, cu_p=cup, S=3, ref=FAKE, ws_bytes=1 << 40, H=FAKE, dH=FAKE, old=FAKE,
+             adv=FAKE, loss=FAKE):
+        sh = sh or shape(T=T)
+        return lib.grpo_loss_fwd_bwd(ctypes.byref(sh), ctypes.byref(prm), H, FAKE, FAKE, cu_p, S, None, old,
+                                     ref, adv, loss, None, None, dH, FAKE, ws_bytes, None, None)
+
+    assert call(ws_bytes=16) == 4
+    assert call(H=None) == 1
+    assert call(dH=None) == 1
+    assert call(old=None) == 1
+    assert call(adv=None) == 1
+    assert call(loss=None) == 1
+    assert call(ref=None) == 1                                    # beta != 0 needs ref_logp
+    assert call(ref=None, prm=B.GrpoLossParams(0.2, 0.2, 0.0, 0), ws_bytes=16) == 4  # beta == 0: ref optional
+    assert call(prm=B.GrpoLossParams(1.0, 0.2, 0.001, 0)) == 3    # eps_low must be < 1
+    assert call(prm=B.GrpoLossParams(-0.1, 0.2, 0.001, 0)) == 3
+    assert call(prm=B.GrpoLossParams(0.2, float("inf"), 0.001, 0)) == 3
+    assert call(prm=B.GrpoLossParams(0.2, 0.2, -1.0, 0)) == 3
+    assert call(prm=B.GrpoLossParams(0.2, 0.2, 0.001, 5)) == 3
+    assert call(cu_p=None) == 1
+    assert call(S=0) == 2
+    bad = np.array([1, 30, 60, 100], dtype=np.int32)
+    assert call(cu_p=bad.ctypes.data_as(ctypes.c_void_p)) == 2     # cu[0] != 0
+    bad = np.array([0, 60, 30, 100], dtype=np.int32)
+    assert call(cu_p=bad.ctypes.data_as(ctypes.c_void_p)) == 2     # not monotone
+    bad = np.array([0, 30, 60, 99], dtype=np.int32)
+    assert call(cu_p=bad.ctypes.data_as(ctypes.c_void_p)) == 2     # cu[S] != T
+    assert call(sh=shape(T=T, tau=0.0)) == 3
+    assert call(dH=ctypes.c_void_p((1 << 20) + 4)) == 5
+
+
+def test_advantages_validation():
+    lib = B.lib()
+    f = lambda S=8, G=4, mode=0, eps=1e-4, r=FAKE, a=FAKE: lib.grpo_advantages(r, S, G, mode, eps, a, None)
+    assert f(r=None) == 1
+    assert f(a=None) == 1
+    assert f(S=7) == 2
+    assert f(S=0) == 2
+    assert f(G=0) == 2
+    assert f(mode=3) == 3
+    assert f(eps=-1.0) == 3
+    assert f(eps=float("nan")) == 3
+
+
+def test_debug_index_and_timer_validation():
+    lib = B.lib()
+    cu = np.array([0, 3, 3, 10], dtype=np.int32)
+    cup = cu.ctypes.data_as(ctypes.c_void_p)
+    assert lib.grpo_debug_token_index(cup, 3, 11, 4, FAKE, FAKE, FAKE, FAKE, 256, None) == 2
+    assert lib.grpo_debug_token_index(cup, 3, 10, 0, FAKE, FAKE, FAKE, FAKE, 256, None) == 2
+    assert lib.grpo_debug_token_index(cup, 3, 10, 4, FAKE, FAKE, FAKE, None, 256, None) == 4
+    assert lib.grpo_debug_token_index(cup, 3, 10, 4, None, FAKE, FAKE, FAKE, 256, None) == 1
+    h = ctypes.c_void_p()
+    assert lib.grpo_timer_create(0, ctypes.byref(h)) == 3
+    assert lib.grpo_timer_create(4, None) == 1
+    assert lib.grpo_timer_read(None, 0, None, None, None) == 1

@@ -1,0 +1,118 @@
+"""GPU parity of grpo_logp_fwd against the fp64 oracle (selective log-softmax over
+chunks of the flattened stream), with ragged shapes and tails in every dimension."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from rl_fine_tuning_amd import grpo_logp_fwd
+from synth import make_case, make_config
+
+from gpu_cases import LOGP_ATOL, dev_matrix, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_logp(c, chunk, tau=1.0, targets=None):
+    H = dev_matrix(c.H, c.dtype)
+    W = dev_matrix(c.W, c.dtype)
+    y = torch.from_numpy(c.targets if targets is None else targets).cuda()
+    logp, lse = grpo_logp_fwd(H, W, y, chunk, tau, return_lse=True)
+    torch.cuda.synchronize()
+    return logp.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def oracle_logp(c, tau=1.0, targets=None):
+    return oracle.selective_log_softmax(oracle.widen(c.H, c.dtype), oracle.widen(c.W, c.dtype),
+                                        c.targets if targets is None else targets, tau)
+
+
+def test_config0_tiny_fp32():
+    c = make_config(0)
+    say(f"logp config 0 T={c.T} D={c.D} V={c.V} chunk={c.chunk}")
+    lp, lse = run_logp(c, c.chunk)
+    ref, ref_lse = oracle_logp(c)
+    assert np.abs(lp - ref).max() <= LOGP_ATOL
+    assert np.abs(lp - ref).max() <= 1e-5  # fp32 inputs: only accumulation-order rounding
+    assert np.abs(lse - ref_lse).max() <= 1e-5
+
+
+@pytest.mark.parametrize("D,V,lengths,chunk,tau", [
+    (64, 512, [100, 28], 32, 1.0),
+    (136, 1000, [300, 211, 250], 256, 1.0),     # K tail (136 = 2 x 64 + 8), vocab tail
+    (520, 999, [513, 400, 600], 300, 0.7),      # odd V, several token tiles, tau
+    (256, 1288, [777], 777, 1.0),
+])
+def test_bf16_ragged_shapes(D, V, lengths, chunk, tau):
+    c = make_case(11 + D + V, D=D, V=V, G=1, lengths=lengths)
+    say(f"logp bf16 T={c.T} D={D} V={V} chunk={chunk} tau={tau}")
+    lp, lse = run_logp(c, chunk, tau)
+    ref, ref_lse = oracle_logp(c, tau)
+    err = np.abs(lp - ref).max()
+    assert err <= LOGP_ATOL, err
+    assert err <= 5e-5, err
+    assert np.abs(lse - ref_lse).max() <= 5e-5
+
+
+def test_fp32_ragged():
+    c = make_case(5, D=68, V=777, G=1, lengths=[300, 159], dtype="f32")
+    say("logp fp32 ragged")
+    lp, _ = run_logp(c, 200, 0.7)
+    ref, _ = oracle_logp(c, 0.7)
+    assert np.abs(lp - ref).max() <= 1e-5
+
+
+def test_chunk_size_invariance_is_bitwise():
+    c = make_case(21, D=128, V=1536, G=1, lengths=[611])
+    say("logp chunk invariance")
+    base, base_lse = run_logp(c, c.T)
+    for chunk in (1, 7, 100, 256, 300):
+        lp, lse = run_logp(c, chunk)
+        assert np.array_equal(lp, base), chunk
+        assert np.array_equal(lse, base_lse), chunk
+
+
+def test_probabilities_sum_to_one_all_targets_expansion():
+    # each of 3 tokens repeated V times with targets 0..V-1: sum_v exp(logp) = 1
+    V = 640
+    c = make_case(31, D=64, V=V, G=1, lengths=[3])
+    H = np.repeat(c.H, V, axis=0)
+    y = np.tile(np.arange(V, dtype=np.int32), 3)
+    say("logp all-targets expansion")
+    Ht = dev_matrix(H, "bf16")
+    lp = grpo_logp_fwd(Ht, dev_matrix(c.W, "bf16"), torch.from_numpy(y).cuda(), 512).cpu().numpy()
+    sums = np.exp(lp.astype(np.float64).reshape(3, V)).sum(axis=1)
+    assert np.abs(sums - 1).max() <= 1e-5
+
+
+@pytest.mark.parametrize("w_std", [0.2, 2.0])
+def test_peaked_softmax(w_std):
+    c = make_case(41, D=256, V=1024, G=1, lengths=[300], w_std=w_std)
+    say(f"logp peaked w_std={w_std}")
+    lp, lse = run_logp(c, 128)
+    ref, _ = oracle_logp(c)
+    assert np.all(np.isfinite(lp)) and np.all(np.isfinite(lse))
+    # logits reach |z| ~ 3e2 here: fp32 rounding of z bounds the error
+    assert np.abs(lp - ref).max() <= LOGP_ATOL * max(1.0, w_std)
+
+
+def test_out_of_range_targets_give_nan_only_there():
+    c = make_case(51, D=64, V=500, G=1, lengths=[50])
+    y = c.targets.copy()
+    y[[3, 17]] = [500, -2]
+    say("logp out-of-range targets")
+    lp, lse = run_logp(c, 16, targets=y)
+    assert np.isnan(lp[3]) and np.isnan(lp[17])
+    keep = np.ones(50, bool)
+    keep[[3, 17]] = False
+    ref, _ = oracle_logp(c, targets=y)
+    assert np.abs(lp[keep] - ref[keep]).max() <= 5e-5
+    assert np.all(np.isfinite(lse))
+
+
+def test_deterministic():
+    c = make_case(61, D=128, V=800, G=1, lengths=[400])
+    say("logp determinism")
+    a, _ = run_logp(c, 128)
+    b, _ = run_logp(c, 128)
+    assert np.array_equal(a, b)

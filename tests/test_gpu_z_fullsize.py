@@ -1,0 +1,84 @@
+"""Full-size workloads (the four bf16 model shapes) in the chunking the benchmark
+times, checked against the oracle on sampled tokens.
+
+Every per-token output (logp, l_t, dH row) depends on its own row only, so the
+oracle computes the sampled rows exactly: the first and last 8 tokens of every
+chunk, 4 tokens on each side of every sequence boundary, and 128 uniform tokens.
+Sampled tokens get old/ref log-probabilities = oracle logp + the workload's noise;
+the others get -log V + noise, which only moves the loss, and the loss is checked
+through its fixed relation to the per-token terms (L = sum_t w_t l_t).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from rl_fine_tuning_amd import grpo_loss_fwd_bwd, grpo_workspace_bytes
+from synth import make_config
+
+from gpu_cases import DH_REL_L2, LOGP_ATOL, dev_matrix, f32, host_matrix, near_clip_boundary, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+
+def sample_rows(c, rng):
+    T, C = c.T, c.chunk
+    rows = set()
+    for t0 in range(0, T, C):
+        t1 = min(T, t0 + C)
+        rows.update(range(t0, min(t1, t0 + 8)))
+        rows.update(range(max(t0, t1 - 8), t1))
+    for b in c.cu[1:-1]:
+        rows.update(range(max(0, b - 4), min(T, b + 4)))
+    rows.update(rng.integers(0, T, 128).tolist())
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_full_size_sampled(cfg):
+    c = make_config(cfg)
+    T, D, V, C = c.T, c.D, c.V, c.chunk
+    say(f"full size config {cfg}: T={T} D={D} V={V} chunk={C}")
+    rng = np.random.default_rng(cfg)
+    rows = sample_rows(c, rng)
+    W64 = oracle.widen(c.W, "bf16")
+    H_rows = oracle.widen(c.H[rows], "bf16")
+    lp_rows, lse_rows = oracle.selective_log_softmax(H_rows, W64, c.targets[rows])
+    base = np.full(T, -np.log(V))
+    base[rows] = lp_rows
+    old = f32(base + c.noise_old)
+    ref = f32(base + c.noise_ref)
+    adv = f32(oracle.group_advantages(c.rewards, c.G))
+
+    H = dev_matrix(c.H, "bf16")
+    W = dev_matrix(c.W, "bf16")
+    ws_bytes = grpo_workspace_bytes(T, D, V, C, 0, num_seqs=c.S)
+    assert ws_bytes <= C * V * 4  # extra memory stays below one chunk's fp32 logits
+    before = torch.cuda.memory_allocated()
+    got = grpo_loss_fwd_bwd(H, W, torch.from_numpy(c.targets).cuda(), c.cu, torch.from_numpy(old).cuda(),
+                            torch.from_numpy(ref).cuda(), torch.from_numpy(adv).cuda(), C)
+    torch.cuda.synchronize()
+    say(f"  gpu done; extra allocated {(torch.cuda.memory_allocated() - before) / 2**30:.2f} GiB")
+
+    logp = got["logp"].cpu().numpy().astype(np.float64)
+    tl = got["token_loss"].cpu().numpy().astype(np.float64)
+    err = np.abs(logp[rows] - lp_rows).max()
+    assert err <= LOGP_ATOL, err
+
+    s = oracle.sequence_of_token(c.cu)
+    w = oracle.token_weights(c.cu, c.mask)
+    terms = oracle.grpo_token_terms(lp_rows, old[rows].astype(np.float64), ref[rows].astype(np.float64),
+                                    adv.astype(np.float64)[s[rows]], 0.2, 0.2, 0.001)
+    assert np.all(np.abs(tl[rows] - terms["ell"]) <= LOGP_ATOL * (1 + np.abs(adv[s[rows]])))
+    g_rows = w[rows] * terms["dell"]
+    dH_ref = oracle.grad_rows(H_rows, W64, c.targets[rows], lse_rows, g_rows)
+    dH = oracle.widen(host_matrix(got["dH"][torch.from_numpy(rows).cuda()], "bf16"), "bf16")
+    amb = near_clip_boundary(lp_rows, old[rows].astype(np.float64), 0.2, 0.2)
+    e = rel_l2(dH[~amb], dH_ref[~amb])
+    assert e <= DH_REL_L2, e
+
+    L = float(got["loss"].cpu().numpy()[0])
+    L_terms = float(np.sum(w * tl))
+    scale = float(np.sum(np.abs(w * tl)))
+    assert abs(L - L_terms) <= 1e-6 * scale, (L, L_terms)
+    say(f"  logp err {err:.2e}, dH rel L2 {e:.2e}, loss {L:.6e}, workspace {ws_bytes / 2**30:.2f} GiB")
