@@ -148,25 +148,46 @@ __device__ __forceinline__ bool map_tile(const GemmArgs& g, int& ta, int& tb) {
   return true;
 }
 
-// Row-major operand, k contiguous: rows [row0, row0 + 256), k in [k0, k0 + 128 bytes)
-// clipped to [.., kend).  Thread tid moves chunk tid % 8 of rows tid / 8 + 32 p.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// A buffer offset beyond every range used here: a buffer load from it returns zeros.
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr uint32_t kMaxRange = 0x7ffffff0u;
+
+// Raw buffer resource over [base, base + bytes): loads at offsets past `bytes` return 0,
+// which zero-fills the rows and K columns beyond the operand without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const uint32_t n = bytes <= 0 ? 0u : (bytes > (int64_t)kMaxRange ? kMaxRange : (uint32_t)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Row-major operand, k contiguous: rows [row0, row0 + 256) of a matrix with `ld` elements
+// per row; one K step covers 128 bytes of k.  Thread tid moves chunk tid % 8 of rows
+// tid / 8 + 32 p.  Rows past the matrix and chunks at or past `kend` read as zero.
 template <typename T>
 struct DirectTile {
   uint4 v[8];
-  __device__ __forceinline__ void load(const T* __restrict__ base, int64_t ld, int row0, int nrows,
-                                       int k0, int kend, int tid) {
-    constexpr int VEC = 16 / sizeof(T);
-    const int kc = k0 + (tid & 7) * VEC;
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t vrow;      // byte offset of this thread's first row and chunk
+  uint32_t rstride;   // bytes between the rows one thread moves (32 rows)
+  int kc;             // k of this thread's chunk within a K step
+  __device__ __forceinline__ void init(const T* base, int64_t ld, int row0, int nrows, int tid) {
+    const int rows = max(0, min(nrows - row0, kTile));
+    rsrc = make_rsrc(base + (int64_t)row0 * ld, (int64_t)rows * ld * (int64_t)sizeof(T));
+    vrow = (uint32_t)((tid >> 3) * ld * (int64_t)sizeof(T)) + (uint32_t)((tid & 7) * 16);
+    rstride = (uint32_t)(32 * ld * (int64_t)sizeof(T));
+    kc = (tid & 7) * (16 / (int)sizeof(T));
+  }
+  __device__ __forceinline__ void load(int k0, int kend) {
+    const uint32_t soff = (uint32_t)k0 * (uint32_t)sizeof(T);
+    const uint32_t base = k0 + kc < kend ? vrow : kOOB;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int row = row0 + (tid >> 3) + 32 * p;
-      uint4 x = make_uint4(0u, 0u, 0u, 0u);
-      if (row < nrows && kc < kend) {
-        x = *reinterpret_cast<const uint4*>(base + (int64_t)row * ld + kc);
-        if (kc + VEC > kend) x = keep_first<T>(x, kend - kc);
-      }
-      v[p] = x;
-    }
+    for (int p = 0; p < 8; ++p) v[p] = bload(rsrc, base == kOOB ? kOOB : base + p * rstride, soff);
   }
   __device__ __forceinline__ void store(char* lds, int tid) const {
 #pragma unroll
@@ -182,16 +203,22 @@ struct TransTile;
 template <>
 struct TransTile<__bf16> {
   uint4 v[8];  // 8 vocabulary rows x 8 hidden columns
-  __device__ __forceinline__ void load(const __bf16* __restrict__ W, int64_t D, int d0, int k0,
-                                       int kend, int tid) {
-    const int d = d0 + 8 * (tid & 31);
-    const int k = k0 + 8 * (tid >> 5);
+  const __bf16* W;
+  int64_t D;
+  int d0;
+  uint32_t voff;  // this thread's block: row 8 (tid / 32), column 8 (tid % 32); kOOB past D
+  __device__ __forceinline__ void init(const __bf16* W_, int64_t D_, int d0_, int tid) {
+    W = W_;
+    D = D_;
+    d0 = d0_;
+    const int col = 8 * (tid & 31);
+    voff = d0 + col < D ? (uint32_t)((8 * (tid >> 5)) * D * 2 + col * 2) : kOOB;
+  }
+  __device__ __forceinline__ void load(int k0, int kend) {
+    const int64_t rows = min(kend - k0, 64);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(W + (int64_t)k0 * D + d0, (rows * D - d0) * 2);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint4 x = make_uint4(0u, 0u, 0u, 0u);
-      if (d < D && k + e < kend) x = *reinterpret_cast<const uint4*>(W + (int64_t)(k + e) * D + d);
-      v[e] = x;
-    }
+    for (int e = 0; e < 8; ++e) v[e] = bload(r, voff, voff == kOOB ? 0u : (uint32_t)(e * D * 2));
   }
   __device__ __forceinline__ void store(char* lds, int tid) const {
     const int b = tid & 31, a = tid >> 5;
@@ -211,20 +238,26 @@ struct TransTile<__bf16> {
 template <>
 struct TransTile<float> {
   uint4 v[8];  // 4 vocabulary rows x 8 hidden columns (two chunks per row)
-  __device__ __forceinline__ void load(const float* __restrict__ W, int64_t D, int d0, int k0,
-                                       int kend, int tid) {
-    const int d = d0 + 8 * (tid & 31);
-    const int k = k0 + 4 * (tid >> 5);
+  const float* W;
+  int64_t D;
+  int d0;
+  uint32_t voff0, voff1;  // first and second chunk of this thread's block; kOOB past D
+  __device__ __forceinline__ void init(const float* W_, int64_t D_, int d0_, int tid) {
+    W = W_;
+    D = D_;
+    d0 = d0_;
+    const int col = 8 * (tid & 31);
+    const uint32_t row = (uint32_t)((4 * (tid >> 5)) * D * 4);
+    voff0 = d0 + col < D ? row + col * 4 : kOOB;
+    voff1 = d0 + col + 4 < D ? row + col * 4 + 16 : kOOB;
+  }
+  __device__ __forceinline__ void load(int k0, int kend) {
+    const int64_t rows = min(kend - k0, 32);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(W + (int64_t)k0 * D + d0, (rows * D - d0) * 4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      uint4 x0 = make_uint4(0u, 0u, 0u, 0u), x1 = x0;
-      if (k + e < kend) {
-        const float* row = W + (int64_t)(k + e) * D;
-        if (d < D) x0 = *reinterpret_cast<const uint4*>(row + d);
-        if (d + 4 < D) x1 = *reinterpret_cast<const uint4*>(row + d + 4);
-      }
-      v[2 * e] = x0;
-      v[2 * e + 1] = x1;
+      v[2 * e] = bload(r, voff0, voff0 == kOOB ? 0u : (uint32_t)(e * D * 4));
+      v[2 * e + 1] = bload(r, voff1, voff1 == kOOB ? 0u : (uint32_t)(e * D * 4));
     }
   }
   __device__ __forceinline__ void store(char* lds, int tid) const {
@@ -238,30 +271,166 @@ struct TransTile<float> {
   }
 };
 
+// ---- bf16 main loop: a 4-stage LDS ring filled by direct-to-LDS buffer loads.
+//
+// A stage holds 64 bytes (32 bf16) of K for each of the 256 rows of both operands:
+// 16 KB per operand.  Two logical rows share one 128-byte LDS row (row R lives in LDS
+// row R / 2, chunk 4 (R % 2) + c for its 16-byte k chunk c), and the chunk index is
+// XORed with f2(R / 2) so that the 32 consecutive rows of an MFMA operand read, and
+// each 1 KB direct-to-LDS write, touch distinct banks for 32- and for 64-bank LDS.
+#ifndef GRPO_RING_STAGES
+#define GRPO_RING_STAGES 4
+#endif
+constexpr int kStages = GRPO_RING_STAGES;
+constexpr int kOpBytes = 16384;
+constexpr int kStageBytes = 2 * kOpBytes;
+constexpr int kBK16 = 32;  // bf16 elements of K per stage
+
+__device__ __forceinline__ int f2(int y) { return (y & 3) ^ ((y >> 1) & 3); }
+__device__ __forceinline__ int lds_off2(int R, int c) {
+  const int y = R >> 1;
+  return y * 128 + (((4 * (R & 1) + c) ^ f2(y)) << 4);
+}
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Row-major bf16 operand (k contiguous) moved straight into LDS: each wave issues 4
+// buffer loads per stage, each filling 1 KB (8 LDS rows); lane i of a load fills 16
+// bytes at i * 16, so it fetches the row and chunk that the swizzle places there.
+struct DmaTile {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t lane_off;  // byte offset of this lane's row and chunk from the tile base
+  uint32_t jstride;   // bytes between the 16-row groups of consecutive loads
+  int kc;             // k of this lane's chunk within a stage
+  int w;              // wave index (uniform)
+  __device__ __forceinline__ void init(const __bf16* base, int64_t ld, int row0, int nrows, int tid) {
+    const int rows = max(0, min(nrows - row0, kTile));
+    rsrc = make_rsrc(base + (int64_t)row0 * ld, (int64_t)rows * ld * 2);
+    const int i = tid & 63;
+    w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int y = i >> 3;
+    const int cp = (i & 7) ^ f2(y);
+    const int dR = 2 * y + (cp >> 2);
+    const int c = cp & 3;
+    lane_off = (uint32_t)((64 * w + dR) * ld * 2 + 16 * c);
+    jstride = (uint32_t)(16 * ld * 2);
+    kc = 8 * c;
+  }
+  __device__ __forceinline__ void issue(char* lds_op, int k0, int kend) const {
+    const uint32_t v = k0 + kc < kend ? lane_off : kOOB;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(lds_op + (4 * w + j) * 1024), 16, v,
+                                               (uint32_t)(j * jstride + k0 * 2), 0, 0);
+  }
+};
+
+// Transposed W operand of the dH GEMM for the ring: wave c takes vocabulary rows
+// 8c .. 8c + 7 of the stage, lane q hidden columns 4q .. 4q + 3; the 8 x 4 block is
+// transposed in registers into four 16-byte k chunks (one per hidden column).
+struct TransTileRing {
+  uint2 v[8];
+  const __bf16* W;
+  int64_t D;
+  int d0;
+  int c;
+  int q;
+  uint32_t voff;
+  __device__ __forceinline__ void init(const __bf16* W_, int64_t D_, int d0_, int tid) {
+    W = W_;
+    D = D_;
+    d0 = d0_;
+    q = tid & 63;
+    c = tid >> 6;
+    voff = d0 + 4 * q < D ? (uint32_t)((8 * c) * D * 2 + 8 * q) : kOOB;
+  }
+  __device__ __forceinline__ void load(int k0, int kend) {
+    const int64_t rows = min(kend - k0, kBK16);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(W + (int64_t)k0 * D + d0, (rows * D - d0) * 2);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, voff == kOOB ? 0u : (uint32_t)(e * D * 2), 0);
+      v[e] = make_uint2(x.x, x.y);
+    }
+  }
+  __device__ __forceinline__ void store(char* lds_op) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = (i < 2) ? v[2 * j].x : v[2 * j].y;
+        const uint32_t hi = (i < 2) ? v[2 * j + 1].x : v[2 * j + 1].y;
+        o[j] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+      }
+      *reinterpret_cast<uint4*>(lds_op + lds_off2(4 * q + i, c)) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+};
+
+// Fragments of one 16-wide k step (kk = 0, 1) of a ring stage for a wave's 128 x 128 tile.
+__device__ __forceinline__ void ring_frags(const char* As, const char* Bs, int kk, int wm, int wn, int lane,
+                                           bf16x8 (&a)[4], bf16x8 (&b)[4]) {
+  const int c = 2 * kk + (lane >> 5);
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    a[f] = *reinterpret_cast<const bf16x8*>(As + lds_off2(wm * 128 + f * 32 + (lane & 31), c));
+    b[f] = *reinterpret_cast<const bf16x8*>(Bs + lds_off2(wn * 128 + f * 32 + (lane & 31), c));
+  }
+}
+
+__device__ __forceinline__ void mma16(const bf16x8 (&a)[4], const bf16x8 (&b)[4], floatx16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+// At the mid-iteration barrier of iteration kt the loads of stage kt + 1 must have
+// landed; the loads of the kStages - 2 later iterations (8 per wave each) may still fly.
+constexpr int kWaitVm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xf00; }
+constexpr int kWaitVmLgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70; }
+constexpr int kWaitRing = kWaitVmLgkm0(8 * (kStages - 2));
+constexpr int kWaitAll = 0x0070;
+
 // One LDS stage (128 bytes of K per row) of MFMA work for a wave's 128 x 128 sub-tile.
 // Lane l supplies row (l % 32) of each 32-row block and k = 8 (l / 32) + 0..7 of each
-// 16-wide k step, for both operands alike.
+// 16-wide k step, for both operands alike.  The fragments of k step i + 1 are read from
+// LDS while the 16 MFMAs of step i run.
 template <typename T>
 struct Mma;
 
 template <>
 struct Mma<__bf16> {
+  __device__ __forceinline__ static void frags(const char* As, const char* Bs, int kk, int wm, int wn, int lane,
+                                               bf16x8 (&a)[4], bf16x8 (&b)[4]) {
+    const int c = 2 * kk + (lane >> 5);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      a[f] = *reinterpret_cast<const bf16x8*>(As + lds_off(wm * 128 + f * 32 + (lane & 31), c));
+      b[f] = *reinterpret_cast<const bf16x8*>(Bs + lds_off(wn * 128 + f * 32 + (lane & 31), c));
+    }
+  }
+  __device__ __forceinline__ static void mma(const bf16x8 (&a)[4], const bf16x8 (&b)[4], floatx16 (&acc)[4][4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
   __device__ __forceinline__ static void stage(const char* As, const char* Bs, floatx16 (&acc)[4][4],
                                                int wm, int wn, int lane) {
+    bf16x8 a[2][4], b[2][4];
+    frags(As, Bs, 0, wm, wn, lane, a[0], b[0]);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const int c = 2 * kk + (lane >> 5);
-      bf16x8 a[4], b[4];
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        a[f] = *reinterpret_cast<const bf16x8*>(As + lds_off(wm * 128 + f * 32 + (lane & 31), c));
-        b[f] = *reinterpret_cast<const bf16x8*>(Bs + lds_off(wn * 128 + f * 32 + (lane & 31), c));
-      }
+      if (kk < 3) frags(As, Bs, kk + 1, wm, wn, lane, a[(kk + 1) & 1], b[(kk + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][i], b[kk & 1][j], acc[i][j], 0, 0, 0);
     }
   }
 };
@@ -316,7 +485,7 @@ __device__ __forceinline__ void load4(const float* src, float (&o)[4]) {
 template <typename T, int KIND>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(const GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * kTileBytes];
+  __shared__ __attribute__((aligned(16))) char smem[sizeof(T) == 2 ? kStages * kStageBytes : 2 * 2 * kTileBytes];
   int ta, tb;
   if (!map_tile(g, ta, tb)) return;
   constexpr int BK = 128 / (int)sizeof(T);
@@ -333,7 +502,8 @@ void gemm_kernel(const GemmArgs g) {
   const int row_b0 = tb * kTile;
   const int k_begin = ks * g.k_len;
   const int k_end = min(g.K, k_begin + g.k_len);
-  const int nk = k_end > k_begin ? (k_end - k_begin + BK - 1) / BK : 0;
+  constexpr int BKL = sizeof(T) == 2 ? kBK16 : BK;  // K per pipeline stage
+  const int nk = k_end > k_begin ? (k_end - k_begin + BKL - 1) / BKL : 0;
 
   floatx16 acc[4][4];
 #pragma unroll
@@ -347,33 +517,112 @@ void gemm_kernel(const GemmArgs g) {
   const T* B = reinterpret_cast<const T*>(g.b);
   // stage s: A operand at smem + s * 64 KB, B operand 32 KB after it
 
-  using ALoader = typename std::conditional<KIND == KIND_DH, TransTile<T>, DirectTile<T>>::type;
-  ALoader la;
-  DirectTile<T> lb;
-  if (nk > 0) {
-    if constexpr (KIND == KIND_DH) la.load(A, g.lda, row_a0, k_begin, k_end, tid);
-    else la.load(A, g.lda, row_a0, g.a_rows, k_begin, k_end, tid);
-    lb.load(B, g.ldb, row_b0, g.b_rows, k_begin, k_end, tid);
-    la.store(smem, tid);
-    lb.store(smem + kTileBytes, tid);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      const bool more = kt + 1 < nk;
-      if (more) {
-        const int k0 = k_begin + (kt + 1) * BK;
-        if constexpr (KIND == KIND_DH) la.load(A, g.lda, row_a0, k0, k_end, tid);
-        else la.load(A, g.lda, row_a0, g.a_rows, k0, k_end, tid);
-        lb.load(B, g.ldb, row_b0, g.b_rows, k0, k_end, tid);
+  if constexpr (sizeof(T) == 2) {
+    // 4-stage ring, one stage = 32 bf16 of K.  Iteration kt computes stage kt in two
+    // 16-wide k steps: the loads for stage kt + 3 and the fragments of step 1 are issued
+    // under the MFMAs of step 0; then this wave's loads of stage kt + 1 are waited for and
+    // a barrier publishes every wave's; the fragments of stage kt + 1, step 0 are read
+    // under the MFMAs of step 1.  A ring slot is refilled only after the barrier that
+    // follows its last read.
+    DmaTile db;
+    db.init(B, g.ldb, row_b0, g.b_rows, tid);
+    [[maybe_unused]] DmaTile da;
+    [[maybe_unused]] TransTileRing ta;
+    if constexpr (KIND == KIND_DH) ta.init(A, g.lda, row_a0, tid);
+    else da.init(A, g.lda, row_a0, g.a_rows, tid);
+    if (nk > 0) {
+#pragma unroll
+      for (int st = 0; st < kStages - 1; ++st) {
+        char* sb = smem + st * kStageBytes;
+        const int k0 = k_begin + st * kBK16;
+        if constexpr (KIND == KIND_DH) {
+          ta.load(k0, k_end);
+          ta.store(sb);
+        } else {
+          da.issue(sb, k0, k_end);
+        }
+        db.issue(sb + kOpBytes, k0, k_end);
       }
-      char* sc = smem + cur * (2 * kTileBytes);
-      char* sn = smem + (cur ^ 1) * (2 * kTileBytes);
-      Mma<T>::stage(sc, sc + kTileBytes, acc, wm, wn, lane);
-      if (more) {
-        la.store(sn, tid);
-        lb.store(sn + kTileBytes, tid);
+      __builtin_amdgcn_s_waitcnt(kWaitAll);
+      __builtin_amdgcn_s_barrier();
+      bf16x8 a0[4], b0[4], a1[4], b1[4];
+      ring_frags(smem, smem + kOpBytes, 0, wm, wn, lane, a0, b0);
+      int slot = 0;  // ring slot of stage kt
+      for (int kt = 0; kt < nk; ++kt) {
+        const int slot_n = slot + 1 == kStages ? 0 : slot + 1;
+        const int slot_f = slot == 0 ? kStages - 1 : slot - 1;  // stage kt + kStages - 1
+        char* sc = smem + slot * kStageBytes;
+        char* sn = smem + slot_n * kStageBytes;
+        char* sf = smem + slot_f * kStageBytes;
+        slot = slot_n;
+        const int kf = k_begin + (kt + kStages - 1) * kBK16;
+        if constexpr (KIND == KIND_DH) ta.load(kf, k_end);
+        else da.issue(sf, kf, k_end);
+        db.issue(sf + kOpBytes, kf, k_end);
+        ring_frags(sc, sc + kOpBytes, 1, wm, wn, lane, a1, b1);
+        mma16(a0, b0, acc);
+        // instruction classes: 0x8 MFMA, 0x20 VMEM read, 0x100 DS read, 0x200 DS write
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, KIND == KIND_DH ? 2 : 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(kWaitRing);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        ring_frags(sn, sn + kOpBytes, 0, wm, wn, lane, a0, b0);
+        mma16(a1, b1, acc);
+        if constexpr (KIND == KIND_DH) ta.store(sf);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        if constexpr (KIND == KIND_DH) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_s_waitcnt(kWaitAll);
+      __builtin_amdgcn_s_barrier();
+    }
+  } else {
+    using ALoader = typename std::conditional<KIND == KIND_DH, TransTile<T>, DirectTile<T>>::type;
+    ALoader la;
+    DirectTile<T> lb;
+    if constexpr (KIND == KIND_DH) la.init(A, g.lda, row_a0, tid);
+    else la.init(A, g.lda, row_a0, g.a_rows, tid);
+    lb.init(B, g.ldb, row_b0, g.b_rows, tid);
+    if (nk > 0) {
+      la.load(k_begin, k_end);
+      lb.load(k_begin, k_end);
+      la.store(smem, tid);
+      lb.store(smem + kTileBytes, tid);
       __syncthreads();
+      for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        const bool more = kt + 1 < nk;
+        if (more) {
+          const int k0 = k_begin + (kt + 1) * BK;
+          la.load(k0, k_end);
+          lb.load(k0, k_end);
+        }
+        char* sc = smem + cur * (2 * kTileBytes);
+        char* sn = smem + (cur ^ 1) * (2 * kTileBytes);
+        Mma<T>::stage(sc, sc + kTileBytes, acc, wm, wn, lane);
+        if (more) {
+          la.store(sn, tid);
+          lb.store(sn + kTileBytes, tid);
+        }
+        __syncthreads();
+      }
     }
   }
 
@@ -423,8 +672,8 @@ void gemm_kernel(const GemmArgs g) {
       float S = 0.0f;
       if (m0 > -INFINITY) S += red_s[tid] * __builtin_amdgcn_exp2f((m0 - M) * kLog2e);
       if (m1 > -INFINITY) S += red_s[kTile + tid] * __builtin_amdgcn_exp2f((m1 - M) * kLog2e);
-      g.pm[(int64_t)tile_a * g.b_rows + tok] = M;
-      g.ps[(int64_t)tile_a * g.b_rows + tok] = S;
+      g.pm[(int64_t)tok * g.tiles_a + tile_a] = M;
+      g.ps[(int64_t)tok * g.tiles_a + tile_a] = S;
     }
   } else if constexpr (KIND == KIND_PROBS) {
     // P[token, v] = exp(z - lse[token]) for v < V, written as 4-element vectors.
@@ -446,10 +695,11 @@ void gemm_kernel(const GemmArgs g) {
           for (int u = 0; u < 4; ++u) e[u] = __builtin_amdgcn_exp2f(fmaf(acc[i][j][4 * q + u], c1, c0));
           if (v0 + 4 <= g.V) {
             store4(prow + v0, e[0], e[1], e[2], e[3]);
-          } else {
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-              if (v0 + u < g.V) prow[v0 + u] = (T)e[u];
+          } else if (v0 < g.ldp) {
+            // the row's padding up to the 16-byte boundary is written as zeros: the dH
+            // GEMM reads whole 16-byte chunks
+            store4(prow + v0, v0 < g.V ? e[0] : 0.0f, v0 + 1 < g.V ? e[1] : 0.0f, v0 + 2 < g.V ? e[2] : 0.0f,
+                   v0 + 3 < g.V ? e[3] : 0.0f);
           }
         }
     }
@@ -562,19 +812,31 @@ struct MergeArgs {
   double* wl;
 };
 
-// Merge of the vocabulary tiles' (max, sum-exp) partials in tile order; then, for the
-// loss, the per-token GRPO terms.
+// Merge of the vocabulary tiles' (max, sum-exp) partials, stored token-major; then, for
+// the loss, the per-token GRPO terms.  16 lanes share a token: lane j takes tiles j,
+// j + 16, ... in order and the 16 partial sums combine in a fixed butterfly, so the
+// result depends on the vocabulary size only, never on the chunking.
 __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= a.rows) return;
-  const int64_t t = a.t0 + j;
+  const int j = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  const bool valid = j < a.rows;
+  const float* pm = a.pm + (int64_t)(valid ? j : 0) * a.ntiles;
+  const float* ps = a.ps + (int64_t)(valid ? j : 0) * a.ntiles;
   float M = -INFINITY;
-  for (int i = 0; i < a.ntiles; ++i) M = fmaxf(M, a.pm[(int64_t)i * a.rows + j]);
+  if (valid)
+    for (int i = sub; i < a.ntiles; i += 16) M = fmaxf(M, pm[i]);
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 16));
   float S = 0.0f;
-  for (int i = 0; i < a.ntiles; ++i) {
-    const float m = a.pm[(int64_t)i * a.rows + j];
-    if (m > -INFINITY) S += a.ps[(int64_t)i * a.rows + j] * expf(m - M);
-  }
+  if (valid)
+    for (int i = sub; i < a.ntiles; i += 16) {
+      const float m = pm[i];
+      if (m > -INFINITY) S += ps[i] * expf(m - M);
+    }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) S += __shfl_xor(S, m, 16);
+  if (!valid || sub != 0) return;
+  const int64_t t = a.t0 + j;
   const float lse = M + logf(S);
   const float lp = a.zy[t] - lse;
   a.lse[t] = lse;
@@ -829,7 +1091,7 @@ grpo_status logp_impl(const Plan& p, const grpo_shape* shape, const T* H, const 
     m.lse = lse;
     m.logp = logp;
     L.run(GRPO_K_MERGE, [&] {
-      hipLaunchKernelGGL(merge_kernel, dim3(grid1(rows, 256)), dim3(256), 0, L.stream, m);
+      hipLaunchKernelGGL(merge_kernel, dim3(grid1(rows, 16)), dim3(256), 0, L.stream, m);
     });
   }
   return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_E_HIP;
@@ -899,7 +1161,7 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, const grpo_loss_pa
     m.g = gbuf;
     m.wl = wl;
     L.run(GRPO_K_MERGE, [&] {
-      hipLaunchKernelGGL(merge_kernel, dim3(grid1(rows, 256)), dim3(256), 0, L.stream, m);
+      hipLaunchKernelGGL(merge_kernel, dim3(grid1(rows, 16)), dim3(256), 0, L.stream, m);
     });
 
     // Recompute the chunk's logits and write its softmax probabilities.
