@@ -326,7 +326,9 @@ struct DmaTile {
 
 // Transposed W operand of the dH GEMM for the ring: wave c takes vocabulary rows
 // 8c .. 8c + 7 of the stage, lane q hidden columns 4q .. 4q + 3; the 8 x 4 block is
-// transposed in registers into four 16-byte k chunks (one per hidden column).
+// transposed in registers into four 16-byte k chunks, one per hidden column.  In store
+// t lane q writes the chunk of column 4q + (t + q / 4) % 4, which spreads the 64 lanes of
+// one store over all LDS banks.
 struct TransTileRing {
   uint2 v[8];
   const __bf16* W;
@@ -353,17 +355,31 @@ struct TransTileRing {
     }
   }
   __device__ __forceinline__ void store(char* lds_op) const {
+    uint4 o[4];  // o[i]: the 8 vocabulary entries of hidden column 4q + i
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint32_t o[4];
+      uint32_t w[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t lo = (i < 2) ? v[2 * j].x : v[2 * j].y;
         const uint32_t hi = (i < 2) ? v[2 * j + 1].x : v[2 * j + 1].y;
-        o[j] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+        w[j] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
       }
-      *reinterpret_cast<uint4*>(lds_op + lds_off2(4 * q + i, c)) = make_uint4(o[0], o[1], o[2], o[3]);
+      o[i] = make_uint4(w[0], w[1], w[2], w[3]);
     }
+    // rotate o by r = (q / 4) % 4 with two conditional swaps (no register indexing)
+    const int r = (q >> 2) & 3;
+    if (r & 1) {
+      const uint4 t0 = o[0];
+      o[0] = o[1]; o[1] = o[2]; o[2] = o[3]; o[3] = t0;
+    }
+    if (r & 2) {
+      uint4 t0 = o[0]; o[0] = o[2]; o[2] = t0;
+      t0 = o[1]; o[1] = o[3]; o[3] = t0;
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      *reinterpret_cast<uint4*>(lds_op + lds_off2(4 * q + ((t + r) & 3), c)) = o[t];
   }
 };
 
@@ -526,18 +542,21 @@ void gemm_kernel(const GemmArgs g) {
     // follows its last read.
     DmaTile db;
     db.init(B, g.ldb, row_b0, g.b_rows, tid);
-    [[maybe_unused]] DmaTile da;
-    [[maybe_unused]] TransTileRing ta;
-    if constexpr (KIND == KIND_DH) ta.init(A, g.lda, row_a0, tid);
+    using ATile = typename std::conditional<KIND == KIND_DH, TransTileRing, DmaTile>::type;
+    ATile da;
+    if constexpr (KIND == KIND_DH) da.init(A, g.lda, row_a0, tid);
     else da.init(A, g.lda, row_a0, g.a_rows, tid);
+    auto frags = [&](const char* st, int kk, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
+      ring_frags(st, st + kOpBytes, kk, wm, wn, lane, a, b);
+    };
     if (nk > 0) {
 #pragma unroll
       for (int st = 0; st < kStages - 1; ++st) {
         char* sb = smem + st * kStageBytes;
         const int k0 = k_begin + st * kBK16;
         if constexpr (KIND == KIND_DH) {
-          ta.load(k0, k_end);
-          ta.store(sb);
+          da.load(k0, k_end);
+          da.store(sb);
         } else {
           da.issue(sb, k0, k_end);
         }
@@ -546,7 +565,7 @@ void gemm_kernel(const GemmArgs g) {
       __builtin_amdgcn_s_waitcnt(kWaitAll);
       __builtin_amdgcn_s_barrier();
       bf16x8 a0[4], b0[4], a1[4], b1[4];
-      ring_frags(smem, smem + kOpBytes, 0, wm, wn, lane, a0, b0);
+      frags(smem, 0, a0, b0);
       int slot = 0;  // ring slot of stage kt
       for (int kt = 0; kt < nk; ++kt) {
         const int slot_n = slot + 1 == kStages ? 0 : slot + 1;
@@ -556,10 +575,10 @@ void gemm_kernel(const GemmArgs g) {
         char* sf = smem + slot_f * kStageBytes;
         slot = slot_n;
         const int kf = k_begin + (kt + kStages - 1) * kBK16;
-        if constexpr (KIND == KIND_DH) ta.load(kf, k_end);
+        if constexpr (KIND == KIND_DH) da.load(kf, k_end);
         else da.issue(sf, kf, k_end);
         db.issue(sf + kOpBytes, kf, k_end);
-        ring_frags(sc, sc + kOpBytes, 1, wm, wn, lane, a1, b1);
+        frags(sc, 1, a1, b1);
         mma16(a0, b0, acc);
         // instruction classes: 0x8 MFMA, 0x20 VMEM read, 0x100 DS read, 0x200 DS write
 #pragma unroll
@@ -573,9 +592,9 @@ void gemm_kernel(const GemmArgs g) {
         __builtin_amdgcn_s_waitcnt(kWaitRing);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        ring_frags(sn, sn + kOpBytes, 0, wm, wn, lane, a0, b0);
+        frags(sn, 0, a0, b0);
         mma16(a1, b1, acc);
-        if constexpr (KIND == KIND_DH) ta.store(sf);
+        if constexpr (KIND == KIND_DH) da.store(sf);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
