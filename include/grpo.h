@@ -99,7 +99,8 @@ typedef enum {
   GRPO_K_TOKEN_INDEX = 6,  /* sequence index, per-sequence token counts and weights */
   GRPO_K_LOSS_FINALIZE = 7,/* fixed-order fp64 sum of the per-token loss terms */
   GRPO_K_ADVANTAGES = 8,
-  GRPO_K_COUNT = 9
+  GRPO_K_FRAG_COPY = 9,    /* fragment-major copy of a chunk's hidden states (bf16 path) */
+  GRPO_K_COUNT = 10
 } grpo_kernel_id;
 
 typedef struct grpo_timer grpo_timer; /* opaque, owned by the caller */

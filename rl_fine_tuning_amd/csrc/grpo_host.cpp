@@ -55,7 +55,8 @@ grpo_status validate_cu(const int32_t* cu, int64_t S, int64_t T) {
 // order.  The cost model counts rounds of workgroups over the compute units per unit
 // of split work, plus a small charge per split for the fp32 partials' traffic.
 int dh_ksplit(int64_t chunk_rows, int64_t D, int64_t V, int32_t dtype) {
-  const int64_t tiles = cdiv(D, kTile) * cdiv(chunk_rows, kTile);
+  const int64_t tiles = dtype == GRPO_BF16 ? cdiv(D, kTileA16) * cdiv(chunk_rows, kTileB16)
+                                           : cdiv(D, kTile) * cdiv(chunk_rows, kTile);
   const int64_t kblocks = cdiv(V, k_step(dtype));
   int best = 1;
   double best_cost = 1e300;
@@ -84,8 +85,12 @@ grpo_status make_plan(const grpo_shape* s, int64_t S, bool backward, Plan* out) 
   p.bk = k_step(s->dtype);
   p.C = s->T > 0 ? (s->chunk_tokens < s->T ? s->chunk_tokens : s->T) : 0;
   p.nchunks = p.C > 0 ? cdiv(p.T, p.C) : 0;
-  p.ntiles_v = cdiv(p.V, kTile);
+  const bool bf16 = s->dtype == GRPO_BF16;
+  p.ntiles_v = bf16 ? cdiv(p.V, kTileA16) : cdiv(p.V, kTile);
   p.ldp = cdiv(p.V, 16 / p.esize) * (16 / p.esize);
+  p.rows_pad = cdiv(p.C, kTileB16) * kTileB16;
+  p.ks_d = cdiv(p.D, 16);
+  p.ks_v = cdiv(p.V, 16);
   p.backward = backward;
 
   size_t off = 0;
@@ -99,6 +104,7 @@ grpo_status make_plan(const grpo_shape* s, int64_t S, bool backward, Plan* out) 
   p.off_lse = take(T * 4);
   p.off_pm = take((size_t)p.ntiles_v * C * 4);
   p.off_ps = take((size_t)p.ntiles_v * C * 4);
+  if (bf16) p.off_Hf = take((size_t)p.rows_pad * (size_t)p.ks_d * 16 * 2);
   if (backward) {
     p.off_g = take(T * 4);
     p.off_wl = take(T * 8);
@@ -106,7 +112,7 @@ grpo_status make_plan(const grpo_shape* s, int64_t S, bool backward, Plan* out) 
     p.off_cu = take((size_t)(S + 1) * 4);
     p.off_cnt = take((size_t)S * 4);
     p.off_wseq = take((size_t)S * 8);
-    p.off_P = take(C * (size_t)p.ldp * p.esize);
+    p.off_P = bf16 ? take((size_t)p.rows_pad * (size_t)p.ks_v * 16 * 2) : take(C * (size_t)p.ldp * p.esize);
     if (p.nchunks > 0) {
       p.ksplit_full = dh_ksplit(p.C, p.D, p.V, p.dtype);
       const int64_t tail = p.T - (p.nchunks - 1) * p.C;

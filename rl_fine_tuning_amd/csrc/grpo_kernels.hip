@@ -122,6 +122,8 @@ struct GemmArgs {
   float* part;            // [ksplit][b_rows][D] (ksplit > 1)
   int D;
   int ksplit;
+  int b_ks;           // bf16: k steps (ceil(K / 16)) of the fragment-major B copy
+  int p_ks;           // bf16 PROBS: k steps (ceil(V / 16)) of the fragment-major probabilities
 };
 
 // Tile of this workgroup.  Workgroup i runs on XCD i % 8; each XCD owns a contiguous
@@ -271,21 +273,22 @@ struct TransTile<float> {
   }
 };
 
-// ---- bf16 main loop: a 4-stage LDS ring filled by direct-to-LDS buffer loads.
-//
-// A stage holds 64 bytes (32 bf16) of K for each of the 256 rows of both operands:
-// 16 KB per operand.  Two logical rows share one 128-byte LDS row (row R lives in LDS
-// row R / 2, chunk 4 (R % 2) + c for its 16-byte k chunk c), and the chunk index is
-// XORed with f2(R / 2) so that the 32 consecutive rows of an MFMA operand read, and
-// each 1 KB direct-to-LDS write, touch distinct banks for 32- and for 64-bank LDS.
-#ifndef GRPO_RING_STAGES
-#define GRPO_RING_STAGES 4
-#endif
-constexpr int kStages = GRPO_RING_STAGES;
-constexpr int kOpBytes = 16384;
-constexpr int kStageBytes = 2 * kOpBytes;
-constexpr int kBK16 = 32;  // bf16 elements of K per stage
+// ---- bf16 GEMMs: 128 x 512 workgroup tiles, four waves side by side (wave w owns
+// B rows 128 w .. 128 w + 127 and all 128 A rows).  Only the A tile goes through LDS,
+// a 4-stage ring of 32 bf16 of K per stage (8 KB); each wave streams its own B rows
+// from global memory straight into registers, from a fragment-major copy of B in which
+// every 32-row x 16-k MFMA operand fragment is one contiguous 1 KB block.
+constexpr int kTA = 128;                // A rows per workgroup
+constexpr int kTB = 512;                // B rows per workgroup
+constexpr int kFB = kTB / 32;           // B fragments (32 rows) per tile
+constexpr int kBK16 = 32;               // K per ring stage
+constexpr int kStagesA = 4;
+constexpr int kAStageBytes = kTA * kBK16 * 2;  // 8 KB
 
+// Ring stage layout: two logical rows share one 128-byte LDS row (row R in LDS row
+// R / 2, chunk 4 (R % 2) + c for its 16-byte k chunk c); the chunk index is XORed with
+// f2(R / 2), so that the 32 consecutive rows of an MFMA fragment read, and each 1 KB
+// direct-to-LDS write, touch distinct banks for 32- and 64-bank LDS.
 __device__ __forceinline__ int f2(int y) { return (y & 3) ^ ((y >> 1) & 3); }
 __device__ __forceinline__ int lds_off2(int R, int c) {
   const int y = R >> 1;
@@ -293,17 +296,25 @@ __device__ __forceinline__ int lds_off2(int R, int c) {
 }
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-// Row-major bf16 operand (k contiguous) moved straight into LDS: each wave issues 4
-// buffer loads per stage, each filling 1 KB (8 LDS rows); lane i of a load fills 16
-// bytes at i * 16, so it fetches the row and chunk that the swizzle places there.
-struct DmaTile {
+// Byte offset of element (row, k) in the fragment-major layout of a B operand with
+// ks_count = ceil(K / 16) k steps: [row / 512][k / 16][(row % 512) / 32][lane][8 elements]
+// with lane = row % 32 + 32 ((k % 16) / 8).
+__device__ __forceinline__ int64_t frag_off(int row, int k, int ks_count) {
+  return ((((int64_t)(row >> 9) * ks_count + (k >> 4)) * kFB + ((row & 511) >> 5)) * 64 +
+          ((row & 31) + 32 * ((k >> 3) & 1))) * 16 + (k & 7) * 2;
+}
+
+// Row-major bf16 A operand (k contiguous) moved straight into the ring: each wave issues
+// two buffer loads per stage, each filling 1 KB (16 logical rows); lane i of a load
+// fills 16 bytes at i * 16, so it fetches the row and chunk the swizzle places there.
+struct DmaTileA {
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t lane_off;  // byte offset of this lane's row and chunk from the tile base
-  uint32_t jstride;   // bytes between the 16-row groups of consecutive loads
+  uint32_t jstride;   // bytes between the 16-row groups of the wave's two loads
   int kc;             // k of this lane's chunk within a stage
   int w;              // wave index (uniform)
   __device__ __forceinline__ void init(const __bf16* base, int64_t ld, int row0, int nrows, int tid) {
-    const int rows = max(0, min(nrows - row0, kTile));
+    const int rows = max(0, min(nrows - row0, kTA));
     rsrc = make_rsrc(base + (int64_t)row0 * ld, (int64_t)rows * ld * 2);
     const int i = tid & 63;
     w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -311,86 +322,93 @@ struct DmaTile {
     const int cp = (i & 7) ^ f2(y);
     const int dR = 2 * y + (cp >> 2);
     const int c = cp & 3;
-    lane_off = (uint32_t)((64 * w + dR) * ld * 2 + 16 * c);
+    lane_off = (uint32_t)((32 * w + dR) * ld * 2 + 16 * c);
     jstride = (uint32_t)(16 * ld * 2);
     kc = 8 * c;
   }
-  __device__ __forceinline__ void issue(char* lds_op, int k0, int kend) const {
+  __device__ __forceinline__ void issue(char* lds_stage, int k0, int kend) const {
     const uint32_t v = k0 + kc < kend ? lane_off : kOOB;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(lds_op + (4 * w + j) * 1024), 16, v,
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(lds_stage + (2 * w + j) * 1024), 16, v,
                                                (uint32_t)(j * jstride + k0 * 2), 0, 0);
   }
 };
 
-// Transposed W operand of the dH GEMM for the ring: wave c takes vocabulary rows
-// 8c .. 8c + 7 of the stage, lane q hidden columns 4q .. 4q + 3; the 8 x 4 block is
-// transposed in registers into four 16-byte k chunks, one per hidden column.  In store
-// t lane q writes the chunk of column 4q + (t + q / 4) % 4, which spreads the 64 lanes of
-// one store over all LDS banks.
-struct TransTileRing {
-  uint2 v[8];
+// Transposed A operand of the dH GEMM (W read as W^T): lane (h = lane % 2, q = lane / 2)
+// of wave c loads vocabulary rows 8c + 4h .. + 3 of the stage at hidden columns
+// d0 + 4q .. + 3, transposes the 4 x 4 block in registers and writes four 8-byte half
+// chunks; in store t it writes column 4q + (t + q / 4) % 4, which keeps the 64 lanes of
+// a store on distinct banks.
+struct TransTileA {
+  uint2 v[4];
   const __bf16* W;
   int64_t D;
-  int d0;
-  int c;
-  int q;
+  int d0, c, h, q;
   uint32_t voff;
   __device__ __forceinline__ void init(const __bf16* W_, int64_t D_, int d0_, int tid) {
     W = W_;
     D = D_;
     d0 = d0_;
-    q = tid & 63;
+    const int lane = tid & 63;
     c = tid >> 6;
-    voff = d0 + 4 * q < D ? (uint32_t)((8 * c) * D * 2 + 8 * q) : kOOB;
+    h = lane & 1;
+    q = lane >> 1;
+    voff = d0 + 4 * q < D ? (uint32_t)(((8 * c + 4 * h) * D + 4 * q) * 2) : kOOB;
   }
   __device__ __forceinline__ void load(int k0, int kend) {
     const int64_t rows = min(kend - k0, kBK16);
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(W + (int64_t)k0 * D + d0, (rows * D - d0) * 2);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(W + (int64_t)k0 * D + d0, rows > 0 ? (rows * D - d0) * 2 : 0);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < 4; ++e) {
       const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, voff == kOOB ? 0u : (uint32_t)(e * D * 2), 0);
       v[e] = make_uint2(x.x, x.y);
     }
   }
-  __device__ __forceinline__ void store(char* lds_op) const {
-    uint4 o[4];  // o[i]: the 8 vocabulary entries of hidden column 4q + i
+  __device__ __forceinline__ void store(char* lds_stage) const {
+    uint2 o[4];  // o[i]: vocabulary rows 4h .. 4h + 3 of hidden column 4q + i
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint32_t w[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t lo = (i < 2) ? v[2 * j].x : v[2 * j].y;
-        const uint32_t hi = (i < 2) ? v[2 * j + 1].x : v[2 * j + 1].y;
-        w[j] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-      }
-      o[i] = make_uint4(w[0], w[1], w[2], w[3]);
+      const uint32_t a0 = (i < 2) ? v[0].x : v[0].y, a1 = (i < 2) ? v[1].x : v[1].y;
+      const uint32_t a2 = (i < 2) ? v[2].x : v[2].y, a3 = (i < 2) ? v[3].x : v[3].y;
+      if (i & 1)
+        o[i] = make_uint2((a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u));
+      else
+        o[i] = make_uint2((a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16));
     }
-    // rotate o by r = (q / 4) % 4 with two conditional swaps (no register indexing)
     const int r = (q >> 2) & 3;
     if (r & 1) {
-      const uint4 t0 = o[0];
+      const uint2 t0 = o[0];
       o[0] = o[1]; o[1] = o[2]; o[2] = o[3]; o[3] = t0;
     }
     if (r & 2) {
-      uint4 t0 = o[0]; o[0] = o[2]; o[2] = t0;
+      uint2 t0 = o[0]; o[0] = o[2]; o[2] = t0;
       t0 = o[1]; o[1] = o[3]; o[3] = t0;
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-      *reinterpret_cast<uint4*>(lds_op + lds_off2(4 * q + ((t + r) & 3), c)) = o[t];
+      *reinterpret_cast<uint2*>(lds_stage + lds_off2(4 * q + ((t + r) & 3), c) + 8 * h) = o[t];
   }
 };
 
-// Fragments of one 16-wide k step (kk = 0, 1) of a ring stage for a wave's 128 x 128 tile.
-__device__ __forceinline__ void ring_frags(const char* As, const char* Bs, int kk, int wm, int wn, int lane,
-                                           bf16x8 (&a)[4], bf16x8 (&b)[4]) {
+// A fragments of one 16-wide k step (kk = 0, 1) of a ring stage: rows 32 f + l % 32,
+// k = 16 kk + 8 (l / 32) + 0..7.
+__device__ __forceinline__ void a_frags(const char* As, int kk, int lane, bf16x8 (&a)[4]) {
   const int c = 2 * kk + (lane >> 5);
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    a[f] = *reinterpret_cast<const bf16x8*>(As + lds_off2(wm * 128 + f * 32 + (lane & 31), c));
-    b[f] = *reinterpret_cast<const bf16x8*>(Bs + lds_off2(wn * 128 + f * 32 + (lane & 31), c));
+  for (int f = 0; f < 4; ++f)
+    a[f] = *reinterpret_cast<const bf16x8*>(As + lds_off2(f * 32 + (lane & 31), c));
+}
+
+// This wave's B fragments of one stage (2 k steps x 4 fragments) from the fragment-major
+// copy.  K steps past the end are clamped to the last one: the copy holds finite values
+// everywhere and the A operand of those stages is zero, so they add nothing.
+__device__ __forceinline__ void b_load(const char* Bw, int ks, int ks_count, bf16x8 (&b)[2][4]) {
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const char* p = Bw + (int64_t)min(ks + kk, ks_count - 1) * (kFB * 1024);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) b[kk][f] = *reinterpret_cast<const bf16x8*>(p + f * 1024);
   }
 }
 
@@ -403,11 +421,7 @@ __device__ __forceinline__ void mma16(const bf16x8 (&a)[4], const bf16x8 (&b)[4]
 }
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-// At the mid-iteration barrier of iteration kt the loads of stage kt + 1 must have
-// landed; the loads of the kStages - 2 later iterations (8 per wave each) may still fly.
-constexpr int kWaitVm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xf00; }
 constexpr int kWaitVmLgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70; }
-constexpr int kWaitRing = kWaitVmLgkm0(8 * (kStages - 2));
 constexpr int kWaitAll = 0x0070;
 
 // One LDS stage (128 bytes of K per row) of MFMA work for a wave's 128 x 128 sub-tile.
@@ -496,12 +510,13 @@ __device__ __forceinline__ void load4(const float* src, float (&o)[4]) {
   o[0] = u.x; o[1] = u.y; o[2] = u.z; o[3] = u.w;
 }
 
-// Accumulator element (i, j, r) of lane l: A-row wm*128 + 32 i + 8 (r / 4) + 4 (l / 32) + r % 4,
-// B-row (token) wn*128 + 32 j + l % 32.
+// fp32 GEMMs (inputs kept in fp32): 256 x 256 tiles, 2 x 2 waves of 128 x 128, K staged
+// through a double-buffered LDS tile of 128-byte rows.  Accumulator element (i, j, r) of
+// lane l: A-row wm*128 + 32 i + 8 (r / 4) + 4 (l / 32) + r % 4, B-row (token) wn*128 + 32 j + l % 32.
 template <typename T, int KIND>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(const GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) char smem[sizeof(T) == 2 ? kStages * kStageBytes : 2 * 2 * kTileBytes];
+  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * kTileBytes];
   int ta, tb;
   if (!map_tile(g, ta, tb)) return;
   constexpr int BK = 128 / (int)sizeof(T);
@@ -518,8 +533,7 @@ void gemm_kernel(const GemmArgs g) {
   const int row_b0 = tb * kTile;
   const int k_begin = ks * g.k_len;
   const int k_end = min(g.K, k_begin + g.k_len);
-  constexpr int BKL = sizeof(T) == 2 ? kBK16 : BK;  // K per pipeline stage
-  const int nk = k_end > k_begin ? (k_end - k_begin + BKL - 1) / BKL : 0;
+  const int nk = k_end > k_begin ? (k_end - k_begin + BK - 1) / BK : 0;
 
   floatx16 acc[4][4];
 #pragma unroll
@@ -533,86 +547,7 @@ void gemm_kernel(const GemmArgs g) {
   const T* B = reinterpret_cast<const T*>(g.b);
   // stage s: A operand at smem + s * 64 KB, B operand 32 KB after it
 
-  if constexpr (sizeof(T) == 2) {
-    // 4-stage ring, one stage = 32 bf16 of K.  Iteration kt computes stage kt in two
-    // 16-wide k steps: the loads for stage kt + 3 and the fragments of step 1 are issued
-    // under the MFMAs of step 0; then this wave's loads of stage kt + 1 are waited for and
-    // a barrier publishes every wave's; the fragments of stage kt + 1, step 0 are read
-    // under the MFMAs of step 1.  A ring slot is refilled only after the barrier that
-    // follows its last read.
-    DmaTile db;
-    db.init(B, g.ldb, row_b0, g.b_rows, tid);
-    using ATile = typename std::conditional<KIND == KIND_DH, TransTileRing, DmaTile>::type;
-    ATile da;
-    if constexpr (KIND == KIND_DH) da.init(A, g.lda, row_a0, tid);
-    else da.init(A, g.lda, row_a0, g.a_rows, tid);
-    auto frags = [&](const char* st, int kk, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
-      ring_frags(st, st + kOpBytes, kk, wm, wn, lane, a, b);
-    };
-    if (nk > 0) {
-#pragma unroll
-      for (int st = 0; st < kStages - 1; ++st) {
-        char* sb = smem + st * kStageBytes;
-        const int k0 = k_begin + st * kBK16;
-        if constexpr (KIND == KIND_DH) {
-          da.load(k0, k_end);
-          da.store(sb);
-        } else {
-          da.issue(sb, k0, k_end);
-        }
-        db.issue(sb + kOpBytes, k0, k_end);
-      }
-      __builtin_amdgcn_s_waitcnt(kWaitAll);
-      __builtin_amdgcn_s_barrier();
-      bf16x8 a0[4], b0[4], a1[4], b1[4];
-      frags(smem, 0, a0, b0);
-      int slot = 0;  // ring slot of stage kt
-      for (int kt = 0; kt < nk; ++kt) {
-        const int slot_n = slot + 1 == kStages ? 0 : slot + 1;
-        const int slot_f = slot == 0 ? kStages - 1 : slot - 1;  // stage kt + kStages - 1
-        char* sc = smem + slot * kStageBytes;
-        char* sn = smem + slot_n * kStageBytes;
-        char* sf = smem + slot_f * kStageBytes;
-        slot = slot_n;
-        const int kf = k_begin + (kt + kStages - 1) * kBK16;
-        if constexpr (KIND == KIND_DH) da.load(kf, k_end);
-        else da.issue(sf, kf, k_end);
-        db.issue(sf + kOpBytes, kf, k_end);
-        frags(sc, 1, a1, b1);
-        mma16(a0, b0, acc);
-        // instruction classes: 0x8 MFMA, 0x20 VMEM read, 0x100 DS read, 0x200 DS write
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, KIND == KIND_DH ? 2 : 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(kWaitRing);
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        frags(sn, 0, a0, b0);
-        mma16(a1, b1, acc);
-        if constexpr (KIND == KIND_DH) da.store(sf);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        if constexpr (KIND == KIND_DH) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      __builtin_amdgcn_s_waitcnt(kWaitAll);
-      __builtin_amdgcn_s_barrier();
-    }
-  } else {
+  {
     using ALoader = typename std::conditional<KIND == KIND_DH, TransTile<T>, DirectTile<T>>::type;
     ALoader la;
     DirectTile<T> lb;
@@ -764,6 +699,251 @@ void gemm_kernel(const GemmArgs g) {
         }
     }
   }
+}
+
+// bf16 GEMMs on 128 x 512 tiles.  Accumulator element (i, j, r) of lane l of wave w:
+// A-row 32 i + 8 (r / 4) + 4 (l / 32) + r % 4 of the tile, B-row (token) 128 w + 32 j + l % 32.
+// Iteration kt computes ring stage kt in two 16-wide k steps: the loads of A stage kt + 3
+// and of this wave's B stage kt + 2 and the A fragments of step 1 are issued under the
+// MFMAs of step 0; then the A loads of stage kt + 1 are waited for, a barrier publishes
+// every wave's, and the A fragments of stage kt + 1, step 0 are read under the MFMAs of
+// step 1.  A ring slot is refilled only after the barrier that follows its last read.
+template <int KIND>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm16_kernel(const GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) char smem[kStagesA * kAStageBytes];
+  int ta, tb;
+  if (!map_tile(g, ta, tb)) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int ks = 0, tile_a = ta;
+  if (KIND == KIND_DH) {
+    ks = ta / g.tiles_a_base;
+    tile_a = ta - ks * g.tiles_a_base;
+  }
+  const int row_a0 = tile_a * kTA;
+  const int row_b0 = tb * kTB;
+  const int k_begin = ks * g.k_len;
+  const int k_end = min(g.K, k_begin + g.k_len);
+  const int nk = k_end > k_begin ? (k_end - k_begin + kBK16 - 1) / kBK16 : 0;
+
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const __bf16* A = reinterpret_cast<const __bf16*>(g.a);
+  // this wave's 128 rows of the B tile in the fragment-major copy
+  const char* Bw = reinterpret_cast<const char*>(g.b) + (int64_t)tb * g.b_ks * kFB * 1024 + 4 * w * 1024 + lane * 16;
+  const int ks0 = k_begin >> 4;
+  using ATile = typename std::conditional<KIND == KIND_DH, TransTileA, DmaTileA>::type;
+  ATile at;
+  if constexpr (KIND == KIND_DH) at.init(A, g.lda, row_a0, tid);
+  else at.init(A, g.lda, row_a0, g.a_rows, tid);
+
+  if (nk > 0) {
+#pragma unroll
+    for (int st = 0; st < kStagesA - 1; ++st) {
+      const int k0 = k_begin + st * kBK16;
+      if constexpr (KIND == KIND_DH) {
+        at.load(k0, k_end);
+        at.store(smem + st * kAStageBytes);
+      } else {
+        at.issue(smem + st * kAStageBytes, k0, k_end);
+      }
+    }
+    bf16x8 bb0[2][4], bb1[2][4], bb2[2][4];
+    b_load(Bw, ks0, g.b_ks, bb0);
+    b_load(Bw, ks0 + 2, g.b_ks, bb1);
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    __builtin_amdgcn_s_barrier();
+    bf16x8 a0[4], a1[4];
+    a_frags(smem, 0, lane, a0);
+    int slot = 0;
+    auto step = [&](int kt, bf16x8 (&cur)[2][4], bf16x8 (&nxt)[2][4]) {
+      const int slot_n = slot + 1 == kStagesA ? 0 : slot + 1;
+      const int slot_f = slot == 0 ? kStagesA - 1 : slot - 1;  // stage kt + kStagesA - 1
+      char* sc = smem + slot * kAStageBytes;
+      char* sn = smem + slot_n * kAStageBytes;
+      char* sf = smem + slot_f * kAStageBytes;
+      slot = slot_n;
+      const int kf = k_begin + (kt + kStagesA - 1) * kBK16;
+      if constexpr (KIND == KIND_DH) at.load(kf, k_end);
+      else at.issue(sf, kf, k_end);
+      b_load(Bw, ks0 + 2 * (kt + 2), g.b_ks, nxt);
+      a_frags(sc, 1, lane, a1);
+      mma16(a0, cur[0], acc);
+      // instruction classes: 0x8 MFMA, 0x20 VMEM read, 0x100 DS read, 0x200 DS write
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      // A stage kt + 1 was issued two iterations ago; 28 later loads may still fly
+      __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0(28));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      a_frags(sn, 0, lane, a0);
+      mma16(a1, cur[1], acc);
+      if constexpr (KIND == KIND_DH) at.store(sf);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      if constexpr (KIND == KIND_DH) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // three B register buffers rotate, so the loop runs in groups of three stages; the
+    // stages past the end of K read zeros
+    for (int kt = 0; kt < nk; kt += 3) {
+      step(kt, bb0, bb2);
+      step(kt + 1, bb1, bb0);
+      step(kt + 2, bb2, bb1);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    __builtin_amdgcn_s_barrier();
+  }
+
+  const int hi = lane >> 5;
+  const int col = lane & 31;
+  if constexpr (KIND == KIND_LSE) {
+    // Per token: max and sum of exp over this tile's 128 vocabulary rows (those < V).
+    const bool full = row_a0 + kTA <= g.a_rows;
+    const int vbase = row_a0 + 4 * hi;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int v = vbase + 32 * i + 8 * (r >> 2) + (r & 3);
+          if (full || v < g.a_rows) mx = fmaxf(mx, acc[i][j][r]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float zmax = mx * g.inv_tau;  // inv_tau > 0, so this is the max of z
+      float sum = 0.0f;
+      if (mx > -INFINITY) {
+        const float c1 = g.inv_tau * kLog2e, c0 = -zmax * kLog2e;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int v = vbase + 32 * i + 8 * (r >> 2) + (r & 3);
+            if (full || v < g.a_rows) sum += __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], c1, c0));
+          }
+      }
+      sum += __shfl_xor(sum, 32);
+      const int tok = row_b0 + 128 * w + 32 * j + col;
+      if (hi == 0 && tok < g.b_rows) {
+        g.pm[(int64_t)tok * g.tiles_a + tile_a] = zmax;
+        g.ps[(int64_t)tok * g.tiles_a + tile_a] = sum;
+      }
+    }
+  } else if constexpr (KIND == KIND_PROBS) {
+    // P[token, v] = exp(z - lse[token]) into the fragment-major copy used as the dH GEMM's
+    // B operand; the vocabulary padding up to the next 16 is written as zeros.
+    char* P = reinterpret_cast<char*>(g.p);
+    const int vpad = g.p_ks * 16;
+    const float c1 = g.inv_tau * kLog2e;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tok = row_b0 + 128 * w + 32 * j + col;
+      if (tok >= g.b_rows) continue;
+      const float c0 = -g.lse[tok] * kLog2e;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int v0 = row_a0 + 32 * i + 8 * q + 4 * hi;
+          if (v0 >= vpad) continue;
+          float e[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            e[u] = v0 + u < g.V ? __builtin_amdgcn_exp2f(fmaf(acc[i][j][4 * q + u], c1, c0)) : 0.0f;
+          store4(reinterpret_cast<__bf16*>(P + frag_off(tok, v0, g.p_ks)), e[0], e[1], e[2], e[3]);
+        }
+    }
+  } else {
+    // dH[token, d] = (g / tau) (W[y, d] - acc), or the raw fp32 partial when split.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tok = row_b0 + 128 * w + 32 * j + col;
+      if (tok >= g.b_rows) continue;
+      if (g.ksplit > 1) {
+        float* dst = g.part + ((int64_t)ks * g.b_rows + tok) * g.D;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int d0 = row_a0 + 32 * i + 8 * q + 4 * hi;
+            if (d0 < g.D)
+              *reinterpret_cast<float4*>(dst + d0) =
+                  make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          }
+        continue;
+      }
+      const float gt = g.g[tok];
+      const int y = g.targets[tok];
+      const bool live = gt != 0.0f && y >= 0 && y < g.V;
+      const float scale = gt * g.inv_tau;
+      const __bf16* wrow = reinterpret_cast<const __bf16*>(g.w) + (int64_t)(live ? y : 0) * g.D;
+      __bf16* dst = reinterpret_cast<__bf16*>(g.dh) + (int64_t)tok * g.D;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int d0 = row_a0 + 32 * i + 8 * q + 4 * hi;
+          if (d0 >= g.D) continue;
+          float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+          if (live) {
+            float wv[4];
+            load4(wrow + d0, wv);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) o[u] = scale * (wv[u] - acc[i][j][4 * q + u]);
+          }
+          store4(dst + d0, o[0], o[1], o[2], o[3]);
+        }
+    }
+  }
+}
+
+// Fragment-major copy of `rows` rows of a row-major bf16 matrix [rows, K] (ld = K):
+// one thread per 16-byte unit; rows past `rows` and k past K are zero.
+__global__ __launch_bounds__(256) void frag_copy_kernel(const __bf16* __restrict__ X, int rows, int K, int ks_count,
+                                                        int64_t units, uint4* __restrict__ out) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= units) return;
+  const int l = (int)(u & 63);
+  const int64_t fr = u >> 6;
+  const int fb = (int)(fr % kFB);
+  const int64_t rest = fr / kFB;
+  const int kstep = (int)(rest % ks_count);
+  const int tb = (int)(rest / ks_count);
+  const int row = tb * kTB + fb * 32 + (l & 31);
+  const int k = kstep * 16 + 8 * (l >> 5);
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (row < rows && k < K) v = *reinterpret_cast<const uint4*>(X + (int64_t)row * K + k);
+  out[u] = v;
 }
 
 // ---------------------------------------------------------------------------- small kernels
@@ -1055,15 +1235,28 @@ void launch_gemm(Launcher& L, int kid, const GemmArgs& g) {
   if (g.xcd_axis == 0) per_xcd = (int)cdiv(g.tiles_a, 8) * g.tiles_b;
   else per_xcd = g.tiles_a * (int)cdiv(g.tiles_b, 8);
   const int blocks = 8 * per_xcd;
-  L.run(kid, [&] { hipLaunchKernelGGL((gemm_kernel<T, KIND>), dim3(blocks), dim3(kThreads), 0, L.stream, g); });
+  if constexpr (sizeof(T) == 2)
+    L.run(kid, [&] { hipLaunchKernelGGL((gemm16_kernel<KIND>), dim3(blocks), dim3(kThreads), 0, L.stream, g); });
+  else
+    L.run(kid, [&] { hipLaunchKernelGGL((gemm_kernel<T, KIND>), dim3(blocks), dim3(kThreads), 0, L.stream, g); });
 }
 
+// Tokens' operand of the bf16 logits GEMMs: the fragment-major copy of the chunk's rows.
+inline void enqueue_frag_copy(Launcher& L, const Plan& p, const __bf16* Hc, int rows, char* Hf) {
+  const int64_t units = p.rows_pad / kTileB16 * p.ks_d * kFB * 64;
+  L.run(GRPO_K_FRAG_COPY, [&] {
+    hipLaunchKernelGGL(frag_copy_kernel, dim3(grid1(units, 256)), dim3(256), 0, L.stream, Hc, rows, (int)p.D,
+                       (int)p.ks_d, units, reinterpret_cast<uint4*>(Hf));
+  });
+}
+
+// Arguments shared by the two logits GEMMs of a chunk (W rows x tokens, K = D).
 template <typename T>
-void enqueue_logits_lse(Launcher& L, const Plan& p, const T* W, const T* Hc, int rows, float inv_tau,
-                        float* pm, float* ps) {
+GemmArgs logits_args(const Plan& p, const T* W, const T* Hc, const char* Hf, int rows, float inv_tau) {
   GemmArgs g = {};
+  const bool bf16 = sizeof(T) == 2;
   g.a = W;
-  g.b = Hc;
+  g.b = bf16 ? static_cast<const void*>(Hf) : static_cast<const void*>(Hc);
   g.lda = p.D;
   g.ldb = p.D;
   g.a_rows = (int)p.V;
@@ -1072,16 +1265,16 @@ void enqueue_logits_lse(Launcher& L, const Plan& p, const T* W, const T* Hc, int
   g.k_len = (int)p.D;
   g.tiles_a_base = (int)p.ntiles_v;
   g.tiles_a = (int)p.ntiles_v;
-  g.tiles_b = (int)cdiv(rows, kTile);
+  g.tiles_b = (int)cdiv(rows, bf16 ? kTileB16 : kTile);
   g.xcd_axis = 0;
-  g.group_b = 8;
+  g.group_b = bf16 ? 4 : 8;
   g.inv_tau = inv_tau;
-  g.pm = pm;
-  g.ps = ps;
   g.V = (int)p.V;
   g.D = (int)p.D;
   g.ksplit = 1;
-  launch_gemm<T, KIND_LSE>(L, GRPO_K_LOGITS_LSE, g);
+  g.b_ks = (int)p.ks_d;
+  g.p_ks = (int)p.ks_v;
+  return g;
 }
 
 template <typename T>
@@ -1092,6 +1285,7 @@ grpo_status logp_impl(const Plan& p, const grpo_shape* shape, const T* H, const 
   float* lse = lse_out ? lse_out : reinterpret_cast<float*>(ws + p.off_lse);
   float* pm = reinterpret_cast<float*>(ws + p.off_pm);
   float* ps = reinterpret_cast<float*>(ws + p.off_ps);
+  char* Hf = ws + p.off_Hf;
   L.run(GRPO_K_TARGET_LOGIT, [&] {
     hipLaunchKernelGGL((target_logit_kernel<T>), dim3(grid1(p.T, 4)), dim3(256), 0, L.stream, H, W, targets,
                        (int)p.T, (int)p.D, (int)p.V, inv_tau, zy);
@@ -1099,7 +1293,11 @@ grpo_status logp_impl(const Plan& p, const grpo_shape* shape, const T* H, const 
   for (int64_t k = 0; k < p.nchunks; ++k) {
     const int64_t t0 = k * p.C;
     const int rows = (int)(p.T - t0 < p.C ? p.T - t0 : p.C);
-    enqueue_logits_lse<T>(L, p, W, H + t0 * p.D, rows, inv_tau, pm, ps);
+    if constexpr (sizeof(T) == 2) enqueue_frag_copy(L, p, H + t0 * p.D, rows, Hf);
+    GemmArgs g = logits_args<T>(p, W, H + t0 * p.D, Hf, rows, inv_tau);
+    g.pm = pm;
+    g.ps = ps;
+    launch_gemm<T, KIND_LSE>(L, GRPO_K_LOGITS_LSE, g);
     MergeArgs m = {};
     m.pm = pm;
     m.ps = ps;
@@ -1133,6 +1331,7 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, const grpo_loss_pa
   int32_t* cnt = reinterpret_cast<int32_t*>(ws + p.off_cnt);
   double* wseq = reinterpret_cast<double*>(ws + p.off_wseq);
   T* P = reinterpret_cast<T*>(ws + p.off_P);
+  char* Hf = ws + p.off_Hf;
   float* part = reinterpret_cast<float*>(ws + p.off_part);
   const int S = (int)p.S;
 
@@ -1155,7 +1354,11 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, const grpo_loss_pa
     const int64_t t0 = k * p.C;
     const int rows = (int)(p.T - t0 < p.C ? p.T - t0 : p.C);
     const T* Hc = H + t0 * p.D;
-    enqueue_logits_lse<T>(L, p, W, Hc, rows, inv_tau, pm, ps);
+    if constexpr (sizeof(T) == 2) enqueue_frag_copy(L, p, Hc, rows, Hf);
+    GemmArgs gl = logits_args<T>(p, W, Hc, Hf, rows, inv_tau);
+    gl.pm = pm;
+    gl.ps = ps;
+    launch_gemm<T, KIND_LSE>(L, GRPO_K_LOGITS_LSE, gl);
 
     MergeArgs m = {};
     m.pm = pm;
@@ -1184,27 +1387,10 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, const grpo_loss_pa
     });
 
     // Recompute the chunk's logits and write its softmax probabilities.
-    GemmArgs gp = {};
-    gp.a = W;
-    gp.b = Hc;
-    gp.lda = p.D;
-    gp.ldb = p.D;
-    gp.a_rows = (int)p.V;
-    gp.b_rows = rows;
-    gp.K = (int)p.D;
-    gp.k_len = (int)p.D;
-    gp.tiles_a_base = (int)p.ntiles_v;
-    gp.tiles_a = (int)p.ntiles_v;
-    gp.tiles_b = (int)cdiv(rows, kTile);
-    gp.xcd_axis = 0;
-    gp.group_b = 8;
-    gp.inv_tau = inv_tau;
+    GemmArgs gp = logits_args<T>(p, W, Hc, Hf, rows, inv_tau);
     gp.lse = lse + t0;
     gp.p = P;
     gp.ldp = p.ldp;
-    gp.V = (int)p.V;
-    gp.D = (int)p.D;
-    gp.ksplit = 1;
     launch_gemm<T, KIND_PROBS>(L, GRPO_K_PROBS, gp);
 
     // dH^T tiles: hidden x tokens, K = vocabulary, split over the vocabulary if needed.
@@ -1220,11 +1406,13 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, const grpo_loss_pa
     gd.b_rows = rows;
     gd.K = (int)p.V;
     gd.k_len = k_len;
-    gd.tiles_a_base = (int)cdiv(p.D, kTile);
+    const bool bf16 = sizeof(T) == 2;
+    gd.tiles_a_base = (int)cdiv(p.D, bf16 ? kTileA16 : kTile);
     gd.tiles_a = gd.tiles_a_base * ksplit;
-    gd.tiles_b = (int)cdiv(rows, kTile);
+    gd.tiles_b = (int)cdiv(rows, bf16 ? kTileB16 : kTile);
     gd.xcd_axis = 1;
-    gd.group_b = 2;
+    gd.group_b = bf16 ? 1 : 2;
+    gd.b_ks = (int)p.ks_v;
     gd.inv_tau = inv_tau;
     gd.g = gbuf + t0;
     gd.targets = targets + t0;

@@ -9,9 +9,12 @@
 
 namespace grpo {
 
-// MFMA tile edge: a workgroup computes a 256 x 256 output tile (vocabulary x tokens for
-// the logits GEMMs, hidden x tokens for the dH GEMM).
+// MFMA workgroup tiles.  fp32 inputs: 256 x 256 (vocabulary or hidden x tokens).  bf16
+// inputs: 128 rows of the first operand x 512 tokens, with the tokens' operand in a
+// fragment-major copy (16-element k steps, 512-row tiles).
 constexpr int kTile = 256;
+constexpr int kTileA16 = 128;
+constexpr int kTileB16 = 512;
 // MI355X compute units; sizes the vocabulary split of the dH GEMM for small chunks.
 constexpr int kNumCUs = 256;
 constexpr int kMaxKSplit = 8;
@@ -29,13 +32,16 @@ struct Plan {
   int32_t dtype = 0;
   int esize = 0, bk = 0;
   int64_t ntiles_v = 0;   // vocabulary tiles = (max, sum-exp) partials per token
-  int64_t ldp = 0;        // row stride (elements) of the chunk probability matrix
+  int64_t ldp = 0;        // fp32: row stride (elements) of the chunk probability matrix
+  int64_t rows_pad = 0;   // bf16: chunk rows rounded up to the 512-row tile
+  int64_t ks_d = 0;       // bf16: k steps of 16 over D (fragment-major hidden states)
+  int64_t ks_v = 0;       // bf16: k steps of 16 over V (fragment-major probabilities)
   int ksplit_full = 1;    // dH vocabulary split for a full chunk
   int ksplit_tail = 1;    // ... and for the last, shorter chunk
   bool backward = false;
   size_t off_zy = 0, off_lse = 0, off_pm = 0, off_ps = 0;
   size_t off_g = 0, off_wl = 0, off_seq = 0, off_cu = 0, off_cnt = 0, off_wseq = 0;
-  size_t off_P = 0, off_part = 0;
+  size_t off_P = 0, off_part = 0, off_Hf = 0;
   size_t total = 0;
 };
 
