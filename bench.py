@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--chunk", type=int, default=0, help="override the workload's chunk tokens")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for HBM counter scaling)")
@@ -161,7 +161,7 @@ def main():
                   "dh_gemm": sum(2.0 * r * D * V for r in rows)}
     kernels = {}
     for k in ("target_logit", "logits_lse", "merge", "probs", "dh_gemm", "dh_reduce", "token_index",
-              "loss_finalize"):
+              "loss_finalize", "frag_copy", "transpose_w"):
         ms, n, dropped = timer.read(k)
         kernels[k] = {"ms_total": ms, "launches": n}
     dominant = max(gemm_flops, key=lambda k: kernels[k]["ms_total"])

@@ -100,7 +100,8 @@ typedef enum {
   GRPO_K_LOSS_FINALIZE = 7,/* fixed-order fp64 sum of the per-token loss terms */
   GRPO_K_ADVANTAGES = 8,
   GRPO_K_FRAG_COPY = 9,    /* fragment-major copy of a chunk's hidden states (bf16 path) */
-  GRPO_K_COUNT = 10
+  GRPO_K_TRANSPOSE_W = 10, /* transposed copy of W for the dH GEMM (bf16, when it fits) */
+  GRPO_K_COUNT = 11
 } grpo_kernel_id;
 
 typedef struct grpo_timer grpo_timer; /* opaque, owned by the caller */
@@ -108,7 +109,9 @@ typedef struct grpo_timer grpo_timer; /* opaque, owned by the caller */
 /* Bytes of workspace that grpo_logp_fwd (with_backward = 0) or grpo_loss_fwd_bwd
  * (with_backward = 1) needs for this shape and num_seqs sequences.  Returns 0 for an
  * invalid shape.  Bounded by chunk_tokens * V * 4 (one chunk's fp32 logits) plus
- * O(T + chunk_tokens * (V / 256 + D)) bytes of per-token state. */
+ * O(T + chunk_tokens * (V / 128 + D)) bytes of per-token state.  For bf16 the
+ * backward also keeps a transposed copy of W (D * V * 2 bytes) when the total then
+ * stays within chunk_tokens * V * 4. */
 size_t grpo_workspace_bytes(const grpo_shape* shape, int64_t num_seqs, int with_backward);
 
 /* Per-token log-probabilities of the targets ([P4]: chunked hidden-state selective

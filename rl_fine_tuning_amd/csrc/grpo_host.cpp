@@ -126,6 +126,14 @@ grpo_status make_plan(const grpo_shape* s, int64_t S, bool backward, Plan* out) 
       if (tpart > part) part = tpart;
     }
     p.off_part = take(part);
+    // A transposed copy of W for the dH GEMM's direct-to-LDS loads, only when the whole
+    // workspace still fits in one chunk's fp32 logits.
+    p.ldt = cdiv(p.V, 8) * 8;
+    const size_t wt = align_up((size_t)p.D * (size_t)p.ldt * 2);
+    if (bf16 && p.nchunks > 0 && off + wt <= C * (size_t)p.V * 4) {
+      p.use_wt = true;
+      p.off_WT = take(wt);
+    }
   }
   p.total = off;
   *out = p;

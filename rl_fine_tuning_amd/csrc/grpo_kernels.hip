@@ -58,7 +58,9 @@ constexpr int kRowBytes = 128;                   // one LDS tile row: 8 chunks o
 constexpr int kTileBytes = kTile * kRowBytes;    // one operand, one stage: 32 KB
 constexpr float kLog2e = 1.4426950408889634f;
 
-enum Kind { KIND_LSE = 0, KIND_PROBS = 1, KIND_DH = 2 };
+// KIND_DH reads W for the dH GEMM transposed on the fly; KIND_DHT (bf16) reads a
+// transposed copy W^T [D, ldt] with the direct-to-LDS loads of the logits GEMMs.
+enum Kind { KIND_LSE = 0, KIND_PROBS = 1, KIND_DH = 2, KIND_DHT = 3 };
 
 // Byte offset of 16-byte chunk c of row r inside a [256 rows x 8 chunks] LDS tile.
 __device__ __forceinline__ int lds_off(int r, int c) {
@@ -717,8 +719,10 @@ void gemm16_kernel(const GemmArgs g) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr bool kDH = KIND == KIND_DH || KIND == KIND_DHT;  // dH epilogue, split vocabulary
+  constexpr bool kTrans = KIND == KIND_DH;                   // A transposed in registers
   int ks = 0, tile_a = ta;
-  if (KIND == KIND_DH) {
+  if (kDH) {
     ks = ta / g.tiles_a_base;
     tile_a = ta - ks * g.tiles_a_base;
   }
@@ -740,16 +744,16 @@ void gemm16_kernel(const GemmArgs g) {
   // this wave's 128 rows of the B tile in the fragment-major copy
   const char* Bw = reinterpret_cast<const char*>(g.b) + (int64_t)tb * g.b_ks * kFB * 1024 + 4 * w * 1024 + lane * 16;
   const int ks0 = k_begin >> 4;
-  using ATile = typename std::conditional<KIND == KIND_DH, TransTileA, DmaTileA>::type;
+  using ATile = typename std::conditional<kTrans, TransTileA, DmaTileA>::type;
   ATile at;
-  if constexpr (KIND == KIND_DH) at.init(A, g.lda, row_a0, tid);
+  if constexpr (kTrans) at.init(A, g.lda, row_a0, tid);
   else at.init(A, g.lda, row_a0, g.a_rows, tid);
 
   if (nk > 0) {
 #pragma unroll
     for (int st = 0; st < kStagesA - 1; ++st) {
       const int k0 = k_begin + st * kBK16;
-      if constexpr (KIND == KIND_DH) {
+      if constexpr (kTrans) {
         at.load(k0, k_end);
         at.store(smem + st * kAStageBytes);
       } else {
@@ -772,7 +776,7 @@ void gemm16_kernel(const GemmArgs g) {
       char* sf = smem + slot_f * kAStageBytes;
       slot = slot_n;
       const int kf = k_begin + (kt + kStagesA - 1) * kBK16;
-      if constexpr (KIND == KIND_DH) at.load(kf, k_end);
+      if constexpr (kTrans) at.load(kf, k_end);
       else at.issue(sf, kf, k_end);
       b_load(Bw, ks0 + 2 * (kt + 2), g.b_ks, nxt);
       a_frags(sc, 1, lane, a1);
@@ -797,13 +801,13 @@ void gemm16_kernel(const GemmArgs g) {
       __builtin_amdgcn_sched_barrier(0);
       a_frags(sn, 0, lane, a0);
       mma16(a1, cur[1], acc);
-      if constexpr (KIND == KIND_DH) at.store(sf);
+      if constexpr (kTrans) at.store(sf);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      if constexpr (KIND == KIND_DH) {
+      if constexpr (kTrans) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
@@ -944,6 +948,33 @@ __global__ __launch_bounds__(256) void frag_copy_kernel(const __bf16* __restrict
   uint4 v = make_uint4(0u, 0u, 0u, 0u);
   if (row < rows && k < K) v = *reinterpret_cast<const uint4*>(X + (int64_t)row * K + k);
   out[u] = v;
+}
+
+// W^T [D, ldt] from W [V, D] (bf16), zeros in columns V .. ldt - 1: each thread moves an
+// 8 x 8 block (8 vocabulary rows x 8 hidden columns), transposed in registers.  Lane
+// l = 8 bv + bd of a wave covers vocabulary rows 8 bv .. and hidden columns 8 bd .. of
+// the wave's 64 x 64 block, so the reads (lanes along d) and the writes (lanes along v)
+// both move 128 contiguous bytes per 8 lanes.
+__global__ __launch_bounds__(256) void transpose_w_kernel(const __bf16* __restrict__ W, int V, int D, int ldt,
+                                                          __bf16* __restrict__ WT) {
+  const int lane = threadIdx.x & 63;
+  const int v0 = blockIdx.x * 256 + (threadIdx.x >> 6) * 64 + 8 * (lane >> 3);
+  const int d0 = blockIdx.y * 64 + 8 * (lane & 7);
+  if (v0 >= ldt || d0 >= D) return;
+  uint4 r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    r[i] = v0 + i < V ? *reinterpret_cast<const uint4*>(W + (int64_t)(v0 + i) * D + d0) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t o[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t a = u4get(r[2 * m], j >> 1), b = u4get(r[2 * m + 1], j >> 1);
+      o[m] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+    }
+    *reinterpret_cast<uint4*>(WT + (int64_t)(d0 + j) * ldt + v0) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
 }
 
 // ---------------------------------------------------------------------------- small kernels
@@ -1334,6 +1365,9 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, const grpo_loss_pa
   char* Hf = ws + p.off_Hf;
   float* part = reinterpret_cast<float*>(ws + p.off_part);
   const int S = (int)p.S;
+  // bf16 with room in the workspace: the dH GEMM reads W through a transposed copy
+  const bool use_wt = sizeof(T) == 2 && p.use_wt;
+  const T* WT = reinterpret_cast<const T*>(ws + p.off_WT);
 
   if (hipMemcpyAsync(cu, cu_host, sizeof(int32_t) * (S + 1), hipMemcpyHostToDevice, L.stream) != hipSuccess)
     return GRPO_E_HIP;
@@ -1349,6 +1383,13 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, const grpo_loss_pa
       hipLaunchKernelGGL((target_logit_kernel<T>), dim3(grid1(p.T, 4)), dim3(256), 0, L.stream, H, W, targets,
                          (int)p.T, (int)p.D, (int)p.V, inv_tau, zy);
     });
+    if (use_wt) {
+      L.run(GRPO_K_TRANSPOSE_W, [&] {
+        hipLaunchKernelGGL(transpose_w_kernel, dim3(grid1(p.ldt, 256), grid1(p.D, 64)), dim3(256), 0, L.stream,
+                           reinterpret_cast<const __bf16*>(W), (int)p.V, (int)p.D, (int)p.ldt,
+                           reinterpret_cast<__bf16*>(const_cast<T*>(WT)));
+      });
+    }
   }
   for (int64_t k = 0; k < p.nchunks; ++k) {
     const int64_t t0 = k * p.C;
@@ -1398,9 +1439,9 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, const grpo_loss_pa
     const int k_len = (int)(cdiv(cdiv(p.V, ks_plan), p.bk) * p.bk);
     const int ksplit = (int)cdiv(p.V, k_len);
     GemmArgs gd = {};
-    gd.a = W;
+    gd.a = use_wt ? WT : W;
     gd.b = P;
-    gd.lda = p.D;
+    gd.lda = use_wt ? p.ldt : p.D;
     gd.ldb = p.ldp;
     gd.a_rows = (int)p.D;
     gd.b_rows = rows;
@@ -1422,7 +1463,8 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, const grpo_loss_pa
     gd.V = (int)p.V;
     gd.D = (int)p.D;
     gd.ksplit = ksplit;
-    launch_gemm<T, KIND_DH>(L, GRPO_K_DH_GEMM, gd);
+    if (use_wt) launch_gemm<T, KIND_DHT>(L, GRPO_K_DH_GEMM, gd);
+    else launch_gemm<T, KIND_DH>(L, GRPO_K_DH_GEMM, gd);
     if (ksplit > 1) {
       L.run(GRPO_K_DH_REDUCE, [&] {
         hipLaunchKernelGGL((dh_reduce_kernel<T>), dim3(grid1((int64_t)rows * (p.D / 4), 256)), dim3(256), 0,

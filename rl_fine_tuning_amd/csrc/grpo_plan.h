@@ -36,12 +36,14 @@ struct Plan {
   int64_t rows_pad = 0;   // bf16: chunk rows rounded up to the 512-row tile
   int64_t ks_d = 0;       // bf16: k steps of 16 over D (fragment-major hidden states)
   int64_t ks_v = 0;       // bf16: k steps of 16 over V (fragment-major probabilities)
+  int64_t ldt = 0;        // bf16: row stride of the transposed W copy (V rounded up to 8)
+  bool use_wt = false;    // bf16: the dH GEMM reads W^T from the workspace
   int ksplit_full = 1;    // dH vocabulary split for a full chunk
   int ksplit_tail = 1;    // ... and for the last, shorter chunk
   bool backward = false;
   size_t off_zy = 0, off_lse = 0, off_pm = 0, off_ps = 0;
   size_t off_g = 0, off_wl = 0, off_seq = 0, off_cu = 0, off_cnt = 0, off_wseq = 0;
-  size_t off_P = 0, off_part = 0, off_Hf = 0;
+  size_t off_P = 0, off_part = 0, off_Hf = 0, off_WT = 0;
   size_t total = 0;
 };
 

@@ -130,3 +130,23 @@ def test_fp32_ragged_with_mask():
     torch.cuda.synchronize()
     r = check_loss_outputs(k, got)
     assert r["dH_rel"] <= 1e-4
+
+
+@pytest.mark.parametrize("V,chunk,expect_wt", [(10000, 512, 1), (1000, 256, 0)])
+def test_dh_gemm_both_operand_paths(V, chunk, expect_wt):
+    # With room in the workspace (within one chunk's fp32 logits) the dH GEMM reads a
+    # transposed copy of W (one transpose launch per call); otherwise it transposes W tiles
+    # in registers.  Both against the oracle.
+    from rl_fine_tuning_amd import Timer
+    k = case(31, D=256, V=V, lengths=[300, 400, 324], G=3, chunk=chunk, old_std=0.3, ref_std=0.3)
+    say(f"loss dH operand path V={V} chunk={chunk} expect transposed copy={expect_wt}")
+    d = to_device(k)
+    tm = Timer(256)
+    prm = dict(k["prm"])
+    got = grpo_loss_fwd_bwd(d["H"], d["W"], d["targets"], k["c"].cu, d["old"], d["ref"], d["adv"], chunk,
+                            temperature=k["tau"], mask=d["mask"], timer=tm, **prm)
+    torch.cuda.synchronize()
+    assert tm.read("transpose_w")[1] == expect_wt
+    tm.close()
+    r = check_loss_outputs(k, got)
+    say(f"  logp err {r['logp_err']:.2e} dH rel {r['dH_rel']:.2e}")
