@@ -275,17 +275,22 @@ struct TransTile<float> {
   }
 };
 
-// ---- bf16 GEMMs: 128 x 512 workgroup tiles, four waves side by side (wave w owns
-// B rows 128 w .. 128 w + 127 and all 128 A rows).  Only the A tile goes through LDS,
-// a 4-stage ring of 32 bf16 of K per stage (8 KB); each wave streams its own B rows
+// ---- bf16 GEMMs: 256 x 256 workgroup tiles, four waves side by side (wave w owns
+// B rows 64 w .. 64 w + 63 and all 256 A rows).  Only the A tile goes through LDS,
+// a 4-stage ring of 32 bf16 of K per stage (16 KB); each wave streams its own B rows
 // from global memory straight into registers, from a fragment-major copy of B in which
-// every 32-row x 16-k MFMA operand fragment is one contiguous 1 KB block.
-constexpr int kTA = 128;                // A rows per workgroup
-constexpr int kTB = 512;                // B rows per workgroup
+// every 32-row x 16-k MFMA operand fragment is one contiguous 1 KB block.  Per 32 of K
+// a workgroup moves 32 KB from L2 (16 KB of A, 4 x 4 KB of B) for 4.2 MFLOP.
+constexpr int kTA = kTileA16;           // A rows per workgroup
+constexpr int kTB = kTileB16;           // B rows per workgroup
 constexpr int kFB = kTB / 32;           // B fragments (32 rows) per tile
+constexpr int kFA = kTA / 32;           // A fragments per tile
+constexpr int kFBW = kFB / 4;           // B fragments per wave
 constexpr int kBK16 = 32;               // K per ring stage
 constexpr int kStagesA = 4;
-constexpr int kAStageBytes = kTA * kBK16 * 2;  // 8 KB
+constexpr int kAStageBytes = kTA * kBK16 * 2;  // 16 KB
+constexpr int kDmaA = kAStageBytes / 1024 / 4; // 1 KB direct-to-LDS loads per wave per stage
+static_assert(kTA == 256 && kTB == 256, "the wave layout below assumes 256 x 256 tiles");
 
 // Ring stage layout: two logical rows share one 128-byte LDS row (row R in LDS row
 // R / 2, chunk 4 (R % 2) + c for its 16-byte k chunk c); the chunk index is XORed with
@@ -299,20 +304,22 @@ __device__ __forceinline__ int lds_off2(int R, int c) {
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 // Byte offset of element (row, k) in the fragment-major layout of a B operand with
-// ks_count = ceil(K / 16) k steps: [row / 512][k / 16][(row % 512) / 32][lane][8 elements]
+// ks_count = ceil(K / 16) k steps: [row / 256][k / 16][(row % 256) / 32][lane][8 elements]
 // with lane = row % 32 + 32 ((k % 16) / 8).
 __device__ __forceinline__ int64_t frag_off(int row, int k, int ks_count) {
-  return ((((int64_t)(row >> 9) * ks_count + (k >> 4)) * kFB + ((row & 511) >> 5)) * 64 +
-          ((row & 31) + 32 * ((k >> 3) & 1))) * 16 + (k & 7) * 2;
+  const unsigned r = (unsigned)row;
+  return ((((int64_t)(r / kTB) * ks_count + (k >> 4)) * kFB + ((r % kTB) >> 5)) * 64 +
+          ((r & 31) + 32 * ((k >> 3) & 1))) * 16 + (k & 7) * 2;
 }
 
-// Row-major bf16 A operand (k contiguous) moved straight into the ring: each wave issues
-// two buffer loads per stage, each filling 1 KB (16 logical rows); lane i of a load
-// fills 16 bytes at i * 16, so it fetches the row and chunk the swizzle places there.
+// Row-major bf16 A operand (k contiguous) moved straight into the ring: wave w issues
+// kDmaA buffer loads per stage, load j filling 1 KB (16 logical rows 64 w + 16 j ..);
+// lane i of a load fills 16 bytes at i * 16, so it fetches the row and chunk the
+// swizzle places there (the swizzle depends on the LDS row modulo 8 only).
 struct DmaTileA {
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t lane_off;  // byte offset of this lane's row and chunk from the tile base
-  uint32_t jstride;   // bytes between the 16-row groups of the wave's two loads
+  uint32_t jstride;   // bytes between the 16-row groups of the wave's loads
   int kc;             // k of this lane's chunk within a stage
   int w;              // wave index (uniform)
   __device__ __forceinline__ void init(const __bf16* base, int64_t ld, int row0, int nrows, int tid) {
@@ -324,30 +331,30 @@ struct DmaTileA {
     const int cp = (i & 7) ^ f2(y);
     const int dR = 2 * y + (cp >> 2);
     const int c = cp & 3;
-    lane_off = (uint32_t)((32 * w + dR) * ld * 2 + 16 * c);
+    lane_off = (uint32_t)(((kTA / 4) * w + dR) * ld * 2 + 16 * c);
     jstride = (uint32_t)(16 * ld * 2);
     kc = 8 * c;
   }
   __device__ __forceinline__ void issue(char* lds_stage, int k0, int kend) const {
     const uint32_t v = k0 + kc < kend ? lane_off : kOOB;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(lds_stage + (2 * w + j) * 1024), 16, v,
+    for (int j = 0; j < kDmaA; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(lds_stage + (kDmaA * w + j) * 1024), 16, v,
                                                (uint32_t)(j * jstride + k0 * 2), 0, 0);
   }
 };
 
 // Transposed A operand of the dH GEMM (W read as W^T): lane (h = lane % 2, q = lane / 2)
 // of wave c loads vocabulary rows 8c + 4h .. + 3 of the stage at hidden columns
-// d0 + 4q .. + 3, transposes the 4 x 4 block in registers and writes four 8-byte half
-// chunks; in store t it writes column 4q + (t + q / 4) % 4, which keeps the 64 lanes of
-// a store on distinct banks.
+// d0 + 128 p + 4q .. + 3 (p = 0, 1), transposes each 4 x 4 block in registers and
+// writes four 8-byte half chunks per block; in store t it writes column 4q + (t + q / 4) % 4,
+// which keeps the 64 lanes of a store on distinct banks.
 struct TransTileA {
-  uint2 v[4];
+  uint2 v[2][4];
   const __bf16* W;
   int64_t D;
   int d0, c, h, q;
-  uint32_t voff;
+  uint32_t voff[2];
   __device__ __forceinline__ void init(const __bf16* W_, int64_t D_, int d0_, int tid) {
     W = W_;
     D = D_;
@@ -356,69 +363,78 @@ struct TransTileA {
     c = tid >> 6;
     h = lane & 1;
     q = lane >> 1;
-    voff = d0 + 4 * q < D ? (uint32_t)(((8 * c + 4 * h) * D + 4 * q) * 2) : kOOB;
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      voff[p] = d0 + 128 * p + 4 * q < D ? (uint32_t)(((8 * c + 4 * h) * D + 128 * p + 4 * q) * 2) : kOOB;
   }
   __device__ __forceinline__ void load(int k0, int kend) {
     const int64_t rows = min(kend - k0, kBK16);
     const __amdgpu_buffer_rsrc_t r = make_rsrc(W + (int64_t)k0 * D + d0, rows > 0 ? (rows * D - d0) * 2 : 0);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, voff == kOOB ? 0u : (uint32_t)(e * D * 2), 0);
-      v[e] = make_uint2(x.x, x.y);
-    }
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const u32x2 x =
+            __builtin_amdgcn_raw_buffer_load_b64(r, voff[p], voff[p] == kOOB ? 0u : (uint32_t)(e * D * 2), 0);
+        v[p][e] = make_uint2(x.x, x.y);
+      }
   }
   __device__ __forceinline__ void store(char* lds_stage) const {
-    uint2 o[4];  // o[i]: vocabulary rows 4h .. 4h + 3 of hidden column 4q + i
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t a0 = (i < 2) ? v[0].x : v[0].y, a1 = (i < 2) ? v[1].x : v[1].y;
-      const uint32_t a2 = (i < 2) ? v[2].x : v[2].y, a3 = (i < 2) ? v[3].x : v[3].y;
-      if (i & 1)
-        o[i] = make_uint2((a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u));
-      else
-        o[i] = make_uint2((a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16));
-    }
     const int r = (q >> 2) & 3;
-    if (r & 1) {
-      const uint2 t0 = o[0];
-      o[0] = o[1]; o[1] = o[2]; o[2] = o[3]; o[3] = t0;
-    }
-    if (r & 2) {
-      uint2 t0 = o[0]; o[0] = o[2]; o[2] = t0;
-      t0 = o[1]; o[1] = o[3]; o[3] = t0;
-    }
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      *reinterpret_cast<uint2*>(lds_stage + lds_off2(4 * q + ((t + r) & 3), c) + 8 * h) = o[t];
+    for (int p = 0; p < 2; ++p) {
+      uint2 o[4];  // o[i]: vocabulary rows 4h .. 4h + 3 of hidden column 128 p + 4q + i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t a0 = (i < 2) ? v[p][0].x : v[p][0].y, a1 = (i < 2) ? v[p][1].x : v[p][1].y;
+        const uint32_t a2 = (i < 2) ? v[p][2].x : v[p][2].y, a3 = (i < 2) ? v[p][3].x : v[p][3].y;
+        if (i & 1)
+          o[i] = make_uint2((a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u));
+        else
+          o[i] = make_uint2((a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16));
+      }
+      if (r & 1) {
+        const uint2 t0 = o[0];
+        o[0] = o[1]; o[1] = o[2]; o[2] = o[3]; o[3] = t0;
+      }
+      if (r & 2) {
+        uint2 t0 = o[0]; o[0] = o[2]; o[2] = t0;
+        t0 = o[1]; o[1] = o[3]; o[3] = t0;
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        *reinterpret_cast<uint2*>(lds_stage + lds_off2(128 * p + 4 * q + ((t + r) & 3), c) + 8 * h) = o[t];
+    }
   }
 };
 
 // A fragments of one 16-wide k step (kk = 0, 1) of a ring stage: rows 32 f + l % 32,
 // k = 16 kk + 8 (l / 32) + 0..7.
-__device__ __forceinline__ void a_frags(const char* As, int kk, int lane, bf16x8 (&a)[4]) {
+__device__ __forceinline__ void a_frags(const char* As, int kk, int lane, bf16x8 (&a)[kFA]) {
   const int c = 2 * kk + (lane >> 5);
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
+  for (int f = 0; f < kFA; ++f)
     a[f] = *reinterpret_cast<const bf16x8*>(As + lds_off2(f * 32 + (lane & 31), c));
 }
 
-// This wave's B fragments of one stage (2 k steps x 4 fragments) from the fragment-major
+// This wave's B fragments of one stage (2 k steps x 2 fragments) from the fragment-major
 // copy.  K steps past the end are clamped to the last one: the copy holds finite values
 // everywhere and the A operand of those stages is zero, so they add nothing.
-__device__ __forceinline__ void b_load(const char* Bw, int ks, int ks_count, bf16x8 (&b)[2][4]) {
+__device__ __forceinline__ void b_load(const char* Bw, int ks, int ks_count, bf16x8 (&b)[2][kFBW]) {
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     const char* p = Bw + (int64_t)min(ks + kk, ks_count - 1) * (kFB * 1024);
 #pragma unroll
-    for (int f = 0; f < 4; ++f) b[kk][f] = *reinterpret_cast<const bf16x8*>(p + f * 1024);
+    for (int f = 0; f < kFBW; ++f) b[kk][f] = *reinterpret_cast<const bf16x8*>(p + f * 1024);
   }
 }
 
-__device__ __forceinline__ void mma16(const bf16x8 (&a)[4], const bf16x8 (&b)[4], floatx16 (&acc)[4][4]) {
+__device__ __forceinline__ void mma16(const bf16x8 (&a)[kFA], const bf16x8 (&b)[kFBW],
+                                      floatx16 (&acc)[kFA][kFBW]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kFA; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kFBW; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
 }
 
@@ -703,46 +719,41 @@ void gemm_kernel(const GemmArgs g) {
   }
 }
 
-// bf16 GEMMs on 128 x 512 tiles.  Accumulator element (i, j, r) of lane l of wave w:
-// A-row 32 i + 8 (r / 4) + 4 (l / 32) + r % 4 of the tile, B-row (token) 128 w + 32 j + l % 32.
+// bf16 GEMMs on 256 x 256 tiles.  Accumulator element (i, j, r) of lane l of wave w:
+// A-row 32 i + 8 (r / 4) + 4 (l / 32) + r % 4 of the tile, B-row (token) 64 w + 32 j + l % 32.
 // Iteration kt computes ring stage kt in two 16-wide k steps: the loads of A stage kt + 3
-// and of this wave's B stage kt + 2 and the A fragments of step 1 are issued under the
+// and of this wave's B stage kt + 3 and the A fragments of step 1 are issued under the
 // MFMAs of step 0; then the A loads of stage kt + 1 are waited for, a barrier publishes
 // every wave's, and the A fragments of stage kt + 1, step 0 are read under the MFMAs of
 // step 1.  A ring slot is refilled only after the barrier that follows its last read.
-template <int KIND>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm16_kernel(const GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) char smem[kStagesA * kAStageBytes];
-  int ta, tb;
-  if (!map_tile(g, ta, tb)) return;
+//
+// The tile body is instantiated per kind of tile, so that the common case (a tile inside
+// the matrix, unsplit K) has straight-line epilogues: kEdge marks the last tile along the
+// vocabulary (LSE / PROBS) or hidden (DH) axis, kSplit a dH tile of a split vocabulary.
+template <int KIND, bool kEdge, bool kSplit>
+__device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int ks, int tile_a, int tb) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  constexpr bool kDH = KIND == KIND_DH || KIND == KIND_DHT;  // dH epilogue, split vocabulary
-  constexpr bool kTrans = KIND == KIND_DH;                   // A transposed in registers
-  int ks = 0, tile_a = ta;
-  if (kDH) {
-    ks = ta / g.tiles_a_base;
-    tile_a = ta - ks * g.tiles_a_base;
-  }
+  constexpr bool kTrans = KIND == KIND_DH;  // A transposed in registers
   const int row_a0 = tile_a * kTA;
   const int row_b0 = tb * kTB;
   const int k_begin = ks * g.k_len;
   const int k_end = min(g.K, k_begin + g.k_len);
   const int nk = k_end > k_begin ? (k_end - k_begin + kBK16 - 1) / kBK16 : 0;
 
-  floatx16 acc[4][4];
+  floatx16 acc[kFA][kFBW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kFA; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kFBW; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const __bf16* A = reinterpret_cast<const __bf16*>(g.a);
-  // this wave's 128 rows of the B tile in the fragment-major copy
-  const char* Bw = reinterpret_cast<const char*>(g.b) + (int64_t)tb * g.b_ks * kFB * 1024 + 4 * w * 1024 + lane * 16;
+  // this wave's 64 rows of the B tile in the fragment-major copy
+  const char* Bw =
+      reinterpret_cast<const char*>(g.b) + (int64_t)tb * g.b_ks * kFB * 1024 + kFBW * w * 1024 + lane * 16;
   const int ks0 = k_begin >> 4;
   using ATile = typename std::conditional<kTrans, TransTileA, DmaTileA>::type;
   ATile at;
@@ -760,15 +771,19 @@ void gemm16_kernel(const GemmArgs g) {
         at.issue(smem + st * kAStageBytes, k0, k_end);
       }
     }
-    bf16x8 bb0[2][4], bb1[2][4], bb2[2][4];
+    bf16x8 bb0[2][kFBW], bb1[2][kFBW], bb2[2][kFBW], bb3[2][kFBW];
     b_load(Bw, ks0, g.b_ks, bb0);
     b_load(Bw, ks0 + 2, g.b_ks, bb1);
+    b_load(Bw, ks0 + 4, g.b_ks, bb2);
     __builtin_amdgcn_s_waitcnt(kWaitAll);
     __builtin_amdgcn_s_barrier();
-    bf16x8 a0[4], a1[4];
+    bf16x8 a0[kFA], a1[kFA];
     a_frags(smem, 0, lane, a0);
     int slot = 0;
-    auto step = [&](int kt, bf16x8 (&cur)[2][4], bf16x8 (&nxt)[2][4]) {
+    // loads issued per iteration after A stage kt + 1 (two iterations ago) that may still
+    // be in flight when it is waited for: its iteration's B loads and two full iterations
+    constexpr int kVmAfterA = 2 * kFBW + 2 * (kDmaA + 2 * kFBW);
+    auto step = [&](int kt, bf16x8 (&cur)[2][kFBW], bf16x8 (&nxt)[2][kFBW]) {
       const int slot_n = slot + 1 == kStagesA ? 0 : slot + 1;
       const int slot_f = slot == 0 ? kStagesA - 1 : slot - 1;  // stage kt + kStagesA - 1
       char* sc = smem + slot * kAStageBytes;
@@ -778,50 +793,60 @@ void gemm16_kernel(const GemmArgs g) {
       const int kf = k_begin + (kt + kStagesA - 1) * kBK16;
       if constexpr (kTrans) at.load(kf, k_end);
       else at.issue(sf, kf, k_end);
-      b_load(Bw, ks0 + 2 * (kt + 2), g.b_ks, nxt);
+      b_load(Bw, ks0 + 2 * (kt + 3), g.b_ks, nxt);
       a_frags(sc, 1, lane, a1);
       mma16(a0, cur[0], acc);
       // instruction classes: 0x8 MFMA, 0x20 VMEM read, 0x100 DS read, 0x200 DS write
+      if constexpr (kTrans) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       __builtin_amdgcn_sched_barrier(0);
-      // A stage kt + 1 was issued two iterations ago; 28 later loads may still fly
-      __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0(28));
+      __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0(kTrans ? 28 : kVmAfterA));
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       a_frags(sn, 0, lane, a0);
       mma16(a1, cur[1], acc);
       if constexpr (kTrans) at.store(sf);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 8; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       if constexpr (kTrans) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     };
-    // three B register buffers rotate, so the loop runs in groups of three stages; the
+    // four B register buffers rotate, so the loop runs in groups of four stages; the
     // stages past the end of K read zeros
-    for (int kt = 0; kt < nk; kt += 3) {
-      step(kt, bb0, bb2);
+    for (int kt = 0; kt < nk; kt += 4) {
+      step(kt, bb0, bb3);
       step(kt + 1, bb1, bb0);
       step(kt + 2, bb2, bb1);
+      step(kt + 3, bb3, bb2);
     }
     __builtin_amdgcn_s_waitcnt(kWaitAll);
     __builtin_amdgcn_s_barrier();
@@ -829,105 +854,148 @@ void gemm16_kernel(const GemmArgs g) {
 
   const int hi = lane >> 5;
   const int col = lane & 31;
-  if constexpr (KIND == KIND_LSE) {
-    // Per token: max and sum of exp over this tile's 128 vocabulary rows (those < V).
-    const bool full = row_a0 + kTA <= g.a_rows;
-    const int vbase = row_a0 + 4 * hi;
+  // Epilogues without per-element bounds masks: in a tile that crosses the end of the
+  // vocabulary, a one-time pass sets the accumulators of rows >= V to -inf (exp gives 0,
+  // max ignores them); column bounds of 8-aligned groups are wave-uniform scalar tests
+  // (every limit is a multiple of 8 and the tile origin of 256); only stores depend on
+  // the lane's token.
+  if constexpr ((KIND == KIND_LSE || KIND == KIND_PROBS) && kEdge) {
+    {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kFA; ++i) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int v = vbase + 32 * i + 8 * (r >> 2) + (r & 3);
-          if (full || v < g.a_rows) mx = fmaxf(mx, acc[i][j][r]);
+          const bool out = row_a0 + 4 * hi + 32 * i + 8 * (r >> 2) + (r & 3) >= g.V;
+#pragma unroll
+          for (int j = 0; j < kFBW; ++j) acc[i][j][r] = out ? -INFINITY : acc[i][j][r];
         }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  if constexpr (KIND == KIND_LSE) {
+    // Per token: max and sum of exp over this tile's 256 vocabulary rows (those < V).
+#pragma unroll
+    for (int j = 0; j < kFBW; ++j) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < kFA; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float zmax = mx * g.inv_tau;  // inv_tau > 0, so this is the max of z
       float sum = 0.0f;
       if (mx > -INFINITY) {
         const float c1 = g.inv_tau * kLog2e, c0 = -zmax * kLog2e;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kFA; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int v = vbase + 32 * i + 8 * (r >> 2) + (r & 3);
-            if (full || v < g.a_rows) sum += __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], c1, c0));
-          }
+          for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], c1, c0));
       }
       sum += __shfl_xor(sum, 32);
-      const int tok = row_b0 + 128 * w + 32 * j + col;
+      const int tok = row_b0 + 64 * w + 32 * j + col;
       if (hi == 0 && tok < g.b_rows) {
         g.pm[(int64_t)tok * g.tiles_a + tile_a] = zmax;
         g.ps[(int64_t)tok * g.tiles_a + tile_a] = sum;
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   } else if constexpr (KIND == KIND_PROBS) {
     // P[token, v] = exp(z - lse[token]) into the fragment-major copy used as the dH GEMM's
-    // B operand; the vocabulary padding up to the next 16 is written as zeros.
+    // B operand; the vocabulary padding up to the next 16 is written as zeros.  Rows of
+    // the copy past the chunk's tokens are written too (the dH GEMM ignores them).
     char* P = reinterpret_cast<char*>(g.p);
-    const int vpad = g.p_ks * 16;
+    const int vrem = g.p_ks * 16 - row_a0;  // uniform; multiple of 16
     const float c1 = g.inv_tau * kLog2e;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tok = row_b0 + 128 * w + 32 * j + col;
-      if (tok >= g.b_rows) continue;
-      const float c0 = -g.lse[tok] * kLog2e;
+    for (int j = 0; j < kFBW; ++j) {
+      const int tok = row_b0 + 64 * w + 32 * j + col;
+      const float c0 = -(tok < g.b_rows ? g.lse[tok] : 0.0f) * kLog2e;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kFA; ++i) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+          if (kEdge && 32 * i + 8 * q >= vrem) continue;
           const int v0 = row_a0 + 32 * i + 8 * q + 4 * hi;
-          if (v0 >= vpad) continue;
           float e[4];
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            e[u] = v0 + u < g.V ? __builtin_amdgcn_exp2f(fmaf(acc[i][j][4 * q + u], c1, c0)) : 0.0f;
+          for (int u = 0; u < 4; ++u) e[u] = __builtin_amdgcn_exp2f(fmaf(acc[i][j][4 * q + u], c1, c0));
           store4(reinterpret_cast<__bf16*>(P + frag_off(tok, v0, g.p_ks)), e[0], e[1], e[2], e[3]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   } else {
     // dH[token, d] = (g / tau) (W[y, d] - acc), or the raw fp32 partial when split.
+    const int drem = g.D - row_a0;  // uniform; multiple of 8
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tok = row_b0 + 128 * w + 32 * j + col;
-      if (tok >= g.b_rows) continue;
-      if (g.ksplit > 1) {
-        float* dst = g.part + ((int64_t)ks * g.b_rows + tok) * g.D;
+    for (int j = 0; j < kFBW; ++j) {
+      const int tok = row_b0 + 64 * w + 32 * j + col;
+      const bool ok = tok < g.b_rows;
+      if constexpr (kSplit) {
+        float* dst = g.part + ((int64_t)ks * g.b_rows + (ok ? tok : 0)) * g.D;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kFA; ++i) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
+            if (kEdge && 32 * i + 8 * q >= drem) continue;
             const int d0 = row_a0 + 32 * i + 8 * q + 4 * hi;
-            if (d0 < g.D)
-              *reinterpret_cast<float4*>(dst + d0) =
-                  make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            const float4 o =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            if (ok) *reinterpret_cast<float4*>(dst + d0) = o;
           }
+          __builtin_amdgcn_sched_barrier(0);
+        }
         continue;
       }
-      const float gt = g.g[tok];
-      const int y = g.targets[tok];
+      const float gt = ok ? g.g[tok] : 0.0f;
+      const int y = ok ? g.targets[tok] : 0;
       const bool live = gt != 0.0f && y >= 0 && y < g.V;
-      const float scale = gt * g.inv_tau;
+      const float scale = live ? gt * g.inv_tau : 0.0f;
       const __bf16* wrow = reinterpret_cast<const __bf16*>(g.w) + (int64_t)(live ? y : 0) * g.D;
-      __bf16* dst = reinterpret_cast<__bf16*>(g.dh) + (int64_t)tok * g.D;
+      __bf16* dst = reinterpret_cast<__bf16*>(g.dh) + (int64_t)(ok ? tok : 0) * g.D;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kFA; ++i) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+          if (kEdge && 32 * i + 8 * q >= drem) continue;
           const int d0 = row_a0 + 32 * i + 8 * q + 4 * hi;
-          if (d0 >= g.D) continue;
-          float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-          if (live) {
-            float wv[4];
-            load4(wrow + d0, wv);
+          float wv[4], o[4];
+          load4(wrow + d0, wv);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) o[u] = scale * (wv[u] - acc[i][j][4 * q + u]);
-          }
-          store4(dst + d0, o[0], o[1], o[2], o[3]);
+          for (int u = 0; u < 4; ++u) o[u] = live ? scale * (wv[u] - acc[i][j][4 * q + u]) : 0.0f;
+          if (ok) store4(dst + d0, o[0], o[1], o[2], o[3]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
+  }
+}
+
+template <int KIND>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm16_kernel(const GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) char smem[kStagesA * kAStageBytes];
+  int ta, tb;
+  if (!map_tile(g, ta, tb)) return;
+  constexpr bool kDH = KIND == KIND_DH || KIND == KIND_DHT;
+  int ks = 0, tile_a = ta;
+  if (kDH) {
+    ks = ta / g.tiles_a_base;
+    tile_a = ta - ks * g.tiles_a_base;
+  }
+  const bool edge = (tile_a + 1) * kTA > (kDH ? g.D : g.V);
+  if constexpr (kDH) {
+    if (g.ksplit > 1) {
+      if (edge) gemm16_tile<KIND, true, true>(g, smem, ks, tile_a, tb);
+      else gemm16_tile<KIND, false, true>(g, smem, ks, tile_a, tb);
+    } else {
+      if (edge) gemm16_tile<KIND, true, false>(g, smem, ks, tile_a, tb);
+      else gemm16_tile<KIND, false, false>(g, smem, ks, tile_a, tb);
+    }
+  } else {
+    if (edge) gemm16_tile<KIND, true, false>(g, smem, ks, tile_a, tb);
+    else gemm16_tile<KIND, false, false>(g, smem, ks, tile_a, tb);
   }
 }
 

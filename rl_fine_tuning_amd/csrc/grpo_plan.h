@@ -10,11 +10,11 @@
 namespace grpo {
 
 // MFMA workgroup tiles.  fp32 inputs: 256 x 256 (vocabulary or hidden x tokens).  bf16
-// inputs: 128 rows of the first operand x 512 tokens, with the tokens' operand in a
-// fragment-major copy (16-element k steps, 512-row tiles).
+// inputs: 256 rows of the first operand x 256 tokens, with the tokens' operand in a
+// fragment-major copy (16-element k steps, 256-row tiles).
 constexpr int kTile = 256;
-constexpr int kTileA16 = 128;
-constexpr int kTileB16 = 512;
+constexpr int kTileA16 = 256;
+constexpr int kTileB16 = 256;
 // MI355X compute units; sizes the vocabulary split of the dH GEMM for small chunks.
 constexpr int kNumCUs = 256;
 constexpr int kMaxKSplit = 8;
