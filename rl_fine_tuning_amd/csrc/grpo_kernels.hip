@@ -222,7 +222,7 @@ struct TransTile<__bf16> {
     const int64_t rows = min(kend - k0, 64);
     const __amdgpu_buffer_rsrc_t r = make_rsrc(W + (int64_t)k0 * D + d0, (rows * D - d0) * 2);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = bload(r, voff, voff == kOOB ? 0u : (uint32_t)(e * D * 2));
+    for (int e = 0; e < 8; ++e) v[e] = bload(r, voff, (uint32_t)(e * D * 2));  // kOOB + soff stays out of range
   }
   __device__ __forceinline__ void store(char* lds, int tid) const {
     const int b = tid & 31, a = tid >> 5;
@@ -260,8 +260,8 @@ struct TransTile<float> {
     const __amdgpu_buffer_rsrc_t r = make_rsrc(W + (int64_t)k0 * D + d0, (rows * D - d0) * 4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      v[2 * e] = bload(r, voff0, voff0 == kOOB ? 0u : (uint32_t)(e * D * 4));
-      v[2 * e + 1] = bload(r, voff1, voff1 == kOOB ? 0u : (uint32_t)(e * D * 4));
+      v[2 * e] = bload(r, voff0, (uint32_t)(e * D * 4));  // kOOB + soff stays out of range
+      v[2 * e + 1] = bload(r, voff1, (uint32_t)(e * D * 4));
     }
   }
   __device__ __forceinline__ void store(char* lds, int tid) const {
@@ -374,8 +374,8 @@ struct TransTileA {
     for (int p = 0; p < 2; ++p)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const u32x2 x =
-            __builtin_amdgcn_raw_buffer_load_b64(r, voff[p], voff[p] == kOOB ? 0u : (uint32_t)(e * D * 2), 0);
+        // the scalar offset must stay uniform; kOOB + e * D * 2 is still past the range
+        const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, voff[p], (uint32_t)(e * D * 2), 0);
         v[p][e] = make_uint2(x.x, x.y);
       }
   }
