@@ -1366,7 +1366,7 @@ GemmArgs logits_args(const Plan& p, const T* W, const T* Hc, const char* Hf, int
   g.tiles_a = (int)p.ntiles_v;
   g.tiles_b = (int)cdiv(rows, bf16 ? kTileB16 : kTile);
   g.xcd_axis = 0;
-  g.group_b = bf16 ? 4 : 8;
+  g.group_b = 8;  // B tiles walked together
   g.inv_tau = inv_tau;
   g.V = (int)p.V;
   g.D = (int)p.D;
@@ -1520,7 +1520,7 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, const grpo_loss_pa
     gd.tiles_a = gd.tiles_a_base * ksplit;
     gd.tiles_b = (int)cdiv(rows, bf16 ? kTileB16 : kTile);
     gd.xcd_axis = 1;
-    gd.group_b = bf16 ? 1 : 2;
+    gd.group_b = bf16 ? 4 : 2;  // 8 W^T tiles x 4 token tiles per XCD round (bf16)
     gd.b_ks = (int)p.ks_v;
     gd.inv_tau = inv_tau;
     gd.g = gbuf + t0;
