@@ -24,6 +24,10 @@ What it computes, and where the pages state it (page titles as printed):
      tokens equals 1 in value and carries gradient A on policy.
 [P1] "Unsloth GRPO Implementation ...", section "Corrected Hyperparameters
      for GRPO Stability": beta = 0.001.
+[P2] "Unsloth internals", the paragraph on the fused, chunked cross-entropy:
+     the supervised loss over the vocabulary is computed without the full fp32
+     logits tensor or its same-shape gradient; here it is the mean over the
+     unmasked tokens of -logp through the same chunked log-softmax.
 
 Readings where the pages are silent (each is also listed in the design notes):
 unbiased std, eps added to the std (default 1e-4), A = 0 for a group whose
@@ -244,6 +248,56 @@ def grpo_loss_and_grad(H, W, targets, cu, mask, old_logp, ref_logp, adv, tempera
         dz[np.arange(dz.shape[0]), y[live]] += 1.0
         dH[rows[live]] = (g[rows[live]] / temperature)[:, None] * (dz @ W)
     return dict(loss=L, logp=logp, lse=lse, token_loss=ell, g=g, dH=dH)
+
+
+def logp_backward(H, W, targets, grad_logp, temperature=1.0, block: int = ROW_BLOCK):
+    """Gradient with respect to H of sum_t grad_logp[t] * logp_t.
+
+    The backward of the chunked selective log-softmax ([P4], "Auslagern von
+    Aktivierungen fuer Log-Softmax"): the forward keeps only the log-sum-exp,
+    the backward recomputes the logits and applies the incoming gradient of
+    the log-probabilities, dH_t = (grad_t / temperature) * (W[y_t] - sum_v
+    softmax(z_t)_v W[v]).  Rows with grad_t = 0 or an out-of-range target are
+    exactly 0.
+    """
+    T, D = H.shape
+    V = W.shape[0]
+    g = np.asarray(grad_logp, dtype=np.float64)
+    _, lse = selective_log_softmax(H, W, targets, temperature, block)
+    dH = np.zeros((T, D))
+    y_all = np.asarray(targets, dtype=np.int64)
+    for r0 in range(0, T, block):
+        r1 = min(T, r0 + block)
+        rows = np.arange(r0, r1)
+        y = y_all[r0:r1]
+        live = (g[r0:r1] != 0) & (y >= 0) & (y < V)
+        if not live.any():
+            continue
+        z = logits(H[r0:r1][live], W, temperature)
+        p = np.exp(z - lse[rows[live]][:, None])
+        dz = -p
+        dz[np.arange(dz.shape[0]), y[live]] += 1.0
+        dH[rows[live]] = (g[rows[live]] / temperature)[:, None] * (dz @ W)
+    return dH
+
+
+def cross_entropy_loss_and_grad(H, W, targets, mask=None, temperature=1.0, block: int = ROW_BLOCK):
+    """Chunked cross-entropy (the supervised loss the same chunked log-softmax
+    serves): L = -(1/N) sum_t mask_t logp_t with N = sum_t mask_t (L = 0 and
+    dH = 0 when N = 0), per-token loss -logp_t, g_t = dL/dlogp_t = -mask_t / N,
+    dH by the backward above.  A masked token contributes exactly 0 even when
+    its target is out of range.
+    """
+    T = H.shape[0]
+    m = np.ones(T) if mask is None else np.asarray(mask, dtype=np.float64)
+    logp, lse = selective_log_softmax(H, W, targets, temperature, block)
+    n = m.sum()
+    w = m / n if n > 0 else np.zeros(T)
+    terms = [w[t] * (-logp[t]) for t in range(T) if w[t] != 0]
+    L = math.fsum(terms) if terms else 0.0
+    g = -w
+    dH = logp_backward(H, W, targets, g, temperature, block)
+    return dict(loss=L, logp=logp, lse=lse, token_loss=-logp, g=g, dH=dH)
 
 
 def grad_rows(H_rows, W, targets_rows, lse_rows, g_rows, temperature=1.0):

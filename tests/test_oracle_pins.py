@@ -343,3 +343,69 @@ def test_grad_rows_agrees_with_full_gradient():
     rows = np.array([0, 3, 7, 11])
     dr = oracle.grad_rows(H[rows], W, y[rows], out["lse"][rows], out["g"][rows], tau)
     np.testing.assert_allclose(dr, out["dH"][rows], rtol=0, atol=1e-13)
+
+
+# ------------------------------------------------- split backward, cross-entropy
+
+def test_logp_backward_matches_finite_differences():
+    # d/dH of sum_t c_t * logp_t for arbitrary c (zeros included), tau = 0.7
+    H, W, y = _tiny(21, T=9, D=6, V=13)
+    tau = 0.7
+    c = np.random.default_rng(22).standard_normal(9)
+    c[[2, 5]] = 0.0
+    dH = oracle.logp_backward(H, W, y, c, tau)
+
+    def f(Hx):
+        lp, _ = oracle.selective_log_softmax(Hx, W, y, tau)
+        return float(np.dot(c, lp))
+
+    h = 1e-6
+    fd = np.zeros_like(H)
+    for t in range(H.shape[0]):
+        for d in range(H.shape[1]):
+            e = np.zeros_like(H)
+            e[t, d] = h
+            fd[t, d] = (f(H + e) - f(H - e)) / (2 * h)
+    assert np.linalg.norm(dH - fd) / np.linalg.norm(fd) < 1e-6
+    assert np.all(dH[[2, 5]] == 0)
+
+
+def test_logp_backward_invalid_target_row_is_zero():
+    H, W, y = _tiny(23, T=6, D=5, V=9)
+    y = y.copy()
+    y[3] = 9  # out of range
+    dH = oracle.logp_backward(H, W, y, np.ones(6))
+    assert np.all(dH[3] == 0) and np.all(np.isfinite(dH))
+
+
+def test_cross_entropy_matches_torch_autograd():
+    # mean cross-entropy over unmasked tokens: torch.nn.functional.cross_entropy with
+    # ignore_index on the masked tokens, in float64 on the CPU, and its autograd gradient
+    torch = pytest.importorskip("torch")
+    H, W, y = _tiny(24, T=14, D=7, V=19)
+    tau = 0.7
+    mask = np.ones(14)
+    mask[[1, 8, 9]] = 0
+    out = oracle.cross_entropy_loss_and_grad(H, W, y, mask, tau)
+    Ht = torch.tensor(H, requires_grad=True)
+    z = Ht @ torch.tensor(W).T / tau
+    yt = torch.tensor(np.where(mask > 0, y, -100))
+    ce = torch.nn.functional.cross_entropy(z, yt, ignore_index=-100, reduction="mean")
+    ce.backward()
+    assert abs(out["loss"] - ce.item()) <= 1e-14 * abs(ce.item())
+    np.testing.assert_allclose(out["dH"], Ht.grad.numpy(), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(out["g"], -mask / mask.sum(), rtol=0, atol=0)
+
+
+def test_cross_entropy_all_masked_and_masked_invalid_target():
+    H, W, y = _tiny(25, T=5, D=4, V=7)
+    out = oracle.cross_entropy_loss_and_grad(H, W, y, np.zeros(5))
+    assert out["loss"] == 0.0 and np.all(out["dH"] == 0)
+    y = y.copy()
+    y[2] = -1
+    mask = np.ones(5)
+    mask[2] = 0
+    out = oracle.cross_entropy_loss_and_grad(H, W, y, mask)
+    assert np.isfinite(out["loss"]) and np.isnan(out["logp"][2]) and np.all(out["dH"][2] == 0)
+    mask[2] = 1
+    assert np.isnan(oracle.cross_entropy_loss_and_grad(H, W, y, mask)["loss"])
