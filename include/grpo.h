@@ -23,6 +23,8 @@
  *  [P1] "Unsloth GRPO Implementation: How It Accelerates Reinforcement Learning
  *       Training", section "Corrected Hyperparameters for GRPO Stability":
  *       beta = 0.001.
+ *  [P2] also describes the fused, chunked cross-entropy that the same chunked
+ *       log-softmax serves for supervised fine-tuning.
  *
  * Conventions shared by every entry point:
  *  - Pointers are device pointers unless marked [host].  `stream` is a
@@ -161,6 +163,35 @@ grpo_status grpo_loss_fwd_bwd(const grpo_shape* shape, const grpo_loss_params* p
                               double* loss, float* logp, float* token_loss, void* dH,
                               void* workspace, size_t workspace_bytes, void* stream,
                               grpo_timer* timer);
+
+/* Backward of grpo_logp_fwd ([P4] "Auslagern von Aktivierungen fuer Log-Softmax": the
+ * forward keeps only the per-token log-sum-exp; the backward recomputes each chunk's logits
+ * and applies the incoming gradient of the log-probabilities):
+ *   dH_t = (grad_logp_t / temperature) (W[y_t] - sum_v softmax(z_t)_v W[v]),
+ * the gradient of sum_t grad_logp_t * logp_t with respect to H.  Any loss written on top of
+ * the log-probabilities (other GRPO variants, other aggregations) back-propagates through it.
+ *   H, W, targets, shape as for grpo_logp_fwd; lse fp32 [T]: the log-sum-exp grpo_logp_fwd
+ *   returned for the same H, W and temperature; grad_logp fp32 [T] (dL/dlogp; 0 for tokens
+ *   that do not contribute); dH [T, D] of shape->dtype (overwritten; +0 rows where
+ *   grad_logp is 0 or the target is outside [0, V)); workspace of
+ *   grpo_workspace_bytes(shape, 1, 1) bytes. */
+grpo_status grpo_logp_bwd(const grpo_shape* shape, const void* H, const void* W, const int32_t* targets,
+                          const float* lse, const float* grad_logp, void* dH, void* workspace,
+                          size_t workspace_bytes, void* stream, grpo_timer* timer);
+
+/* Chunked cross-entropy, forward and backward ([P2] "Unsloth internals", the fused, chunked
+ * cross-entropy: the loss over the vocabulary without the [T, V] logits or their gradient):
+ *   loss = -(1/N) sum_t mask_t logp_t,  N = sum_t mask_t  (loss = 0 and dH = 0 when N = 0),
+ *   dH   = the grpo_logp_bwd of g_t = -mask_t / N.
+ *   mask uint8 [T] (NULL = every token counts); loss fp64 [1] (written, summed in fp64 in a
+ *   fixed token order); logp, token_loss fp32 [T] (written when not NULL; token_loss holds
+ *   -logp_t); dH [T, D] of shape->dtype (overwritten); workspace of
+ *   grpo_workspace_bytes(shape, 1, 1) bytes.  A counted token whose target is outside [0, V)
+ *   makes the loss NaN; its dH row is +0. */
+grpo_status grpo_ce_loss_fwd_bwd(const grpo_shape* shape, const void* H, const void* W,
+                                 const int32_t* targets, const uint8_t* mask, double* loss,
+                                 float* logp, float* token_loss, void* dH, void* workspace,
+                                 size_t workspace_bytes, void* stream, grpo_timer* timer);
 
 /* Human-readable name of a status code (static storage). */
 const char* grpo_status_string(grpo_status status);

@@ -9,7 +9,9 @@ from .grpo import (  # noqa: F401
     GrpoError,
     Timer,
     grpo_advantages,
+    grpo_ce_loss_fwd_bwd,
     grpo_debug_token_index,
+    grpo_logp_bwd,
     grpo_logp_fwd,
     grpo_loss_fwd_bwd,
     grpo_workspace_bytes,

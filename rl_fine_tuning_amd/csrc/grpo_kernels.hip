@@ -1097,7 +1097,7 @@ struct MergeArgs {
   const float* zy;      // [T]
   float* lse;           // [T]
   float* logp;          // [T] or NULL
-  int grpo;
+  int mode;               // 0: log-probs only, 1: GRPO terms, 2: cross-entropy terms
   const float* old_logp;
   const float* ref_logp;  // NULL when beta == 0
   const float* adv;
@@ -1139,18 +1139,21 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   const float lp = a.zy[t] - lse;
   a.lse[t] = lse;
   if (a.logp) a.logp[t] = lp;
-  if (!a.grpo) return;
+  if (a.mode == 0) return;
 
   const int s = a.seq[t];
-  const float A = a.adv[s];
   const bool counted = a.mask == nullptr || a.mask[t] != 0;
   const double w64 = counted ? a.wseq[s] : 0.0;
   const float w = (float)w64;
   float ell, dell;
-  if (lp != lp) {  // target outside the vocabulary
+  if (a.mode == 2) {  // cross-entropy: l = -logp, dl/dlogp = -1 (NaN logp stays NaN in l)
+    ell = -lp;
+    dell = -1.0f;
+  } else if (lp != lp) {  // target outside the vocabulary
     ell = __builtin_nanf("");
     dell = __builtin_nanf("");
   } else {
+    const float A = a.adv[s];
     const float rho = expf(lp - a.old_logp[t]);
     const float c = fminf(fmaxf(rho, 1.0f - a.eps_lo), 1.0f + a.eps_hi);
     const float un = rho * A, cl = c * A;
@@ -1169,6 +1172,14 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   if (a.token_loss) a.token_loss[t] = ell;
   a.g[t] = counted ? w * dell : 0.0f;
   a.wl[t] = w64 != 0.0 ? w64 * (double)ell : 0.0;
+}
+
+// cu = {0, T}: the whole stream as one sequence (cross-entropy).
+__global__ void whole_stream_cu_kernel(int32_t* cu, int T) {
+  if (threadIdx.x == 0) {
+    cu[0] = 0;
+    cu[1] = T;
+  }
 }
 
 // Largest s in [0, S) with cu[s] <= t: the sequence of token t.
@@ -1413,8 +1424,78 @@ grpo_status logp_impl(const Plan& p, const grpo_shape* shape, const T* H, const 
   return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_E_HIP;
 }
 
+// Backward of one chunk: recompute its logits into softmax probabilities (PROBS GEMM, with
+// the log-sum-exp of the forward), then dH = (g / tau) (W[y] - P W) (dH GEMM, split over
+// the vocabulary when the chunk is too small to fill the GPU).  Hf holds the chunk's
+// fragment-major hidden states (bf16).
 template <typename T>
-grpo_status loss_impl(const Plan& p, const grpo_shape* shape, const grpo_loss_params* prm, const T* H,
+void backward_chunk(Launcher& L, const Plan& p, const T* W, const T* WT, bool use_wt, const T* Hc, const char* Hf,
+                    int rows, int64_t k, const float* lse_c, const float* g_c, const int32_t* targets_c, T* dH_c,
+                    T* P, float* part, float inv_tau) {
+  GemmArgs gp = logits_args<T>(p, W, Hc, Hf, rows, inv_tau);
+  gp.lse = lse_c;
+  gp.p = P;
+  gp.ldp = p.ldp;
+  launch_gemm<T, KIND_PROBS>(L, GRPO_K_PROBS, gp);
+
+  // dH^T tiles: hidden x tokens, K = vocabulary, split over the vocabulary if needed.
+  const int ks_plan = (k == p.nchunks - 1) ? p.ksplit_tail : p.ksplit_full;
+  const int k_len = (int)(cdiv(cdiv(p.V, ks_plan), p.bk) * p.bk);
+  const int ksplit = (int)cdiv(p.V, k_len);
+  GemmArgs gd = {};
+  gd.a = use_wt ? WT : W;
+  gd.b = P;
+  gd.lda = use_wt ? p.ldt : p.D;
+  gd.ldb = p.ldp;
+  gd.a_rows = (int)p.D;
+  gd.b_rows = rows;
+  gd.K = (int)p.V;
+  gd.k_len = k_len;
+  const bool bf16 = sizeof(T) == 2;
+  gd.tiles_a_base = (int)cdiv(p.D, bf16 ? kTileA16 : kTile);
+  gd.tiles_a = gd.tiles_a_base * ksplit;
+  gd.tiles_b = (int)cdiv(rows, bf16 ? kTileB16 : kTile);
+  gd.xcd_axis = 1;
+  gd.group_b = bf16 ? 4 : 2;  // 8 W^T tiles x 4 token tiles per XCD round (bf16)
+  gd.b_ks = (int)p.ks_v;
+  gd.inv_tau = inv_tau;
+  gd.g = g_c;
+  gd.targets = targets_c;
+  gd.w = W;
+  gd.dh = dH_c;
+  gd.part = part;
+  gd.V = (int)p.V;
+  gd.D = (int)p.D;
+  gd.ksplit = ksplit;
+  if (use_wt) launch_gemm<T, KIND_DHT>(L, GRPO_K_DH_GEMM, gd);
+  else launch_gemm<T, KIND_DH>(L, GRPO_K_DH_GEMM, gd);
+  if (ksplit > 1) {
+    L.run(GRPO_K_DH_REDUCE, [&] {
+      hipLaunchKernelGGL((dh_reduce_kernel<T>), dim3(grid1((int64_t)rows * (p.D / 4), 256)), dim3(256), 0,
+                         L.stream, part, ksplit, rows, (int)p.D, (int)p.V, inv_tau, g_c, targets_c, W, dH_c);
+    });
+  }
+}
+
+// W^T for the dH GEMM, once per call, when the plan has room for it (bf16).
+template <typename T>
+const T* maybe_transpose_w(Launcher& L, const Plan& p, const T* W, char* ws, bool& use_wt) {
+  use_wt = sizeof(T) == 2 && p.use_wt && p.T > 0;
+  const T* WT = reinterpret_cast<const T*>(ws + p.off_WT);
+  if (use_wt) {
+    L.run(GRPO_K_TRANSPOSE_W, [&] {
+      hipLaunchKernelGGL(transpose_w_kernel, dim3(grid1(p.ldt, 256), grid1(p.D, 64)), dim3(256), 0, L.stream,
+                         reinterpret_cast<const __bf16*>(W), (int)p.V, (int)p.D, (int)p.ldt,
+                         reinterpret_cast<__bf16*>(const_cast<T*>(WT)));
+    });
+  }
+  return WT;
+}
+
+// Loss forward + backward.  mode 1: GRPO objective; mode 2: cross-entropy (prm, old_logp,
+// ref_logp and adv unused; one sequence spanning the stream, token-mean weights).
+template <typename T>
+grpo_status loss_impl(const Plan& p, const grpo_shape* shape, int mode, const grpo_loss_params* prm, const T* H,
                       const T* W, const int32_t* targets, const int32_t* cu_host, const uint8_t* mask,
                       const float* old_logp, const float* ref_logp, const float* adv, double* loss,
                       float* logp, float* token_loss, T* dH, char* ws, Launcher& L) {
@@ -1433,31 +1514,29 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, const grpo_loss_pa
   char* Hf = ws + p.off_Hf;
   float* part = reinterpret_cast<float*>(ws + p.off_part);
   const int S = (int)p.S;
-  // bf16 with room in the workspace: the dH GEMM reads W through a transposed copy
-  const bool use_wt = sizeof(T) == 2 && p.use_wt;
-  const T* WT = reinterpret_cast<const T*>(ws + p.off_WT);
+  const int agg = mode == 2 ? (int)GRPO_AGG_TOKEN_MEAN : (int)prm->agg;
 
-  if (hipMemcpyAsync(cu, cu_host, sizeof(int32_t) * (S + 1), hipMemcpyHostToDevice, L.stream) != hipSuccess)
+  if (mode == 2) {
+    hipLaunchKernelGGL(whole_stream_cu_kernel, dim3(1), dim3(64), 0, L.stream, cu, (int)p.T);
+  } else if (hipMemcpyAsync(cu, cu_host, sizeof(int32_t) * (S + 1), hipMemcpyHostToDevice, L.stream) !=
+             hipSuccess) {
     return GRPO_E_HIP;
+  }
   L.run(GRPO_K_TOKEN_INDEX, [&] {
     if (p.T > 0)
       hipLaunchKernelGGL(token_index_kernel, dim3(grid1(p.T, 256)), dim3(256), 0, L.stream, cu, S, (int)p.T,
                          (int)(p.C > 0 ? p.C : 1), seq, (int32_t*)nullptr, (int32_t*)nullptr);
     hipLaunchKernelGGL(seq_count_kernel, dim3(S), dim3(256), 0, L.stream, cu, mask, cnt);
-    hipLaunchKernelGGL(seq_weight_kernel, dim3(1), dim3(256), 0, L.stream, cnt, S, (int)prm->agg, wseq);
+    hipLaunchKernelGGL(seq_weight_kernel, dim3(1), dim3(256), 0, L.stream, cnt, S, agg, wseq);
   });
+  bool use_wt = false;
+  const T* WT = nullptr;
   if (p.T > 0) {
     L.run(GRPO_K_TARGET_LOGIT, [&] {
       hipLaunchKernelGGL((target_logit_kernel<T>), dim3(grid1(p.T, 4)), dim3(256), 0, L.stream, H, W, targets,
                          (int)p.T, (int)p.D, (int)p.V, inv_tau, zy);
     });
-    if (use_wt) {
-      L.run(GRPO_K_TRANSPOSE_W, [&] {
-        hipLaunchKernelGGL(transpose_w_kernel, dim3(grid1(p.ldt, 256), grid1(p.D, 64)), dim3(256), 0, L.stream,
-                           reinterpret_cast<const __bf16*>(W), (int)p.V, (int)p.D, (int)p.ldt,
-                           reinterpret_cast<__bf16*>(const_cast<T*>(WT)));
-      });
-    }
+    WT = maybe_transpose_w<T>(L, p, W, ws, use_wt);
   }
   for (int64_t k = 0; k < p.nchunks; ++k) {
     const int64_t t0 = k * p.C;
@@ -1478,72 +1557,51 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, const grpo_loss_pa
     m.zy = zy;
     m.lse = lse;
     m.logp = logp;
-    m.grpo = 1;
+    m.mode = mode;
     m.old_logp = old_logp;
     m.ref_logp = ref_logp;
     m.adv = adv;
     m.seq = seq;
     m.mask = mask;
     m.wseq = wseq;
-    m.eps_lo = prm->clip_eps_low;
-    m.eps_hi = prm->clip_eps_high;
-    m.beta = prm->beta;
+    if (prm) {
+      m.eps_lo = prm->clip_eps_low;
+      m.eps_hi = prm->clip_eps_high;
+      m.beta = prm->beta;
+    }
     m.token_loss = token_loss;
     m.g = gbuf;
     m.wl = wl;
     L.run(GRPO_K_MERGE, [&] {
       hipLaunchKernelGGL(merge_kernel, dim3(grid1(rows, 16)), dim3(256), 0, L.stream, m);
     });
-
-    // Recompute the chunk's logits and write its softmax probabilities.
-    GemmArgs gp = logits_args<T>(p, W, Hc, Hf, rows, inv_tau);
-    gp.lse = lse + t0;
-    gp.p = P;
-    gp.ldp = p.ldp;
-    launch_gemm<T, KIND_PROBS>(L, GRPO_K_PROBS, gp);
-
-    // dH^T tiles: hidden x tokens, K = vocabulary, split over the vocabulary if needed.
-    const int ks_plan = (k == p.nchunks - 1) ? p.ksplit_tail : p.ksplit_full;
-    const int k_len = (int)(cdiv(cdiv(p.V, ks_plan), p.bk) * p.bk);
-    const int ksplit = (int)cdiv(p.V, k_len);
-    GemmArgs gd = {};
-    gd.a = use_wt ? WT : W;
-    gd.b = P;
-    gd.lda = use_wt ? p.ldt : p.D;
-    gd.ldb = p.ldp;
-    gd.a_rows = (int)p.D;
-    gd.b_rows = rows;
-    gd.K = (int)p.V;
-    gd.k_len = k_len;
-    const bool bf16 = sizeof(T) == 2;
-    gd.tiles_a_base = (int)cdiv(p.D, bf16 ? kTileA16 : kTile);
-    gd.tiles_a = gd.tiles_a_base * ksplit;
-    gd.tiles_b = (int)cdiv(rows, bf16 ? kTileB16 : kTile);
-    gd.xcd_axis = 1;
-    gd.group_b = bf16 ? 4 : 2;  // 8 W^T tiles x 4 token tiles per XCD round (bf16)
-    gd.b_ks = (int)p.ks_v;
-    gd.inv_tau = inv_tau;
-    gd.g = gbuf + t0;
-    gd.targets = targets + t0;
-    gd.w = W;
-    gd.dh = dH + t0 * p.D;
-    gd.part = part;
-    gd.V = (int)p.V;
-    gd.D = (int)p.D;
-    gd.ksplit = ksplit;
-    if (use_wt) launch_gemm<T, KIND_DHT>(L, GRPO_K_DH_GEMM, gd);
-    else launch_gemm<T, KIND_DH>(L, GRPO_K_DH_GEMM, gd);
-    if (ksplit > 1) {
-      L.run(GRPO_K_DH_REDUCE, [&] {
-        hipLaunchKernelGGL((dh_reduce_kernel<T>), dim3(grid1((int64_t)rows * (p.D / 4), 256)), dim3(256), 0,
-                           L.stream, part, ksplit, rows, (int)p.D, (int)p.V, inv_tau, gbuf + t0, targets + t0, W,
-                           dH + t0 * p.D);
-      });
-    }
+    backward_chunk<T>(L, p, W, WT, use_wt, Hc, Hf, rows, k, lse + t0, gbuf + t0, targets + t0, dH + t0 * p.D, P,
+                      part, inv_tau);
   }
   L.run(GRPO_K_LOSS_FINALIZE, [&] {
     hipLaunchKernelGGL(loss_finalize_kernel, dim3(1), dim3(1024), 0, L.stream, wl, (int)p.T, loss);
   });
+  return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_E_HIP;
+}
+
+// Backward of grpo_logp_fwd: dH = (grad / tau) (W[y] - P W) per chunk, from the forward's lse.
+template <typename T>
+grpo_status logp_bwd_impl(const Plan& p, const grpo_shape* shape, const T* H, const T* W, const int32_t* targets,
+                          const float* lse, const float* grad, T* dH, char* ws, Launcher& L) {
+  const float inv_tau = 1.0f / shape->temperature;
+  T* P = reinterpret_cast<T*>(ws + p.off_P);
+  char* Hf = ws + p.off_Hf;
+  float* part = reinterpret_cast<float*>(ws + p.off_part);
+  bool use_wt = false;
+  const T* WT = p.T > 0 ? maybe_transpose_w<T>(L, p, W, ws, use_wt) : nullptr;
+  for (int64_t k = 0; k < p.nchunks; ++k) {
+    const int64_t t0 = k * p.C;
+    const int rows = (int)(p.T - t0 < p.C ? p.T - t0 : p.C);
+    const T* Hc = H + t0 * p.D;
+    if constexpr (sizeof(T) == 2) enqueue_frag_copy(L, p, Hc, rows, Hf);
+    backward_chunk<T>(L, p, W, WT, use_wt, Hc, Hf, rows, k, lse + t0, grad + t0, targets + t0, dH + t0 * p.D, P,
+                      part, inv_tau);
+  }
   return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_E_HIP;
 }
 
@@ -1616,10 +1674,52 @@ grpo_status grpo_loss_fwd_bwd(const grpo_shape* shape, const grpo_loss_params* p
   char* ws = reinterpret_cast<char*>(workspace);
   const float* ref = params->beta != 0.0f ? ref_logp : nullptr;
   if (p.dtype == GRPO_BF16)
-    return loss_impl<__bf16>(p, shape, params, (const __bf16*)H, (const __bf16*)W, targets, cu_seqlens, mask,
+    return loss_impl<__bf16>(p, shape, 1, params, (const __bf16*)H, (const __bf16*)W, targets, cu_seqlens, mask,
                              old_logp, ref, adv, loss, logp, token_loss, (__bf16*)dH, ws, L);
-  return loss_impl<float>(p, shape, params, (const float*)H, (const float*)W, targets, cu_seqlens, mask, old_logp,
-                          ref, adv, loss, logp, token_loss, (float*)dH, ws, L);
+  return loss_impl<float>(p, shape, 1, params, (const float*)H, (const float*)W, targets, cu_seqlens, mask,
+                          old_logp, ref, adv, loss, logp, token_loss, (float*)dH, ws, L);
+}
+
+grpo_status grpo_logp_bwd(const grpo_shape* shape, const void* H, const void* W, const int32_t* targets,
+                          const float* lse, const float* grad_logp, void* dH, void* workspace, size_t workspace_bytes,
+                          void* stream, grpo_timer* timer) {
+  Plan p;
+  grpo_status st = make_plan(shape, 1, true, &p);
+  if (st != GRPO_OK) return st;
+  if (!W) return GRPO_E_NULL;
+  if (p.T > 0 && (!H || !targets || !lse || !grad_logp || !dH)) return GRPO_E_NULL;
+  if (!aligned16(H) || !aligned16(W) || !aligned16(dH)) return GRPO_E_UNSUPPORTED;
+  if (!ws_ok(p, workspace, workspace_bytes)) return GRPO_E_WORKSPACE;
+  if (p.T == 0) return GRPO_OK;
+  (void)hipGetLastError();
+  Launcher L{reinterpret_cast<hipStream_t>(stream), timer};
+  char* ws = reinterpret_cast<char*>(workspace);
+  if (p.dtype == GRPO_BF16)
+    return logp_bwd_impl<__bf16>(p, shape, (const __bf16*)H, (const __bf16*)W, targets, lse, grad_logp,
+                                 (__bf16*)dH, ws, L);
+  return logp_bwd_impl<float>(p, shape, (const float*)H, (const float*)W, targets, lse, grad_logp, (float*)dH, ws,
+                              L);
+}
+
+grpo_status grpo_ce_loss_fwd_bwd(const grpo_shape* shape, const void* H, const void* W, const int32_t* targets,
+                                 const uint8_t* mask, double* loss, float* logp, float* token_loss, void* dH,
+                                 void* workspace, size_t workspace_bytes, void* stream, grpo_timer* timer) {
+  Plan p;
+  grpo_status st = make_plan(shape, 1, true, &p);
+  if (st != GRPO_OK) return st;
+  if (!loss || !W) return GRPO_E_NULL;
+  if (p.T > 0 && (!H || !targets || !dH)) return GRPO_E_NULL;
+  if (!aligned16(H) || !aligned16(W) || !aligned16(dH)) return GRPO_E_UNSUPPORTED;
+  if (!ws_ok(p, workspace, workspace_bytes)) return GRPO_E_WORKSPACE;
+  (void)hipGetLastError();
+  Launcher L{reinterpret_cast<hipStream_t>(stream), timer};
+  char* ws = reinterpret_cast<char*>(workspace);
+  // one sequence spanning the stream (its bounds are written on the device): token-mean weights
+  if (p.dtype == GRPO_BF16)
+    return loss_impl<__bf16>(p, shape, 2, nullptr, (const __bf16*)H, (const __bf16*)W, targets, nullptr, mask,
+                             nullptr, nullptr, nullptr, loss, logp, token_loss, (__bf16*)dH, ws, L);
+  return loss_impl<float>(p, shape, 2, nullptr, (const float*)H, (const float*)W, targets, nullptr, mask, nullptr,
+                          nullptr, nullptr, loss, logp, token_loss, (float*)dH, ws, L);
 }
 
 grpo_status grpo_debug_token_index(const int32_t* cu_seqlens, int64_t num_seqs, int64_t T, int64_t chunk_tokens,

@@ -61,6 +61,10 @@ def lib() -> ctypes.CDLL:
         L.grpo_loss_fwd_bwd.argtypes = [sp, ctypes.POINTER(GrpoLossParams), vp, vp, vp, vp, i64, vp, vp,
                                         vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
         L.grpo_loss_fwd_bwd.restype = ctypes.c_int
+        L.grpo_logp_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+        L.grpo_logp_bwd.restype = ctypes.c_int
+        L.grpo_ce_loss_fwd_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+        L.grpo_ce_loss_fwd_bwd.restype = ctypes.c_int
         L.grpo_status_string.argtypes = [ctypes.c_int]
         L.grpo_status_string.restype = ctypes.c_char_p
         L.grpo_debug_token_index.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, sz, vp]
@@ -176,6 +180,51 @@ def grpo_logp_fwd(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, chunk
                              _ptr(ws), wsn, _stream(stream), timer.handle if timer else None)
     _check(st, "grpo_logp_fwd")
     return (logp, lse) if return_lse else logp
+
+
+def grpo_logp_bwd(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: torch.Tensor,
+                  grad_logp: torch.Tensor, chunk_tokens: int, temperature: float = 1.0, *, dH=None,
+                  workspace=None, stream=None, timer: Timer | None = None) -> torch.Tensor:
+    """dH of sum_t grad_logp[t] * logp_t, recomputing each chunk's logits from the forward's lse."""
+    for t, n in ((H, "H"), (W, "W"), (targets, "targets"), (lse, "lse"), (grad_logp, "grad_logp")):
+        _dev(t, n)
+    T, D = H.shape
+    V = W.shape[0]
+    shape = make_shape(T, D, V, chunk_tokens, _dtype_code(H), temperature)
+    nbytes = int(lib().grpo_workspace_bytes(ctypes.byref(shape), 1, 1))
+    ws, wsn = _workspace(nbytes, workspace, H.device)
+    if dH is None:
+        dH = torch.empty_like(H)
+    st = lib().grpo_logp_bwd(ctypes.byref(shape), _ptr(H), _ptr(W), _ptr(targets), _ptr(lse), _ptr(grad_logp),
+                             _ptr(dH), _ptr(ws), wsn, _stream(stream), timer.handle if timer else None)
+    _check(st, "grpo_logp_bwd")
+    return dH
+
+
+def grpo_ce_loss_fwd_bwd(H, W, targets, chunk_tokens, *, temperature=1.0, mask=None, want_logp=True,
+                         want_token_loss=False, dH=None, workspace=None, stream=None,
+                         timer: Timer | None = None):
+    """Mean cross-entropy over the unmasked tokens, per-token logp, and dL/dH."""
+    for t, n in ((H, "H"), (W, "W"), (targets, "targets")):
+        _dev(t, n)
+    if mask is not None:
+        _dev(mask, "mask")
+    T, D = H.shape
+    V = W.shape[0]
+    shape = make_shape(T, D, V, chunk_tokens, _dtype_code(H), temperature)
+    nbytes = int(lib().grpo_workspace_bytes(ctypes.byref(shape), 1, 1))
+    ws, wsn = _workspace(nbytes, workspace, H.device)
+    dev = H.device
+    loss = torch.empty(1, dtype=torch.float64, device=dev)
+    logp = torch.empty(T, dtype=torch.float32, device=dev) if want_logp else None
+    tl = torch.empty(T, dtype=torch.float32, device=dev) if want_token_loss else None
+    if dH is None:
+        dH = torch.empty_like(H)
+    st = lib().grpo_ce_loss_fwd_bwd(ctypes.byref(shape), _ptr(H), _ptr(W), _ptr(targets), _ptr(mask), _ptr(loss),
+                                    _ptr(logp), _ptr(tl), _ptr(dH), _ptr(ws), wsn, _stream(stream),
+                                    timer.handle if timer else None)
+    _check(st, "grpo_ce_loss_fwd_bwd")
+    return dict(loss=loss, logp=logp, token_loss=tl, dH=dH)
 
 
 def grpo_advantages(rewards: torch.Tensor, group_size: int, std_mode: str = "unbiased", eps: float = 1e-4,

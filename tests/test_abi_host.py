@@ -143,3 +143,38 @@ def test_debug_index_and_timer_validation():
     assert lib.grpo_timer_create(0, ctypes.byref(h)) == 3
     assert lib.grpo_timer_create(4, None) == 1
     assert lib.grpo_timer_read(None, 0, None, None, None) == 1
+
+
+def test_logp_bwd_validation():
+    lib = B.lib()
+    ws = ctypes.c_void_p(1 << 20)
+
+    def f(sh=None, H=FAKE, W=FAKE, y=FAKE, lse=FAKE, g=FAKE, dH=FAKE, wsp=ws, n=1 << 40):
+        sh = sh or shape()
+        return lib.grpo_logp_bwd(ctypes.byref(sh), H, W, y, lse, g, dH, wsp, n, None, None)
+
+    assert lib.grpo_logp_bwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, 1 << 40, None, None) == 1
+    for k in ("H", "W", "y", "lse", "g", "dH"):
+        assert f(**{k: None}) == 1, k
+    assert f(shape(tau=0.0)) == 3
+    assert f(shape(D=60)) == 5
+    assert f(dH=ctypes.c_void_p((1 << 20) + 4)) == 5
+    assert f(n=16) == 4
+    assert f(wsp=ctypes.c_void_p((1 << 20) + 16)) == 4
+    assert f(shape(T=0), H=None, y=None, lse=None, g=None, dH=None) == 0  # nothing to do
+
+
+def test_ce_loss_validation():
+    lib = B.lib()
+
+    def f(sh=None, H=FAKE, W=FAKE, y=FAKE, loss=FAKE, dH=FAKE, n=1 << 40, wsp=FAKE):
+        sh = sh or shape()
+        return lib.grpo_ce_loss_fwd_bwd(ctypes.byref(sh), H, W, y, None, loss, None, None, dH, wsp, n, None,
+                                         None)
+
+    for k in ("H", "W", "y", "loss", "dH"):
+        assert f(**{k: None}) == 1, k
+    assert f(shape(tau=float("inf"))) == 3
+    assert f(shape(dtype=3)) == 5
+    assert f(n=16) == 4
+    assert f(wsp=None) == 4

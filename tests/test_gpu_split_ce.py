@@ -1,0 +1,108 @@
+"""GPU parity of the split backward (grpo_logp_bwd) and the chunked cross-entropy
+(grpo_ce_loss_fwd_bwd) against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from rl_fine_tuning_amd import Timer, grpo_ce_loss_fwd_bwd, grpo_logp_bwd, grpo_logp_fwd
+from synth import make_case
+
+from gpu_cases import DH_REL_L2, LOGP_ATOL, LOSS_RTOL, dev_matrix, host_matrix, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(seed, D, V, lengths, dtype="bf16", bad=()):
+    c = make_case(seed, D=D, V=V, G=1, lengths=lengths, dtype=dtype, rewards=("uniform",), chunk=256)
+    y = c.targets.copy()
+    for t in bad:
+        y[t] = V if t % 2 == 0 else -1
+    H64, W64 = oracle.widen(c.H, dtype), oracle.widen(c.W, dtype)
+    d = dict(H=dev_matrix(c.H, dtype), W=dev_matrix(c.W, dtype), targets=torch.from_numpy(y).cuda())
+    return c, y, H64, W64, d
+
+
+@pytest.mark.parametrize("dtype,D,V,lengths,chunk,tau,expect_wt", [
+    ("bf16", 256, 10000, [300, 400, 324], 512, 0.7, 1),   # W^T copy, split vocabulary
+    ("bf16", 264, 999, [700, 1], 128, 1.0, 0),           # in-register W^T, ragged tail
+    ("bf16", 1024, 32000, [1500, 548], 4096, 1.0, 1),    # one chunk, several tiles each way
+    ("f32", 68, 333, [90, 40, 70], 50, 0.7, 0),
+])
+def test_logp_bwd_matches_oracle(dtype, D, V, lengths, chunk, tau, expect_wt):
+    say(f"logp_bwd {dtype} D={D} V={V} T={sum(lengths)} chunk={chunk} tau={tau}")
+    c, y, H64, W64, d = _inputs(41 + D, D, V, lengths, dtype, bad=(5,))
+    T = len(y)
+    grad = np.random.default_rng(42).standard_normal(T).astype(np.float32) * 0.01
+    grad[np.random.default_rng(43).random(T) < 0.1] = 0.0
+    logp, lse = grpo_logp_fwd(d["H"], d["W"], d["targets"], chunk, tau, return_lse=True)
+    tm = Timer(1024)
+    dH = grpo_logp_bwd(d["H"], d["W"], d["targets"], lse, torch.from_numpy(grad).cuda(), chunk, tau, timer=tm)
+    torch.cuda.synchronize()
+    assert tm.read("transpose_w")[1] == expect_wt
+    assert tm.read("logits_lse")[1] == 0  # the backward does not redo the forward's LSE GEMM
+    tm.close()
+    ref = oracle.logp_backward(H64, W64, y, grad.astype(np.float64), tau)
+    got = oracle.widen(host_matrix(dH, dtype), dtype)
+    e = rel_l2(got, ref)
+    say(f"  dH rel L2 {e:.2e}")
+    assert e <= (1e-4 if dtype == "f32" else DH_REL_L2)
+    zero = (grad == 0) | (y < 0) | (y >= V)
+    assert np.all(got[zero] == 0)
+
+
+def test_logp_bwd_chunk_invariance():
+    c, y, H64, W64, d = _inputs(47, 192, 900, [333, 222, 111])
+    T = len(y)
+    grad = torch.from_numpy(np.random.default_rng(48).standard_normal(T).astype(np.float32)).cuda()
+    _, lse = grpo_logp_fwd(d["H"], d["W"], d["targets"], 64, return_lse=True)
+    base = grpo_logp_bwd(d["H"], d["W"], d["targets"], lse, grad, T)
+    for chunk in (1, 100, 256):
+        got = grpo_logp_bwd(d["H"], d["W"], d["targets"], lse, grad, chunk)
+        rel = (got.float() - base.float()).norm() / base.float().norm()
+        assert rel.item() <= 1e-3, (chunk, rel.item())
+
+
+@pytest.mark.parametrize("dtype,D,V,lengths,chunk,tau,mask_frac", [
+    ("bf16", 256, 10000, [300, 400, 324], 512, 0.7, 0.2),
+    ("bf16", 520, 1288, [513, 400, 287], 300, 1.0, 0.0),
+    ("f32", 68, 333, [90, 40, 70], 50, 1.0, 0.3),
+])
+def test_ce_loss_matches_oracle(dtype, D, V, lengths, chunk, tau, mask_frac):
+    say(f"ce {dtype} D={D} V={V} T={sum(lengths)} chunk={chunk} tau={tau} mask={mask_frac}")
+    c, y, H64, W64, d = _inputs(51 + D, D, V, lengths, dtype, bad=(7,))
+    T = len(y)
+    mask = np.ones(T, np.uint8)
+    mask[np.random.default_rng(52).random(T) < mask_frac] = 0
+    mask[7] = 0  # the invalid target is masked, so the loss stays finite
+    out = oracle.cross_entropy_loss_and_grad(H64, W64, y, mask, tau)
+    got = grpo_ce_loss_fwd_bwd(d["H"], d["W"], d["targets"], chunk, temperature=tau,
+                               mask=torch.from_numpy(mask).cuda(), want_token_loss=True)
+    torch.cuda.synchronize()
+    L = float(got["loss"].cpu()[0])
+    assert abs(L - out["loss"]) <= LOSS_RTOL * abs(out["loss"]), (L, out["loss"])
+    lp = got["logp"].cpu().numpy().astype(np.float64)
+    ok = np.isfinite(out["logp"])
+    assert np.array_equal(np.isfinite(lp), ok)
+    assert np.abs(lp[ok] - out["logp"][ok]).max() <= LOGP_ATOL
+    assert np.array_equal(got["token_loss"].cpu().numpy(), -got["logp"].cpu().numpy(), equal_nan=True)
+    dH = oracle.widen(host_matrix(got["dH"], dtype), dtype)
+    e = rel_l2(dH, out["dH"])
+    say(f"  loss {L:.8f} vs {out['loss']:.8f}, dH rel L2 {e:.2e}")
+    assert e <= (1e-4 if dtype == "f32" else DH_REL_L2)
+    assert np.all(dH[mask == 0] == 0)
+
+
+def test_ce_all_masked_and_counted_invalid_target():
+    c, y, H64, W64, d = _inputs(57, 128, 700, [200, 100])
+    T = len(y)
+    got = grpo_ce_loss_fwd_bwd(d["H"], d["W"], d["targets"], 128, mask=torch.zeros(T, dtype=torch.uint8).cuda())
+    torch.cuda.synchronize()
+    assert float(got["loss"].cpu()[0]) == 0.0
+    assert torch.count_nonzero(got["dH"]).item() == 0
+    y2 = y.copy()
+    y2[11] = 700
+    got = grpo_ce_loss_fwd_bwd(d["H"], d["W"], torch.from_numpy(y2).cuda(), 128)
+    torch.cuda.synchronize()
+    assert np.isnan(float(got["loss"].cpu()[0]))
+    assert torch.count_nonzero(got["dH"][11]).item() == 0
