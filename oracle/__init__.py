@@ -6,6 +6,7 @@ from .grpo_oracle import (  # noqa: F401
     grpo_loss_and_grad,
     grpo_loss_from_logp,
     grpo_token_terms,
+    logit_map,
     logits,
     logp_backward,
     selective_log_softmax,

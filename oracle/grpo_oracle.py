@@ -71,13 +71,41 @@ def widen(x: np.ndarray, dtype: str) -> np.ndarray:
 
 # ---------------------------------------------------------------- log-softmax
 
-def logits(H: np.ndarray, W: np.ndarray, temperature: float = 1.0) -> np.ndarray:
-    """z[t, v] = (H[t] . W[v]) / temperature for every vocabulary entry ([P4], call args)."""
-    return (H @ W.T) / temperature
+def logit_map(x: np.ndarray, temperature: float = 1.0, scale: float = 1.0, softcap: float = 0.0):
+    """Logits z from the raw lm_head products x = H[t] . W[v], and dz/dx.
+
+    [P4] lists the call's arguments logit_scale_multiply, logit_scale_divide,
+    logit_softcapping and temperature (item 3 after the call: softcapping
+    and temperature scaling are supported) without fixing their order; the
+    reading taken here: u = scale * x (scale = multiply / divide), with a
+    softcap c > 0 u = c * tanh(u / c), and z = u / temperature.
+    """
+    u = scale * x
+    if softcap > 0:
+        t = np.tanh(u / softcap)
+        return softcap * t / temperature, scale * (1.0 - t * t) / temperature
+    return u / temperature, np.full(np.shape(x), scale / temperature)
+
+
+def logits(H: np.ndarray, W: np.ndarray, temperature: float = 1.0, scale: float = 1.0,
+           softcap: float = 0.0) -> np.ndarray:
+    """z[t, v] for every vocabulary entry: logit_map of H[t] . W[v] ([P4], call args)."""
+    return logit_map(H @ W.T, temperature, scale, softcap)[0]
+
+
+def _dH_rows(H_rows, W, y, lse_rows, g_rows, temperature, scale, softcap):
+    """g_t * d logp_t / dH_t for rows with a valid target: the recomputed logits give
+    softmax p; d logp / dz = onehot(y) - p; dz/dx from logit_map; dx/dH = W."""
+    z, dz = logit_map(H_rows @ W.T, temperature, scale, softcap)
+    p = np.exp(z - lse_rows[:, None])
+    dl = -p
+    dl[np.arange(dl.shape[0]), y] += 1.0
+    return g_rows[:, None] * ((dl * dz) @ W)
 
 
 def selective_log_softmax(H: np.ndarray, W: np.ndarray, targets: np.ndarray,
-                          temperature: float = 1.0, block: int = ROW_BLOCK):
+                          temperature: float = 1.0, block: int = ROW_BLOCK, scale: float = 1.0,
+                          softcap: float = 0.0):
     """Per-token log-probability of the target id, and the log-sum-exp.
 
     Brute force over the full vocabulary, a block of rows at a time ([P4]:
@@ -90,7 +118,7 @@ def selective_log_softmax(H: np.ndarray, W: np.ndarray, targets: np.ndarray,
     lse = np.empty(T)
     for r0 in range(0, T, block):
         r1 = min(T, r0 + block)
-        z = logits(H[r0:r1], W, temperature)
+        z = logits(H[r0:r1], W, temperature, scale, softcap)
         m = z.max(axis=1)
         l = m + np.log(np.exp(z - m[:, None]).sum(axis=1))
         y = targets[r0:r1].astype(np.int64)
@@ -220,17 +248,18 @@ def grpo_loss_from_logp(logp, old_logp, ref_logp, adv, cu, mask, clip_eps_low=0.
 
 def grpo_loss_and_grad(H, W, targets, cu, mask, old_logp, ref_logp, adv, temperature=1.0,
                        clip_eps_low=0.2, clip_eps_high=0.2, beta=0.001, agg="seq_mean",
-                       block: int = ROW_BLOCK):
+                       block: int = ROW_BLOCK, scale: float = 1.0, softcap: float = 0.0):
     """Loss, log-probs and the gradient of the loss with respect to H.
 
     dH_t = (g_t / temperature) * (W[y_t] - sum_v softmax(z_t)_v W[v]), the
     chain rule through logp_t = z_{t,y_t} - LSE_t, whose derivative with
     respect to z_t is onehot(y_t) - softmax(z_t) ([P4], the recompute
-    backward).  Rows with g_t = 0 or an out-of-range target are exactly 0.
+    backward); with a logit scale or softcap the softmax term carries dz/dx (see
+    logit_map).  Rows with g_t = 0 or an out-of-range target are exactly 0.
     """
     T, D = H.shape
     V = W.shape[0]
-    logp, lse = selective_log_softmax(H, W, targets, temperature, block)
+    logp, lse = selective_log_softmax(H, W, targets, temperature, block, scale, softcap)
     L, ell, g = grpo_loss_from_logp(logp, old_logp, ref_logp, adv, cu, mask, clip_eps_low,
                                     clip_eps_high, beta, agg)
     dH = np.zeros((T, D))
@@ -242,15 +271,13 @@ def grpo_loss_and_grad(H, W, targets, cu, mask, old_logp, ref_logp, adv, tempera
         live = (g[r0:r1] != 0) & (y >= 0) & (y < V)
         if not live.any():
             continue
-        z = logits(H[r0:r1][live], W, temperature)
-        p = np.exp(z - lse[rows[live]][:, None])
-        dz = -p
-        dz[np.arange(dz.shape[0]), y[live]] += 1.0
-        dH[rows[live]] = (g[rows[live]] / temperature)[:, None] * (dz @ W)
+        dH[rows[live]] = _dH_rows(H[r0:r1][live], W, y[live], lse[rows[live]], g[rows[live]],
+                                  temperature, scale, softcap)
     return dict(loss=L, logp=logp, lse=lse, token_loss=ell, g=g, dH=dH)
 
 
-def logp_backward(H, W, targets, grad_logp, temperature=1.0, block: int = ROW_BLOCK):
+def logp_backward(H, W, targets, grad_logp, temperature=1.0, block: int = ROW_BLOCK, scale: float = 1.0,
+                  softcap: float = 0.0):
     """Gradient with respect to H of sum_t grad_logp[t] * logp_t.
 
     The backward of the chunked selective log-softmax ([P4], "Auslagern von
@@ -263,7 +290,7 @@ def logp_backward(H, W, targets, grad_logp, temperature=1.0, block: int = ROW_BL
     T, D = H.shape
     V = W.shape[0]
     g = np.asarray(grad_logp, dtype=np.float64)
-    _, lse = selective_log_softmax(H, W, targets, temperature, block)
+    _, lse = selective_log_softmax(H, W, targets, temperature, block, scale, softcap)
     dH = np.zeros((T, D))
     y_all = np.asarray(targets, dtype=np.int64)
     for r0 in range(0, T, block):
@@ -273,15 +300,13 @@ def logp_backward(H, W, targets, grad_logp, temperature=1.0, block: int = ROW_BL
         live = (g[r0:r1] != 0) & (y >= 0) & (y < V)
         if not live.any():
             continue
-        z = logits(H[r0:r1][live], W, temperature)
-        p = np.exp(z - lse[rows[live]][:, None])
-        dz = -p
-        dz[np.arange(dz.shape[0]), y[live]] += 1.0
-        dH[rows[live]] = (g[rows[live]] / temperature)[:, None] * (dz @ W)
+        dH[rows[live]] = _dH_rows(H[r0:r1][live], W, y[live], lse[rows[live]], g[rows[live]],
+                                  temperature, scale, softcap)
     return dH
 
 
-def cross_entropy_loss_and_grad(H, W, targets, mask=None, temperature=1.0, block: int = ROW_BLOCK):
+def cross_entropy_loss_and_grad(H, W, targets, mask=None, temperature=1.0, block: int = ROW_BLOCK,
+                                scale: float = 1.0, softcap: float = 0.0):
     """Chunked cross-entropy (the supervised loss the same chunked log-softmax
     serves): L = -(1/N) sum_t mask_t logp_t with N = sum_t mask_t (L = 0 and
     dH = 0 when N = 0), per-token loss -logp_t, g_t = dL/dlogp_t = -mask_t / N,
@@ -290,26 +315,23 @@ def cross_entropy_loss_and_grad(H, W, targets, mask=None, temperature=1.0, block
     """
     T = H.shape[0]
     m = np.ones(T) if mask is None else np.asarray(mask, dtype=np.float64)
-    logp, lse = selective_log_softmax(H, W, targets, temperature, block)
+    logp, lse = selective_log_softmax(H, W, targets, temperature, block, scale, softcap)
     n = m.sum()
     w = m / n if n > 0 else np.zeros(T)
     terms = [w[t] * (-logp[t]) for t in range(T) if w[t] != 0]
     L = math.fsum(terms) if terms else 0.0
     g = -w
-    dH = logp_backward(H, W, targets, g, temperature, block)
+    dH = logp_backward(H, W, targets, g, temperature, block, scale, softcap)
     return dict(loss=L, logp=logp, lse=lse, token_loss=-logp, g=g, dH=dH)
 
 
-def grad_rows(H_rows, W, targets_rows, lse_rows, g_rows, temperature=1.0):
+def grad_rows(H_rows, W, targets_rows, lse_rows, g_rows, temperature=1.0, scale=1.0, softcap=0.0):
     """dH for selected rows given their lse and g (row-local, for sampled checks)."""
     V = W.shape[0]
     out = np.zeros(H_rows.shape)
     y = np.asarray(targets_rows, dtype=np.int64)
     live = (g_rows != 0) & (y >= 0) & (y < V)
     if live.any():
-        z = logits(H_rows[live], W, temperature)
-        p = np.exp(z - lse_rows[live][:, None])
-        dz = -p
-        dz[np.arange(dz.shape[0]), y[live]] += 1.0
-        out[live] = (g_rows[live] / temperature)[:, None] * (dz @ W)
+        out[live] = _dH_rows(H_rows[live], W, y[live], lse_rows[live], g_rows[live], temperature, scale,
+                             softcap)
     return out

@@ -409,3 +409,57 @@ def test_cross_entropy_all_masked_and_masked_invalid_target():
     assert np.isfinite(out["loss"]) and np.isnan(out["logp"][2]) and np.all(out["dH"][2] == 0)
     mask[2] = 1
     assert np.isnan(oracle.cross_entropy_loss_and_grad(H, W, y, mask)["loss"])
+
+
+# ------------------------------------------------------ logit scale and softcap
+
+def test_logit_map_derivative_and_limits():
+    x = np.linspace(-40, 40, 81)
+    for (tau, s, c) in [(1.0, 1.0, 0.0), (0.7, 0.5, 0.0), (0.7, 1.3, 10.0), (1.0, 1.0, 30.0)]:
+        z, dz = oracle.logit_map(x, tau, s, c)
+        h = 1e-6
+        fd = (oracle.logit_map(x + h, tau, s, c)[0] - oracle.logit_map(x - h, tau, s, c)[0]) / (2 * h)
+        np.testing.assert_allclose(dz, fd, rtol=1e-7, atol=2e-8)  # FD rounding ~ eps |z| / h
+        if c > 0:
+            assert np.all(np.abs(z) <= c / tau + 1e-12)  # the cap bounds |z| by c / tau
+    z_big, _ = oracle.logit_map(x, 0.7, 1.3, 1e9)  # a cap far above every |s x| changes nothing
+    np.testing.assert_allclose(z_big, 1.3 * x / 0.7, rtol=1e-12)
+    np.testing.assert_allclose(oracle.logit_map(x, 2.0, 2.0)[0], x, rtol=0, atol=0)
+
+
+def test_softcapped_loss_gradient_by_finite_differences():
+    H, W, y, cu, mask, old, ref, adv, tau = _case(31)
+    kw = dict(clip_eps_low=0.2, clip_eps_high=0.2, beta=0.1, scale=0.8, softcap=3.0)
+    out = oracle.grpo_loss_and_grad(H, W, y, cu, mask, old, ref, adv, tau, **kw)
+    rho = np.exp(out["logp"] - old)
+    assert np.all(np.abs(rho - 0.8) > 1e-3) and np.all(np.abs(rho - 1.2) > 1e-3)
+    lkw = {k: kw[k] for k in ("clip_eps_low", "clip_eps_high", "beta")}
+
+    def loss(Hx):
+        lp, _ = oracle.selective_log_softmax(Hx, W, y, tau, scale=0.8, softcap=3.0)
+        return oracle.grpo_loss_from_logp(lp, old, ref, adv, cu, mask, **lkw)[0]
+
+    h = 1e-6
+    fd = np.zeros_like(H)
+    for t in range(H.shape[0]):
+        for d in range(H.shape[1]):
+            e = np.zeros_like(H)
+            e[t, d] = h
+            fd[t, d] = (loss(H + e) - loss(H - e)) / (2 * h)
+    assert np.linalg.norm(out["dH"] - fd) / np.linalg.norm(fd) < 1e-6
+
+
+def test_softcapped_cross_entropy_matches_torch_autograd():
+    torch = pytest.importorskip("torch")
+    H, W, y = _tiny(32, T=11, D=6, V=17, scale=2.0)
+    tau, s, c = 0.7, 1.5, 4.0
+    out = oracle.cross_entropy_loss_and_grad(H, W, y, None, tau, scale=s, softcap=c)
+    Ht = torch.tensor(H, requires_grad=True)
+    z = c * torch.tanh(s * (Ht @ torch.tensor(W).T) / c) / tau
+    ce = torch.nn.functional.cross_entropy(z, torch.tensor(y), reduction="mean")
+    ce.backward()
+    assert abs(out["loss"] - ce.item()) <= 1e-14 * abs(ce.item())
+    np.testing.assert_allclose(out["dH"], Ht.grad.numpy(), rtol=0, atol=1e-14)
+    lp, _ = oracle.selective_log_softmax(H, W, y, tau, scale=s, softcap=c)
+    ref = torch.log_softmax(z.detach(), dim=1)[torch.arange(11), torch.tensor(y)].numpy()
+    np.testing.assert_allclose(lp, ref, rtol=0, atol=1e-13)
