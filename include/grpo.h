@@ -68,9 +68,15 @@ typedef enum { GRPO_AGG_SEQ_MEAN = 0, GRPO_AGG_TOKEN_MEAN = 1 } grpo_agg;
 typedef enum { GRPO_STD_UNBIASED = 0, GRPO_STD_POPULATION = 1 } grpo_std;
 
 /* Problem shape.  T >= 0 tokens, D >= 1 hidden size (multiple of 8 for bf16, of 4 for
- * fp32), V >= 1 vocabulary size, chunk_tokens >= 1 tokens per chunk.  T, V and
- * chunk_tokens are below 2^31.  temperature > 0 and finite: logits are
- * (H . W[v]) / temperature ([P4], call arguments). */
+ * fp32, at most 2^20), V >= 1 vocabulary size, chunk_tokens >= 1 tokens per chunk.  T, V
+ * and chunk_tokens are below 2^31.
+ * Logits ([P4], the arguments of the chunked call: logit_scale_multiply,
+ * logit_scale_divide, logit_softcapping, temperature; item 3 after it): with
+ * x = H[t] . W[v] and s = logit_scale_multiply / logit_scale_divide,
+ *   z = s x / temperature                                (logit_softcapping == 0)
+ *   z = c tanh(s x / c) / temperature,  c = logit_softcapping  (> 0).
+ * temperature > 0 and finite; the three logit arguments are finite and >= 0, and 0 means
+ * "not used" (a factor of 1, no cap), so a zero-initialized tail gives plain logits. */
 typedef struct {
   int64_t T;
   int64_t D;
@@ -78,6 +84,9 @@ typedef struct {
   int64_t chunk_tokens;
   int32_t dtype;       /* grpo_dtype */
   float temperature;
+  float logit_scale_multiply;
+  float logit_scale_divide;
+  float logit_softcapping;
 } grpo_shape;
 
 /* GRPO objective parameters ([P2], [P3], [P1]).  The ratio is clipped to
@@ -145,7 +154,8 @@ grpo_status grpo_advantages(const float* rewards, int64_t num_seqs, int64_t grou
  *   l_t    = -(surr_t - beta k3_t)
  *   loss   = sum_t w_t l_t   with w_t = mask_t / (S * L_s(t)) (seq mean; L_i = unmasked
  *            tokens of sequence i) or w_t = mask_t / sum(mask) (token mean)
- *   dH_t   = (g_t / temperature) (W[y_t] - sum_v softmax(z_t)_v W[v]),
+ *   dH_t   = g_t (z'_t,y W[y_t] - sum_v softmax(z_t)_v z'_t,v W[v]),  z' = dz/dx
+ *            (= s / temperature without a softcap),
  *            g_t = w_t (-(rho A if rho A <= clip(rho) A else 0) + beta (1 - exp(d_t)))
  * Arguments:
  *   cu_seqlens [host] int32 [num_seqs + 1]: cu[0] = 0, non-decreasing, cu[S] = T.
@@ -167,7 +177,7 @@ grpo_status grpo_loss_fwd_bwd(const grpo_shape* shape, const grpo_loss_params* p
 /* Backward of grpo_logp_fwd ([P4] "Auslagern von Aktivierungen fuer Log-Softmax": the
  * forward keeps only the per-token log-sum-exp; the backward recomputes each chunk's logits
  * and applies the incoming gradient of the log-probabilities):
- *   dH_t = (grad_logp_t / temperature) (W[y_t] - sum_v softmax(z_t)_v W[v]),
+ *   dH_t = grad_logp_t (z'_t,y W[y_t] - sum_v softmax(z_t)_v z'_t,v W[v]),  z' = dz/dx,
  * the gradient of sum_t grad_logp_t * logp_t with respect to H.  Any loss written on top of
  * the log-probabilities (other GRPO variants, other aggregations) back-propagates through it.
  *   H, W, targets, shape as for grpo_logp_fwd; lse fp32 [T]: the log-sum-exp grpo_logp_fwd

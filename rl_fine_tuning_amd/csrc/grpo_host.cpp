@@ -25,7 +25,29 @@ grpo_status validate_shape(const grpo_shape* s) {
   // 16-byte rows for the vector loads of the GEMMs
   if (s->D % (16 / elem_size(s->dtype)) != 0) return GRPO_E_UNSUPPORTED;
   if (!isfinite(s->temperature) || !(s->temperature > 0.0f)) return GRPO_E_VALUE;
+  for (float a : {s->logit_scale_multiply, s->logit_scale_divide, s->logit_softcapping})
+    if (!isfinite(a) || a < 0.0f) return GRPO_E_VALUE;
+  const LogitMap m = make_logit_map(s);
+  for (float a : {m.zscale, m.dscale, m.cap_in})
+    if (!isfinite(a)) return GRPO_E_VALUE;
+  if (!(m.zscale > 0.0f) || !(m.dscale > 0.0f)) return GRPO_E_VALUE;
   return GRPO_OK;
+}
+
+LogitMap make_logit_map(const grpo_shape* s) {
+  const double mul = s->logit_scale_multiply > 0.0f ? s->logit_scale_multiply : 1.0;
+  const double div = s->logit_scale_divide > 0.0f ? s->logit_scale_divide : 1.0;
+  const double sc = mul / div, tau = s->temperature, cap = s->logit_softcapping;
+  LogitMap m;
+  m.dscale = (float)(sc / tau);
+  if (cap > 0.0) {
+    m.zscale = (float)(cap / tau);
+    m.cap_in = (float)(sc / cap);
+  } else {
+    m.zscale = m.dscale;
+    m.cap_in = 0.0f;
+  }
+  return m;
 }
 
 grpo_status validate_loss_params(const grpo_loss_params* p) {

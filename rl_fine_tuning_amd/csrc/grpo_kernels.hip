@@ -95,6 +95,18 @@ __device__ __forceinline__ uint4 keep_first(uint4 x, int n) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// LogitMap (grpo_plan.h): temperature tau, scale s = multiply / divide, softcap c.  Without
+// a cap zscale = dscale = s / tau; with it zscale = c / tau, dscale = s / tau, cap_in = s / c.
+
+// tanh(a) from its definition (e^{2a} - 1) / (e^{2a} + 1) = 1 - 2 / (e^{2a} + 1), with the
+// Taylor series a - a^3 / 3 for |a| < 2^-6, where the subtraction would cancel; saturates
+// to +-1 for large |a|.
+__device__ __forceinline__ float tanh_fast(float a) {
+  const float e = __builtin_amdgcn_exp2f(2.0f * kLog2e * a);
+  const float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+  return fabsf(a) < 0.015625f ? a * fmaf(-a * a, 1.0f / 3.0f, 1.0f) : t;
+}
+
 struct GemmArgs {
   const void* a;      // LSE / PROBS: W [V, D].  DH: W [V, D], read transposed
   const void* b;      // LSE / PROBS: hidden-state chunk [rows, D].  DH: probabilities [rows, ldp]
@@ -107,7 +119,7 @@ struct GemmArgs {
   int tiles_a, tiles_b;
   int xcd_axis;       // 0: tiles_a are shared out over XCDs; 1: tiles_b
   int group_b;        // B tiles walked together
-  float inv_tau;
+  LogitMap lm;
   // LSE outputs: [tiles_a][b_rows]
   float* pm;
   float* ps;
@@ -118,6 +130,7 @@ struct GemmArgs {
   int V;
   // DH
   const float* g;         // [b_rows]
+  const float* zy;        // [b_rows]: target logits (the softcap's W[y] factor)
   const int32_t* targets; // [b_rows]
   const void* w;          // W, for the W[y] term
   void* dh;               // [b_rows, D] (ksplit == 1)
@@ -601,6 +614,16 @@ void gemm_kernel(const GemmArgs g) {
   const int hi = lane >> 5;     // which 4-row half of each 8-row group this lane holds
   const int col = lane & 31;
 
+  if constexpr (KIND == KIND_LSE || KIND == KIND_PROBS) {
+    if (g.lm.cap_in > 0.0f) {  // softcap: the accumulators become v = tanh(cap_in x)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = tanh_fast(acc[i][j][r] * g.lm.cap_in);
+    }
+  }
   if constexpr (KIND == KIND_LSE) {
     // Per token: max and sum of exp over this tile's vocabulary rows (those < V).
     float* red_m = reinterpret_cast<float*>(smem);
@@ -618,10 +641,10 @@ void gemm_kernel(const GemmArgs g) {
           if (full || v < g.a_rows) mx = fmaxf(mx, acc[i][j][r]);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float zmax = mx * g.inv_tau;  // inv_tau > 0, so this is the max of z
+      const float zmax = mx * g.lm.zscale;  // zscale > 0, so this is the max of z
       float s = 0.0f;
       if (mx > -INFINITY) {
-        const float c1 = g.inv_tau * kLog2e, c0 = -zmax * kLog2e;
+        const float c1 = g.lm.zscale * kLog2e, c0 = -zmax * kLog2e;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -648,9 +671,11 @@ void gemm_kernel(const GemmArgs g) {
       g.ps[(int64_t)tok * g.tiles_a + tile_a] = S;
     }
   } else if constexpr (KIND == KIND_PROBS) {
-    // P[token, v] = exp(z - lse[token]) for v < V, written as 4-element vectors.
+    // P[token, v] = exp(z - lse[token]) (times dv/d(cap_in x) = 1 - v^2 with a softcap) for
+    // v < V, written as 4-element vectors.
     T* P = reinterpret_cast<T*>(g.p);
-    const float c1 = g.inv_tau * kLog2e;
+    const float c1 = g.lm.zscale * kLog2e;
+    const bool cap = g.lm.cap_in > 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int tok = row_b0 + wn * 128 + 32 * j + col;
@@ -664,7 +689,11 @@ void gemm_kernel(const GemmArgs g) {
           const int v0 = row_a0 + wm * 128 + 32 * i + 8 * q + 4 * hi;
           float e[4];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) e[u] = __builtin_amdgcn_exp2f(fmaf(acc[i][j][4 * q + u], c1, c0));
+          for (int u = 0; u < 4; ++u) {
+            const float x = acc[i][j][4 * q + u];
+            e[u] = __builtin_amdgcn_exp2f(fmaf(x, c1, c0));
+            if (cap) e[u] *= 1.0f - x * x;
+          }
           if (v0 + 4 <= g.V) {
             store4(prow + v0, e[0], e[1], e[2], e[3]);
           } else if (v0 < g.ldp) {
@@ -697,7 +726,9 @@ void gemm_kernel(const GemmArgs g) {
       const float gt = g.g[tok];
       const int y = g.targets[tok];
       const bool live = gt != 0.0f && y >= 0 && y < g.V;
-      const float scale = gt * g.inv_tau;
+      const float scale = gt * g.lm.dscale;
+      const float ty = live ? g.zy[tok] / g.lm.zscale : 0.0f;
+      const float wyf = g.lm.cap_in > 0.0f ? 1.0f - ty * ty : 1.0f;  // dv/dx at the target
       const T* wrow = reinterpret_cast<const T*>(g.w) + (int64_t)(live ? y : 0) * g.D;
       T* dst = reinterpret_cast<T*>(g.dh) + (int64_t)tok * g.D;
 #pragma unroll
@@ -711,7 +742,7 @@ void gemm_kernel(const GemmArgs g) {
             float wv[4];
             load4(wrow + d0, wv);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) o[u] = scale * (wv[u] - acc[i][j][4 * q + u]);
+            for (int u = 0; u < 4; ++u) o[u] = scale * (wyf * wv[u] - acc[i][j][4 * q + u]);
           }
           store4(dst + d0, o[0], o[1], o[2], o[3]);
         }
@@ -730,7 +761,7 @@ void gemm_kernel(const GemmArgs g) {
 // The tile body is instantiated per kind of tile, so that the common case (a tile inside
 // the matrix, unsplit K) has straight-line epilogues: kEdge marks the last tile along the
 // vocabulary (LSE / PROBS) or hidden (DH) axis, kSplit a dH tile of a split vocabulary.
-template <int KIND, bool kEdge, bool kSplit>
+template <int KIND, bool kEdge, bool kSplit, bool kCap>
 __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int ks, int tile_a, int tb) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -858,7 +889,17 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
   // vocabulary, a one-time pass sets the accumulators of rows >= V to -inf (exp gives 0,
   // max ignores them); column bounds of 8-aligned groups are wave-uniform scalar tests
   // (every limit is a multiple of 8 and the tile origin of 256); only stores depend on
-  // the lane's token.
+  // the lane's token.  With a softcap the accumulators first become v = tanh(cap_in x).
+  if constexpr ((KIND == KIND_LSE || KIND == KIND_PROBS) && kCap) {
+#pragma unroll
+    for (int i = 0; i < kFA; ++i) {
+#pragma unroll
+      for (int j = 0; j < kFBW; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = tanh_fast(acc[i][j][r] * g.lm.cap_in);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
   if constexpr ((KIND == KIND_LSE || KIND == KIND_PROBS) && kEdge) {
     {
 #pragma unroll
@@ -883,10 +924,10 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float zmax = mx * g.inv_tau;  // inv_tau > 0, so this is the max of z
+      const float zmax = mx * g.lm.zscale;  // zscale > 0, so this is the max of z
       float sum = 0.0f;
       if (mx > -INFINITY) {
-        const float c1 = g.inv_tau * kLog2e, c0 = -zmax * kLog2e;
+        const float c1 = g.lm.zscale * kLog2e, c0 = -zmax * kLog2e;
 #pragma unroll
         for (int i = 0; i < kFA; ++i)
 #pragma unroll
@@ -901,12 +942,13 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
       __builtin_amdgcn_sched_barrier(0);
     }
   } else if constexpr (KIND == KIND_PROBS) {
-    // P[token, v] = exp(z - lse[token]) into the fragment-major copy used as the dH GEMM's
-    // B operand; the vocabulary padding up to the next 16 is written as zeros.  Rows of
-    // the copy past the chunk's tokens are written too (the dH GEMM ignores them).
+    // P[token, v] = exp(z - lse[token]) (times 1 - v^2 with a softcap) into the
+    // fragment-major copy used as the dH GEMM's B operand; the vocabulary padding up to the
+    // next 16 is written as zeros.  Rows of the copy past the chunk's tokens are written too
+    // (the dH GEMM ignores them).
     char* P = reinterpret_cast<char*>(g.p);
     const int vrem = g.p_ks * 16 - row_a0;  // uniform; multiple of 16
-    const float c1 = g.inv_tau * kLog2e;
+    const float c1 = g.lm.zscale * kLog2e;
 #pragma unroll
     for (int j = 0; j < kFBW; ++j) {
       const int tok = row_b0 + 64 * w + 32 * j + col;
@@ -919,7 +961,11 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
           const int v0 = row_a0 + 32 * i + 8 * q + 4 * hi;
           float e[4];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) e[u] = __builtin_amdgcn_exp2f(fmaf(acc[i][j][4 * q + u], c1, c0));
+          for (int u = 0; u < 4; ++u) {
+            const float x = acc[i][j][4 * q + u];
+            e[u] = __builtin_amdgcn_exp2f(fmaf(x, c1, c0));
+            if constexpr (kCap) e[u] = e[u] != 0.0f ? e[u] * (1.0f - x * x) : 0.0f;  // masked: x = -inf
+          }
           store4(reinterpret_cast<__bf16*>(P + frag_off(tok, v0, g.p_ks)), e[0], e[1], e[2], e[3]);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -951,7 +997,9 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
       const float gt = ok ? g.g[tok] : 0.0f;
       const int y = ok ? g.targets[tok] : 0;
       const bool live = gt != 0.0f && y >= 0 && y < g.V;
-      const float scale = live ? gt * g.inv_tau : 0.0f;
+      const float scale = live ? gt * g.lm.dscale : 0.0f;
+      const float ty = live ? g.zy[tok] / g.lm.zscale : 0.0f;
+      const float wyf = g.lm.cap_in > 0.0f ? 1.0f - ty * ty : 1.0f;  // dv/dx at the target
       const __bf16* wrow = reinterpret_cast<const __bf16*>(g.w) + (int64_t)(live ? y : 0) * g.D;
       __bf16* dst = reinterpret_cast<__bf16*>(g.dh) + (int64_t)(ok ? tok : 0) * g.D;
 #pragma unroll
@@ -963,7 +1011,7 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
           float wv[4], o[4];
           load4(wrow + d0, wv);
 #pragma unroll
-          for (int u = 0; u < 4; ++u) o[u] = live ? scale * (wv[u] - acc[i][j][4 * q + u]) : 0.0f;
+          for (int u = 0; u < 4; ++u) o[u] = live ? scale * (wyf * wv[u] - acc[i][j][4 * q + u]) : 0.0f;
           if (ok) store4(dst + d0, o[0], o[1], o[2], o[3]);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -987,15 +1035,18 @@ void gemm16_kernel(const GemmArgs g) {
   const bool edge = (tile_a + 1) * kTA > (kDH ? g.D : g.V);
   if constexpr (kDH) {
     if (g.ksplit > 1) {
-      if (edge) gemm16_tile<KIND, true, true>(g, smem, ks, tile_a, tb);
-      else gemm16_tile<KIND, false, true>(g, smem, ks, tile_a, tb);
+      if (edge) gemm16_tile<KIND, true, true, false>(g, smem, ks, tile_a, tb);
+      else gemm16_tile<KIND, false, true, false>(g, smem, ks, tile_a, tb);
     } else {
-      if (edge) gemm16_tile<KIND, true, false>(g, smem, ks, tile_a, tb);
-      else gemm16_tile<KIND, false, false>(g, smem, ks, tile_a, tb);
+      if (edge) gemm16_tile<KIND, true, false, false>(g, smem, ks, tile_a, tb);
+      else gemm16_tile<KIND, false, false, false>(g, smem, ks, tile_a, tb);
     }
+  } else if (g.lm.cap_in > 0.0f) {
+    if (edge) gemm16_tile<KIND, true, false, true>(g, smem, ks, tile_a, tb);
+    else gemm16_tile<KIND, false, false, true>(g, smem, ks, tile_a, tb);
   } else {
-    if (edge) gemm16_tile<KIND, true, false>(g, smem, ks, tile_a, tb);
-    else gemm16_tile<KIND, false, false>(g, smem, ks, tile_a, tb);
+    if (edge) gemm16_tile<KIND, true, false, false>(g, smem, ks, tile_a, tb);
+    else gemm16_tile<KIND, false, false, false>(g, smem, ks, tile_a, tb);
   }
 }
 
@@ -1057,7 +1108,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 template <typename T>
 __global__ __launch_bounds__(256) void target_logit_kernel(const T* __restrict__ H, const T* __restrict__ W,
                                                            const int32_t* __restrict__ targets, int ntok,
-                                                           int D, int V, float inv_tau, float* __restrict__ zy) {
+                                                           int D, int V, LogitMap lm, float* __restrict__ zy) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= ntok) return;
@@ -1085,7 +1136,7 @@ __global__ __launch_bounds__(256) void target_logit_kernel(const T* __restrict__
     }
   }
   s = wave_sum(s);
-  if (lane == 0) zy[t] = s * inv_tau;
+  if (lane == 0) zy[t] = lm.zscale * (lm.cap_in > 0.0f ? tanh_fast(lm.cap_in * s) : s);
 }
 
 struct MergeArgs {
@@ -1264,7 +1315,8 @@ __global__ __launch_bounds__(1024) void loss_finalize_kernel(const double* __res
 // Fixed-order sum of the split-vocabulary dH partials, then (g / tau) (W[y] - sum).
 template <typename T>
 __global__ __launch_bounds__(256) void dh_reduce_kernel(const float* __restrict__ part, int ksplit, int rows,
-                                                        int D, int V, float inv_tau,
+                                                        int D, int V, LogitMap lm,
+                                                        const float* __restrict__ zy,
                                                         const float* __restrict__ g,
                                                         const int32_t* __restrict__ targets,
                                                         const T* __restrict__ W, T* __restrict__ dh) {
@@ -1284,9 +1336,11 @@ __global__ __launch_bounds__(256) void dh_reduce_kernel(const float* __restrict_
     }
     float wv[4];
     load4(W + (int64_t)y * D + d0, wv);
-    const float scale = gt * inv_tau;
+    const float scale = gt * lm.dscale;
+    const float ty = zy[tok] / lm.zscale;
+    const float wyf = lm.cap_in > 0.0f ? 1.0f - ty * ty : 1.0f;  // dv/dx at the target
 #pragma unroll
-    for (int u = 0; u < 4; ++u) o[u] = scale * (wv[u] - s[u]);
+    for (int u = 0; u < 4; ++u) o[u] = scale * (wyf * wv[u] - s[u]);
   }
   store4(dh + (int64_t)tok * D + d0, o[0], o[1], o[2], o[3]);
 }
@@ -1362,7 +1416,7 @@ inline void enqueue_frag_copy(Launcher& L, const Plan& p, const __bf16* Hc, int 
 
 // Arguments shared by the two logits GEMMs of a chunk (W rows x tokens, K = D).
 template <typename T>
-GemmArgs logits_args(const Plan& p, const T* W, const T* Hc, const char* Hf, int rows, float inv_tau) {
+GemmArgs logits_args(const Plan& p, const T* W, const T* Hc, const char* Hf, int rows, const LogitMap& lm) {
   GemmArgs g = {};
   const bool bf16 = sizeof(T) == 2;
   g.a = W;
@@ -1378,7 +1432,7 @@ GemmArgs logits_args(const Plan& p, const T* W, const T* Hc, const char* Hf, int
   g.tiles_b = (int)cdiv(rows, bf16 ? kTileB16 : kTile);
   g.xcd_axis = 0;
   g.group_b = 8;  // B tiles walked together
-  g.inv_tau = inv_tau;
+  g.lm = lm;
   g.V = (int)p.V;
   g.D = (int)p.D;
   g.ksplit = 1;
@@ -1390,7 +1444,7 @@ GemmArgs logits_args(const Plan& p, const T* W, const T* Hc, const char* Hf, int
 template <typename T>
 grpo_status logp_impl(const Plan& p, const grpo_shape* shape, const T* H, const T* W, const int32_t* targets,
                       float* logp, float* lse_out, char* ws, Launcher& L) {
-  const float inv_tau = 1.0f / shape->temperature;
+  const LogitMap lm = make_logit_map(shape);
   float* zy = reinterpret_cast<float*>(ws + p.off_zy);
   float* lse = lse_out ? lse_out : reinterpret_cast<float*>(ws + p.off_lse);
   float* pm = reinterpret_cast<float*>(ws + p.off_pm);
@@ -1398,13 +1452,13 @@ grpo_status logp_impl(const Plan& p, const grpo_shape* shape, const T* H, const 
   char* Hf = ws + p.off_Hf;
   L.run(GRPO_K_TARGET_LOGIT, [&] {
     hipLaunchKernelGGL((target_logit_kernel<T>), dim3(grid1(p.T, 4)), dim3(256), 0, L.stream, H, W, targets,
-                       (int)p.T, (int)p.D, (int)p.V, inv_tau, zy);
+                       (int)p.T, (int)p.D, (int)p.V, lm, zy);
   });
   for (int64_t k = 0; k < p.nchunks; ++k) {
     const int64_t t0 = k * p.C;
     const int rows = (int)(p.T - t0 < p.C ? p.T - t0 : p.C);
     if constexpr (sizeof(T) == 2) enqueue_frag_copy(L, p, H + t0 * p.D, rows, Hf);
-    GemmArgs g = logits_args<T>(p, W, H + t0 * p.D, Hf, rows, inv_tau);
+    GemmArgs g = logits_args<T>(p, W, H + t0 * p.D, Hf, rows, lm);
     g.pm = pm;
     g.ps = ps;
     launch_gemm<T, KIND_LSE>(L, GRPO_K_LOGITS_LSE, g);
@@ -1431,8 +1485,8 @@ grpo_status logp_impl(const Plan& p, const grpo_shape* shape, const T* H, const 
 template <typename T>
 void backward_chunk(Launcher& L, const Plan& p, const T* W, const T* WT, bool use_wt, const T* Hc, const char* Hf,
                     int rows, int64_t k, const float* lse_c, const float* g_c, const int32_t* targets_c, T* dH_c,
-                    T* P, float* part, float inv_tau) {
-  GemmArgs gp = logits_args<T>(p, W, Hc, Hf, rows, inv_tau);
+                    T* P, float* part, const LogitMap& lm, const float* zy_c) {
+  GemmArgs gp = logits_args<T>(p, W, Hc, Hf, rows, lm);
   gp.lse = lse_c;
   gp.p = P;
   gp.ldp = p.ldp;
@@ -1458,7 +1512,8 @@ void backward_chunk(Launcher& L, const Plan& p, const T* W, const T* WT, bool us
   gd.xcd_axis = 1;
   gd.group_b = bf16 ? 4 : 2;  // 8 W^T tiles x 4 token tiles per XCD round (bf16)
   gd.b_ks = (int)p.ks_v;
-  gd.inv_tau = inv_tau;
+  gd.lm = lm;
+  gd.zy = zy_c;
   gd.g = g_c;
   gd.targets = targets_c;
   gd.w = W;
@@ -1472,7 +1527,7 @@ void backward_chunk(Launcher& L, const Plan& p, const T* W, const T* WT, bool us
   if (ksplit > 1) {
     L.run(GRPO_K_DH_REDUCE, [&] {
       hipLaunchKernelGGL((dh_reduce_kernel<T>), dim3(grid1((int64_t)rows * (p.D / 4), 256)), dim3(256), 0,
-                         L.stream, part, ksplit, rows, (int)p.D, (int)p.V, inv_tau, g_c, targets_c, W, dH_c);
+                         L.stream, part, ksplit, rows, (int)p.D, (int)p.V, lm, zy_c, g_c, targets_c, W, dH_c);
     });
   }
 }
@@ -1499,7 +1554,7 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, int mode, const gr
                       const T* W, const int32_t* targets, const int32_t* cu_host, const uint8_t* mask,
                       const float* old_logp, const float* ref_logp, const float* adv, double* loss,
                       float* logp, float* token_loss, T* dH, char* ws, Launcher& L) {
-  const float inv_tau = 1.0f / shape->temperature;
+  const LogitMap lm = make_logit_map(shape);
   float* zy = reinterpret_cast<float*>(ws + p.off_zy);
   float* lse = reinterpret_cast<float*>(ws + p.off_lse);
   float* pm = reinterpret_cast<float*>(ws + p.off_pm);
@@ -1534,7 +1589,7 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, int mode, const gr
   if (p.T > 0) {
     L.run(GRPO_K_TARGET_LOGIT, [&] {
       hipLaunchKernelGGL((target_logit_kernel<T>), dim3(grid1(p.T, 4)), dim3(256), 0, L.stream, H, W, targets,
-                         (int)p.T, (int)p.D, (int)p.V, inv_tau, zy);
+                         (int)p.T, (int)p.D, (int)p.V, lm, zy);
     });
     WT = maybe_transpose_w<T>(L, p, W, ws, use_wt);
   }
@@ -1543,7 +1598,7 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, int mode, const gr
     const int rows = (int)(p.T - t0 < p.C ? p.T - t0 : p.C);
     const T* Hc = H + t0 * p.D;
     if constexpr (sizeof(T) == 2) enqueue_frag_copy(L, p, Hc, rows, Hf);
-    GemmArgs gl = logits_args<T>(p, W, Hc, Hf, rows, inv_tau);
+    GemmArgs gl = logits_args<T>(p, W, Hc, Hf, rows, lm);
     gl.pm = pm;
     gl.ps = ps;
     launch_gemm<T, KIND_LSE>(L, GRPO_K_LOGITS_LSE, gl);
@@ -1576,7 +1631,7 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, int mode, const gr
       hipLaunchKernelGGL(merge_kernel, dim3(grid1(rows, 16)), dim3(256), 0, L.stream, m);
     });
     backward_chunk<T>(L, p, W, WT, use_wt, Hc, Hf, rows, k, lse + t0, gbuf + t0, targets + t0, dH + t0 * p.D, P,
-                      part, inv_tau);
+                      part, lm, zy + t0);
   }
   L.run(GRPO_K_LOSS_FINALIZE, [&] {
     hipLaunchKernelGGL(loss_finalize_kernel, dim3(1), dim3(1024), 0, L.stream, wl, (int)p.T, loss);
@@ -1588,10 +1643,17 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, int mode, const gr
 template <typename T>
 grpo_status logp_bwd_impl(const Plan& p, const grpo_shape* shape, const T* H, const T* W, const int32_t* targets,
                           const float* lse, const float* grad, T* dH, char* ws, Launcher& L) {
-  const float inv_tau = 1.0f / shape->temperature;
+  const LogitMap lm = make_logit_map(shape);
   T* P = reinterpret_cast<T*>(ws + p.off_P);
   char* Hf = ws + p.off_Hf;
   float* part = reinterpret_cast<float*>(ws + p.off_part);
+  float* zy = reinterpret_cast<float*>(ws + p.off_zy);
+  if (lm.cap_in > 0.0f) {  // the softcap's derivative at the target needs the target logits
+    L.run(GRPO_K_TARGET_LOGIT, [&] {
+      hipLaunchKernelGGL((target_logit_kernel<T>), dim3(grid1(p.T, 4)), dim3(256), 0, L.stream, H, W, targets,
+                         (int)p.T, (int)p.D, (int)p.V, lm, zy);
+    });
+  }
   bool use_wt = false;
   const T* WT = p.T > 0 ? maybe_transpose_w<T>(L, p, W, ws, use_wt) : nullptr;
   for (int64_t k = 0; k < p.nchunks; ++k) {
@@ -1600,7 +1662,7 @@ grpo_status logp_bwd_impl(const Plan& p, const grpo_shape* shape, const T* H, co
     const T* Hc = H + t0 * p.D;
     if constexpr (sizeof(T) == 2) enqueue_frag_copy(L, p, Hc, rows, Hf);
     backward_chunk<T>(L, p, W, WT, use_wt, Hc, Hf, rows, k, lse + t0, grad + t0, targets + t0, dH + t0 * p.D, P,
-                      part, inv_tau);
+                      part, lm, zy + t0);
   }
   return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_E_HIP;
 }

@@ -47,6 +47,15 @@ struct Plan {
   size_t total = 0;
 };
 
+// Logits from the raw lm_head products x = H[t] . W[v]: z = zscale * v with v = x, or with a
+// softcap v = tanh(cap_in * x); dz/dx = dscale, or dscale * (1 - v^2) with the softcap.
+struct LogitMap {
+  float zscale;
+  float dscale;
+  float cap_in;  // 0: no softcap
+};
+LogitMap make_logit_map(const grpo_shape* s);  // s already validated
+
 grpo_status validate_shape(const grpo_shape* s);
 grpo_status validate_loss_params(const grpo_loss_params* p);
 grpo_status validate_cu(const int32_t* cu, int64_t S, int64_t T);

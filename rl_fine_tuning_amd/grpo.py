@@ -25,7 +25,8 @@ KERNEL_ID = {k: i for i, k in enumerate(KERNELS)}
 class GrpoShape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("D", ctypes.c_int64), ("V", ctypes.c_int64),
                 ("chunk_tokens", ctypes.c_int64), ("dtype", ctypes.c_int32),
-                ("temperature", ctypes.c_float)]
+                ("temperature", ctypes.c_float), ("logit_scale_multiply", ctypes.c_float),
+                ("logit_scale_divide", ctypes.c_float), ("logit_softcapping", ctypes.c_float)]
 
 
 class GrpoLossParams(ctypes.Structure):
@@ -114,13 +115,16 @@ def _dev(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be contiguous")
 
 
-def make_shape(T, D, V, chunk_tokens, dtype, temperature=1.0) -> GrpoShape:
-    return GrpoShape(int(T), int(D), int(V), int(chunk_tokens), int(dtype), float(temperature))
+def make_shape(T, D, V, chunk_tokens, dtype, temperature=1.0, logit_scale_multiply=0.0, logit_scale_divide=0.0,
+               logit_softcapping=0.0) -> GrpoShape:
+    """0 for a logit argument means 'not used' (see grpo_shape in include/grpo.h)."""
+    return GrpoShape(int(T), int(D), int(V), int(chunk_tokens), int(dtype), float(temperature),
+                     float(logit_scale_multiply), float(logit_scale_divide), float(logit_softcapping))
 
 
 def grpo_workspace_bytes(T, D, V, chunk_tokens, dtype=GRPO_BF16, temperature=1.0, num_seqs=1,
-                         with_backward=True) -> int:
-    shape = make_shape(T, D, V, chunk_tokens, dtype, temperature)
+                         with_backward=True, logit_softcapping=0.0) -> int:
+    shape = make_shape(T, D, V, chunk_tokens, dtype, temperature, logit_softcapping=logit_softcapping)
     return int(lib().grpo_workspace_bytes(ctypes.byref(shape), int(num_seqs), int(bool(with_backward))))
 
 
@@ -164,14 +168,16 @@ class Timer:
 
 
 def grpo_logp_fwd(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, chunk_tokens: int,
-                  temperature: float = 1.0, *, return_lse: bool = False, out=None, workspace=None,
+                  temperature: float = 1.0, *, logit_scale_multiply=0.0, logit_scale_divide=0.0,
+                  logit_softcapping=0.0, return_lse: bool = False, out=None, workspace=None,
                   stream=None, timer: Timer | None = None):
     """logp[t] = log softmax(H[t] W^T / temperature)[targets[t]] (fp32), chunked."""
     for t, n in ((H, "H"), (W, "W"), (targets, "targets")):
         _dev(t, n)
     T, D = H.shape
     V = W.shape[0]
-    shape = make_shape(T, D, V, chunk_tokens, _dtype_code(H), temperature)
+    shape = make_shape(T, D, V, chunk_tokens, _dtype_code(H), temperature, logit_scale_multiply,
+                       logit_scale_divide, logit_softcapping)
     nbytes = int(lib().grpo_workspace_bytes(ctypes.byref(shape), 1, 0))
     ws, wsn = _workspace(nbytes, workspace, H.device)
     logp = out if out is not None else torch.empty(T, dtype=torch.float32, device=H.device)
@@ -183,14 +189,16 @@ def grpo_logp_fwd(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, chunk
 
 
 def grpo_logp_bwd(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: torch.Tensor,
-                  grad_logp: torch.Tensor, chunk_tokens: int, temperature: float = 1.0, *, dH=None,
+                  grad_logp: torch.Tensor, chunk_tokens: int, temperature: float = 1.0, *,
+                  logit_scale_multiply=0.0, logit_scale_divide=0.0, logit_softcapping=0.0, dH=None,
                   workspace=None, stream=None, timer: Timer | None = None) -> torch.Tensor:
     """dH of sum_t grad_logp[t] * logp_t, recomputing each chunk's logits from the forward's lse."""
     for t, n in ((H, "H"), (W, "W"), (targets, "targets"), (lse, "lse"), (grad_logp, "grad_logp")):
         _dev(t, n)
     T, D = H.shape
     V = W.shape[0]
-    shape = make_shape(T, D, V, chunk_tokens, _dtype_code(H), temperature)
+    shape = make_shape(T, D, V, chunk_tokens, _dtype_code(H), temperature, logit_scale_multiply,
+                       logit_scale_divide, logit_softcapping)
     nbytes = int(lib().grpo_workspace_bytes(ctypes.byref(shape), 1, 1))
     ws, wsn = _workspace(nbytes, workspace, H.device)
     if dH is None:
@@ -201,7 +209,8 @@ def grpo_logp_bwd(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: 
     return dH
 
 
-def grpo_ce_loss_fwd_bwd(H, W, targets, chunk_tokens, *, temperature=1.0, mask=None, want_logp=True,
+def grpo_ce_loss_fwd_bwd(H, W, targets, chunk_tokens, *, temperature=1.0, logit_scale_multiply=0.0,
+                         logit_scale_divide=0.0, logit_softcapping=0.0, mask=None, want_logp=True,
                          want_token_loss=False, dH=None, workspace=None, stream=None,
                          timer: Timer | None = None):
     """Mean cross-entropy over the unmasked tokens, per-token logp, and dL/dH."""
@@ -211,7 +220,8 @@ def grpo_ce_loss_fwd_bwd(H, W, targets, chunk_tokens, *, temperature=1.0, mask=N
         _dev(mask, "mask")
     T, D = H.shape
     V = W.shape[0]
-    shape = make_shape(T, D, V, chunk_tokens, _dtype_code(H), temperature)
+    shape = make_shape(T, D, V, chunk_tokens, _dtype_code(H), temperature, logit_scale_multiply,
+                       logit_scale_divide, logit_softcapping)
     nbytes = int(lib().grpo_workspace_bytes(ctypes.byref(shape), 1, 1))
     ws, wsn = _workspace(nbytes, workspace, H.device)
     dev = H.device
@@ -238,7 +248,8 @@ def grpo_advantages(rewards: torch.Tensor, group_size: int, std_mode: str = "unb
 
 
 def grpo_loss_fwd_bwd(H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk_tokens, *,
-                      temperature=1.0, clip_eps_low=0.2, clip_eps_high=0.2, beta=0.001, agg="seq_mean",
+                      temperature=1.0, logit_scale_multiply=0.0, logit_scale_divide=0.0, logit_softcapping=0.0,
+                      clip_eps_low=0.2, clip_eps_high=0.2, beta=0.001, agg="seq_mean",
                       mask=None, want_logp=True, want_token_loss=True, dH=None, workspace=None, stream=None,
                       timer: Timer | None = None):
     """GRPO loss, per-token logp and objective, and dL/dH.  cu_seqlens is a host int32 array/tensor."""
@@ -252,7 +263,8 @@ def grpo_loss_fwd_bwd(H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk_
     S = cu.numel() - 1
     T, D = H.shape
     V = W.shape[0]
-    shape = make_shape(T, D, V, chunk_tokens, _dtype_code(H), temperature)
+    shape = make_shape(T, D, V, chunk_tokens, _dtype_code(H), temperature, logit_scale_multiply,
+                       logit_scale_divide, logit_softcapping)
     params = GrpoLossParams(float(clip_eps_low), float(clip_eps_high), float(beta), GRPO_AGG[agg])
     nbytes = int(lib().grpo_workspace_bytes(ctypes.byref(shape), S, 1))
     ws, wsn = _workspace(nbytes, workspace, H.device)

@@ -43,7 +43,7 @@ def f32(x):
 
 def case(seed, *, D, V, lengths, G=2, dtype="bf16", chunk=256, rewards=("uniform",), w_std=0.02,
          old_std=None, ref_std=None, mask_frac=0.0, tau=1.0, beta=0.001, eps_lo=0.2, eps_hi=0.2,
-         agg="seq_mean", bad_targets=()):
+         agg="seq_mean", bad_targets=(), scale=1.0, softcap=0.0):
     """A seeded case with every input fixed on the host, plus the oracle's full result."""
     c = make_case(seed, D=D, V=V, G=G, lengths=lengths, dtype=dtype, rewards=rewards, chunk=chunk, w_std=w_std)
     T = c.T
@@ -56,7 +56,7 @@ def case(seed, *, D, V, lengths, G=2, dtype="bf16", chunk=256, rewards=("uniform
     if mask_frac > 0:
         rng = np.random.default_rng(seed + 77)
         mask[rng.random(T) < mask_frac] = 0
-    logp0, _ = oracle.selective_log_softmax(H64, W64, targets, tau)
+    logp0, _ = oracle.selective_log_softmax(H64, W64, targets, tau, scale=scale, softcap=softcap)
     base = np.where(np.isfinite(logp0), logp0, -np.log(V))
     n_old = c.noise_old if old_std is None else c.noise_old * (old_std / 0.01)
     n_ref = c.noise_ref if ref_std is None else c.noise_ref * (ref_std / 0.05)
@@ -65,7 +65,8 @@ def case(seed, *, D, V, lengths, G=2, dtype="bf16", chunk=256, rewards=("uniform
     adv = f32(oracle.group_advantages(c.rewards, G))
     prm = dict(clip_eps_low=eps_lo, clip_eps_high=eps_hi, beta=beta, agg=agg)
     out = oracle.grpo_loss_and_grad(H64, W64, targets, c.cu, mask, old.astype(np.float64),
-                                    ref.astype(np.float64), adv.astype(np.float64), tau, **prm)
+                                    ref.astype(np.float64), adv.astype(np.float64), tau, scale=scale,
+                                    softcap=softcap, **prm)
     w = oracle.token_weights(c.cu, mask, agg)
     return dict(c=c, T=T, D=D, V=V, dtype=dtype, tau=tau, targets=targets, mask=mask, old=old, ref=ref,
                 adv=adv, prm=prm, oracle=out, w=w, H64=H64, W64=W64)

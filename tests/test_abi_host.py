@@ -178,3 +178,25 @@ def test_ce_loss_validation():
     assert f(shape(dtype=3)) == 5
     assert f(n=16) == 4
     assert f(wsp=None) == 4
+
+
+def test_logit_arguments_validation():
+    lib = B.lib()
+    ws = ctypes.c_void_p(1 << 20)
+
+    def f(**kw):
+        sh = B.make_shape(100, 64, 512, 32, 0, kw.pop("tau", 1.0), **kw)
+        return lib.grpo_logp_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, None, ws, 1 << 40, None, None)
+
+    assert f(logit_scale_multiply=-1.0) == 3
+    assert f(logit_scale_divide=float("nan")) == 3
+    assert f(logit_softcapping=float("inf")) == 3
+    assert f(logit_softcapping=-30.0) == 3
+    assert f(logit_scale_multiply=1e30, logit_scale_divide=1e-30) == 3  # scale overflows
+    assert f(logit_scale_multiply=1e-30, logit_scale_divide=1e30) == 3  # scale underflows to 0
+    sh = B.make_shape(100, 64, 512, 32, 0, 0.7, 2.0, 0.0, 30.0)  # valid: only the small workspace fails
+    assert lib.grpo_logp_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, None, ws, 16, None, None) == 4
+    # zeros mean "not used": a zero tail is a valid plain shape (validation passes; the
+    # oversized workspace claim is what fails, with status 4)
+    sh = B.make_shape(100, 64, 512, 32, 0, 1.0)
+    assert lib.grpo_logp_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, None, ws, 16, None, None) == 4
