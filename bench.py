@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--chunk", type=int, default=0, help="override the workload's chunk tokens")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variant", action="store_true",
+                    help="skip timing the variant that keeps the chunk's logits (no recompute GEMM)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for HBM counter scaling)")
     return ap.parse_args()
@@ -159,10 +161,10 @@ def main():
     adv = torch.empty(S, dtype=torch.float32, device=dev)
     cu = case.cu
 
-    def step(timer=None):
+    def step(timer=None, keep=False):
         grpo_advantages(rewards, G, out=adv)
         return grpo_loss_fwd_bwd(H, W, targets, cu, old, ref, adv, C, dH=dH, workspace=ws, timer=timer,
-                                 want_logp=False, want_token_loss=False)
+                                 want_logp=False, want_token_loss=False, keep_chunk_logits=keep)
 
     torch.cuda.synchronize()
     base_mem = torch.cuda.memory_allocated()
@@ -229,6 +231,24 @@ def main():
         "loss": loss,
     }
     timer.close()
+    if not args.no_variant and case.dtype == "bf16":
+        # The same step with keep_chunk_logits: the forward GEMM keeps the chunk's logits, so
+        # the backward has no recompute GEMM (4 D V flop per token instead of 6 D V).
+        for _ in range(args.warmup):
+            step(keep=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(keep=True)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        ms_v = 1e3 * el / args.steps
+        result["variant_keep_chunk_logits"] = {
+            "value": T * args.steps / el, "unit": "tokens/s", "ms_per_step": ms_v,
+            "mfma_frac_step_4DV": 4.0 * T * D * V / (ms_v * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+            "note": "same outputs (logp/loss bitwise, dH within the fp16 rounding of the kept logits); "
+                    "not the headline: the pages' backward recomputes the chunk's logits"}
+        log(f"keep_chunk_logits variant: {result['variant_keep_chunk_logits']['value']:.0f} tokens/s")
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host")
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_sample_tokens)

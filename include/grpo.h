@@ -76,7 +76,15 @@ typedef enum { GRPO_STD_UNBIASED = 0, GRPO_STD_POPULATION = 1 } grpo_std;
  *   z = s x / temperature                                (logit_softcapping == 0)
  *   z = c tanh(s x / c) / temperature,  c = logit_softcapping  (> 0).
  * temperature > 0 and finite; the three logit arguments are finite and >= 0, and 0 means
- * "not used" (a factor of 1, no cap), so a zero-initialized tail gives plain logits. */
+ * "not used" (a factor of 1, no cap), so a zero-initialized tail gives plain logits.
+ * keep_chunk_logits (0 or 1; bf16 only) selects how the loss calls (grpo_loss_fwd_bwd,
+ * grpo_ce_loss_fwd_bwd) form the probabilities of their backward: 0, the pages' method
+ * ([P4] "Auslagern von Aktivierungen fuer Log-Softmax"), recomputes the chunk's logits with
+ * a second GEMM; 1 keeps them from the forward GEMM, as d = z - (max over a 256-entry
+ * vocabulary tile) in fp16, in the buffer the probabilities occupy anyway (no extra
+ * memory), and turns them into probabilities in place: 4 D V instead of 6 D V flop per
+ * token.  logp, token_loss and the loss are bitwise the same either way; dH differs by the
+ * fp16 rounding of d (relative error at most 2^-11 |d| per probability). */
 typedef struct {
   int64_t T;
   int64_t D;
@@ -87,6 +95,7 @@ typedef struct {
   float logit_scale_multiply;
   float logit_scale_divide;
   float logit_softcapping;
+  int32_t keep_chunk_logits;
 } grpo_shape;
 
 /* GRPO objective parameters ([P2], [P3], [P1]).  The ratio is clipped to
@@ -112,7 +121,8 @@ typedef enum {
   GRPO_K_ADVANTAGES = 8,
   GRPO_K_FRAG_COPY = 9,    /* fragment-major copy of a chunk's hidden states (bf16 path) */
   GRPO_K_TRANSPOSE_W = 10, /* transposed copy of W for the dH GEMM (bf16, when it fits) */
-  GRPO_K_COUNT = 11
+  GRPO_K_PROBS_KEPT = 11,  /* probabilities from the kept logits, in place (keep_chunk_logits) */
+  GRPO_K_COUNT = 12
 } grpo_kernel_id;
 
 typedef struct grpo_timer grpo_timer; /* opaque, owned by the caller */

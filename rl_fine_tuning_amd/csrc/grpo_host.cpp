@@ -27,6 +27,8 @@ grpo_status validate_shape(const grpo_shape* s) {
   if (!isfinite(s->temperature) || !(s->temperature > 0.0f)) return GRPO_E_VALUE;
   for (float a : {s->logit_scale_multiply, s->logit_scale_divide, s->logit_softcapping})
     if (!isfinite(a) || a < 0.0f) return GRPO_E_VALUE;
+  if (s->keep_chunk_logits != 0 && s->keep_chunk_logits != 1) return GRPO_E_VALUE;
+  if (s->keep_chunk_logits && s->dtype != GRPO_BF16) return GRPO_E_UNSUPPORTED;
   const LogitMap m = make_logit_map(s);
   for (float a : {m.zscale, m.dscale, m.cap_in})
     if (!isfinite(a)) return GRPO_E_VALUE;

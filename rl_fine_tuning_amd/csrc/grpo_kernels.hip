@@ -60,7 +60,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // KIND_DH reads W for the dH GEMM transposed on the fly; KIND_DHT (bf16) reads a
 // transposed copy W^T [D, ldt] with the direct-to-LDS loads of the logits GEMMs.
-enum Kind { KIND_LSE = 0, KIND_PROBS = 1, KIND_DH = 2, KIND_DHT = 3 };
+// KIND_LSES (bf16): the LSE epilogue that also keeps the chunk's logits, as d = z - (tile
+// max) in fp16, in the probabilities buffer (the variant without the recompute GEMM).
+enum Kind { KIND_LSE = 0, KIND_PROBS = 1, KIND_DH = 2, KIND_DHT = 3, KIND_LSES = 4 };
 
 // Byte offset of 16-byte chunk c of row r inside a [256 rows x 8 chunks] LDS tile.
 __device__ __forceinline__ int lds_off(int r, int c) {
@@ -74,6 +76,14 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   __bf16 x = (__bf16)a, y = (__bf16)b;  // round to nearest even
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
+
+// Two floats as fp16 (round to nearest even), low half first.
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+__device__ __forceinline__ float f16_lo(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xffffu)); }
+__device__ __forceinline__ float f16_hi(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16)); }
 
 __device__ __forceinline__ uint32_t u4get(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
@@ -890,7 +900,8 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
   // max ignores them); column bounds of 8-aligned groups are wave-uniform scalar tests
   // (every limit is a multiple of 8 and the tile origin of 256); only stores depend on
   // the lane's token.  With a softcap the accumulators first become v = tanh(cap_in x).
-  if constexpr ((KIND == KIND_LSE || KIND == KIND_PROBS) && kCap) {
+  constexpr bool kLogits = KIND == KIND_LSE || KIND == KIND_PROBS || KIND == KIND_LSES;
+  if constexpr (kLogits && kCap) {
 #pragma unroll
     for (int i = 0; i < kFA; ++i) {
 #pragma unroll
@@ -900,7 +911,7 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  if constexpr ((KIND == KIND_LSE || KIND == KIND_PROBS) && kEdge) {
+  if constexpr (kLogits && kEdge) {
     {
 #pragma unroll
       for (int i = 0; i < kFA; ++i) {
@@ -914,8 +925,10 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
       }
     }
   }
-  if constexpr (KIND == KIND_LSE) {
-    // Per token: max and sum of exp over this tile's 256 vocabulary rows (those < V).
+  if constexpr (KIND == KIND_LSE || KIND == KIND_LSES) {
+    // Per token: max and sum of exp over this tile's 256 vocabulary rows (those < V);
+    // KIND_LSES also keeps d = z - max (fp16, rounded to nearest) in the fragment-major
+    // layout of the probabilities, -inf past V.
 #pragma unroll
     for (int j = 0; j < kFBW; ++j) {
       float mx = -INFINITY;
@@ -925,6 +938,25 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float zmax = mx * g.lm.zscale;  // zscale > 0, so this is the max of z
+      if constexpr (KIND == KIND_LSES) {
+        char* P = reinterpret_cast<char*>(g.p);
+        const int vrem = g.p_ks * 16 - row_a0;  // uniform; multiple of 16
+        const int tok = row_b0 + 64 * w + 32 * j + col;
+#pragma unroll
+        for (int i = 0; i < kFA; ++i) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (kEdge && 32 * i + 8 * q >= vrem) continue;
+            const int v0 = row_a0 + 32 * i + 8 * q + 4 * hi;
+            float d[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) d[u] = fmaf(acc[i][j][4 * q + u], g.lm.zscale, -zmax);
+            *reinterpret_cast<uint2*>(P + frag_off(tok, v0, g.p_ks)) =
+                make_uint2(pack_f16(d[0], d[1]), pack_f16(d[2], d[3]));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
       float sum = 0.0f;
       if (mx > -INFINITY) {
         const float c1 = g.lm.zscale * kLog2e, c0 = -zmax * kLog2e;
@@ -1094,6 +1126,49 @@ __global__ __launch_bounds__(256) void transpose_w_kernel(const __bf16* __restri
     }
     *reinterpret_cast<uint4*>(WT + (int64_t)(d0 + j) * ldt + v0) = make_uint4(o[0], o[1], o[2], o[3]);
   }
+}
+
+// The kept logits of a chunk (d = z - m_tile, fp16, fragment-major) turned into the
+// probabilities in place: p = exp(d + m_tile - lse) (times 1 - v^2, v = z / zscale, with a
+// softcap), bf16 rounded to nearest even; rows past the chunk's tokens become 0.  One
+// thread per 16-byte unit (8 consecutive vocabulary entries of one token, one tile).
+__global__ __launch_bounds__(256) void probs_from_kept_kernel(uint4* __restrict__ P, int64_t units, int rows,
+                                                              int ks_count, const float* __restrict__ pm,
+                                                              int ntiles, const float* __restrict__ lse_c,
+                                                              LogitMap lm) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= units) return;
+  const int l = (int)(u & 63);
+  const int64_t fr = u >> 6;
+  const int fb = (int)(fr % kFB);
+  const int64_t rest = fr / kFB;
+  const int kstep = (int)(rest % ks_count);
+  const int tb = (int)(rest / ks_count);
+  const int tok = tb * kTB + fb * 32 + (l & 31);
+  const int v0 = kstep * 16 + 8 * (l >> 5);
+  uint4 out = make_uint4(0u, 0u, 0u, 0u);
+  if (tok < rows) {
+    const uint4 in = P[u];
+    const float m = pm[(int64_t)tok * ntiles + v0 / kTA];
+    const float c = m - lse_c[tok];
+    float e[8];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const uint32_t w = u4get(in, h);
+      const float d[2] = {f16_lo(w), f16_hi(w)};
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        float x = __builtin_amdgcn_exp2f((d[k] + c) * kLog2e);
+        if (lm.cap_in > 0.0f) {
+          const float v = (d[k] + m) / lm.zscale;
+          x = x != 0.0f ? x * (1.0f - v * v) : 0.0f;
+        }
+        e[2 * h + k] = x;
+      }
+    }
+    out = make_uint4(pack_bf16(e[0], e[1]), pack_bf16(e[2], e[3]), pack_bf16(e[4], e[5]), pack_bf16(e[6], e[7]));
+  }
+  P[u] = out;
 }
 
 // ---------------------------------------------------------------------------- small kernels
@@ -1478,19 +1553,21 @@ grpo_status logp_impl(const Plan& p, const grpo_shape* shape, const T* H, const 
   return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_E_HIP;
 }
 
-// Backward of one chunk: recompute its logits into softmax probabilities (PROBS GEMM, with
-// the log-sum-exp of the forward), then dH = (g / tau) (W[y] - P W) (dH GEMM, split over
-// the vocabulary when the chunk is too small to fill the GPU).  Hf holds the chunk's
-// fragment-major hidden states (bf16).
+// Backward of one chunk: the softmax probabilities (recomputed by the PROBS GEMM from the
+// forward's log-sum-exp, unless P already holds them), then dH = g (z'_y W[y] - P' W)
+// (dH GEMM, split over the vocabulary when the chunk is too small to fill the GPU).  Hf
+// holds the chunk's fragment-major hidden states (bf16).
 template <typename T>
 void backward_chunk(Launcher& L, const Plan& p, const T* W, const T* WT, bool use_wt, const T* Hc, const char* Hf,
                     int rows, int64_t k, const float* lse_c, const float* g_c, const int32_t* targets_c, T* dH_c,
-                    T* P, float* part, const LogitMap& lm, const float* zy_c) {
-  GemmArgs gp = logits_args<T>(p, W, Hc, Hf, rows, lm);
-  gp.lse = lse_c;
-  gp.p = P;
-  gp.ldp = p.ldp;
-  launch_gemm<T, KIND_PROBS>(L, GRPO_K_PROBS, gp);
+                    T* P, float* part, const LogitMap& lm, const float* zy_c, bool probs_ready = false) {
+  if (!probs_ready) {
+    GemmArgs gp = logits_args<T>(p, W, Hc, Hf, rows, lm);
+    gp.lse = lse_c;
+    gp.p = P;
+    gp.ldp = p.ldp;
+    launch_gemm<T, KIND_PROBS>(L, GRPO_K_PROBS, gp);
+  }
 
   // dH^T tiles: hidden x tokens, K = vocabulary, split over the vocabulary if needed.
   const int ks_plan = (k == p.nchunks - 1) ? p.ksplit_tail : p.ksplit_full;
@@ -1598,10 +1675,20 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, int mode, const gr
     const int rows = (int)(p.T - t0 < p.C ? p.T - t0 : p.C);
     const T* Hc = H + t0 * p.D;
     if constexpr (sizeof(T) == 2) enqueue_frag_copy(L, p, Hc, rows, Hf);
+    const bool keep = sizeof(T) == 2 && shape->keep_chunk_logits;
     GemmArgs gl = logits_args<T>(p, W, Hc, Hf, rows, lm);
     gl.pm = pm;
     gl.ps = ps;
-    launch_gemm<T, KIND_LSE>(L, GRPO_K_LOGITS_LSE, gl);
+    if constexpr (sizeof(T) == 2) {
+      if (keep) {
+        gl.p = P;
+        launch_gemm<T, KIND_LSES>(L, GRPO_K_LOGITS_LSE, gl);
+      } else {
+        launch_gemm<T, KIND_LSE>(L, GRPO_K_LOGITS_LSE, gl);
+      }
+    } else {
+      launch_gemm<T, KIND_LSE>(L, GRPO_K_LOGITS_LSE, gl);
+    }
 
     MergeArgs m = {};
     m.pm = pm;
@@ -1630,8 +1717,15 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, int mode, const gr
     L.run(GRPO_K_MERGE, [&] {
       hipLaunchKernelGGL(merge_kernel, dim3(grid1(rows, 16)), dim3(256), 0, L.stream, m);
     });
+    if (keep) {
+      const int64_t units = p.rows_pad * p.ks_v * 2;
+      L.run(GRPO_K_PROBS_KEPT, [&] {
+        hipLaunchKernelGGL(probs_from_kept_kernel, dim3(grid1(units, 256)), dim3(256), 0, L.stream,
+                           reinterpret_cast<uint4*>(P), units, rows, (int)p.ks_v, pm, (int)p.ntiles_v, lse + t0, lm);
+      });
+    }
     backward_chunk<T>(L, p, W, WT, use_wt, Hc, Hf, rows, k, lse + t0, gbuf + t0, targets + t0, dH + t0 * p.D, P,
-                      part, lm, zy + t0);
+                      part, lm, zy + t0, keep);
   }
   L.run(GRPO_K_LOSS_FINALIZE, [&] {
     hipLaunchKernelGGL(loss_finalize_kernel, dim3(1), dim3(1024), 0, L.stream, wl, (int)p.T, loss);

@@ -18,7 +18,7 @@ GRPO_BF16, GRPO_F32 = 0, 1
 GRPO_AGG = {"seq_mean": 0, "token_mean": 1}
 GRPO_STD = {"unbiased": 0, "population": 1}
 KERNELS = ["target_logit", "logits_lse", "merge", "probs", "dh_gemm", "dh_reduce", "token_index",
-           "loss_finalize", "advantages", "frag_copy", "transpose_w"]
+           "loss_finalize", "advantages", "frag_copy", "transpose_w", "probs_kept"]
 KERNEL_ID = {k: i for i, k in enumerate(KERNELS)}
 
 
@@ -26,7 +26,8 @@ class GrpoShape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("D", ctypes.c_int64), ("V", ctypes.c_int64),
                 ("chunk_tokens", ctypes.c_int64), ("dtype", ctypes.c_int32),
                 ("temperature", ctypes.c_float), ("logit_scale_multiply", ctypes.c_float),
-                ("logit_scale_divide", ctypes.c_float), ("logit_softcapping", ctypes.c_float)]
+                ("logit_scale_divide", ctypes.c_float), ("logit_softcapping", ctypes.c_float),
+                ("keep_chunk_logits", ctypes.c_int32)]
 
 
 class GrpoLossParams(ctypes.Structure):
@@ -116,15 +117,17 @@ def _dev(t: torch.Tensor, name: str):
 
 
 def make_shape(T, D, V, chunk_tokens, dtype, temperature=1.0, logit_scale_multiply=0.0, logit_scale_divide=0.0,
-               logit_softcapping=0.0) -> GrpoShape:
+               logit_softcapping=0.0, keep_chunk_logits=False) -> GrpoShape:
     """0 for a logit argument means 'not used' (see grpo_shape in include/grpo.h)."""
     return GrpoShape(int(T), int(D), int(V), int(chunk_tokens), int(dtype), float(temperature),
-                     float(logit_scale_multiply), float(logit_scale_divide), float(logit_softcapping))
+                     float(logit_scale_multiply), float(logit_scale_divide), float(logit_softcapping),
+                     int(bool(keep_chunk_logits)))
 
 
 def grpo_workspace_bytes(T, D, V, chunk_tokens, dtype=GRPO_BF16, temperature=1.0, num_seqs=1,
-                         with_backward=True, logit_softcapping=0.0) -> int:
-    shape = make_shape(T, D, V, chunk_tokens, dtype, temperature, logit_softcapping=logit_softcapping)
+                         with_backward=True, logit_softcapping=0.0, keep_chunk_logits=False) -> int:
+    shape = make_shape(T, D, V, chunk_tokens, dtype, temperature, logit_softcapping=logit_softcapping,
+                       keep_chunk_logits=keep_chunk_logits)
     return int(lib().grpo_workspace_bytes(ctypes.byref(shape), int(num_seqs), int(bool(with_backward))))
 
 
@@ -210,8 +213,8 @@ def grpo_logp_bwd(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: 
 
 
 def grpo_ce_loss_fwd_bwd(H, W, targets, chunk_tokens, *, temperature=1.0, logit_scale_multiply=0.0,
-                         logit_scale_divide=0.0, logit_softcapping=0.0, mask=None, want_logp=True,
-                         want_token_loss=False, dH=None, workspace=None, stream=None,
+                         logit_scale_divide=0.0, logit_softcapping=0.0, keep_chunk_logits=False, mask=None,
+                         want_logp=True, want_token_loss=False, dH=None, workspace=None, stream=None,
                          timer: Timer | None = None):
     """Mean cross-entropy over the unmasked tokens, per-token logp, and dL/dH."""
     for t, n in ((H, "H"), (W, "W"), (targets, "targets")):
@@ -221,7 +224,7 @@ def grpo_ce_loss_fwd_bwd(H, W, targets, chunk_tokens, *, temperature=1.0, logit_
     T, D = H.shape
     V = W.shape[0]
     shape = make_shape(T, D, V, chunk_tokens, _dtype_code(H), temperature, logit_scale_multiply,
-                       logit_scale_divide, logit_softcapping)
+                       logit_scale_divide, logit_softcapping, keep_chunk_logits)
     nbytes = int(lib().grpo_workspace_bytes(ctypes.byref(shape), 1, 1))
     ws, wsn = _workspace(nbytes, workspace, H.device)
     dev = H.device
@@ -249,7 +252,7 @@ def grpo_advantages(rewards: torch.Tensor, group_size: int, std_mode: str = "unb
 
 def grpo_loss_fwd_bwd(H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk_tokens, *,
                       temperature=1.0, logit_scale_multiply=0.0, logit_scale_divide=0.0, logit_softcapping=0.0,
-                      clip_eps_low=0.2, clip_eps_high=0.2, beta=0.001, agg="seq_mean",
+                      keep_chunk_logits=False, clip_eps_low=0.2, clip_eps_high=0.2, beta=0.001, agg="seq_mean",
                       mask=None, want_logp=True, want_token_loss=True, dH=None, workspace=None, stream=None,
                       timer: Timer | None = None):
     """GRPO loss, per-token logp and objective, and dL/dH.  cu_seqlens is a host int32 array/tensor."""
@@ -264,7 +267,7 @@ def grpo_loss_fwd_bwd(H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk_
     T, D = H.shape
     V = W.shape[0]
     shape = make_shape(T, D, V, chunk_tokens, _dtype_code(H), temperature, logit_scale_multiply,
-                       logit_scale_divide, logit_softcapping)
+                       logit_scale_divide, logit_softcapping, keep_chunk_logits)
     params = GrpoLossParams(float(clip_eps_low), float(clip_eps_high), float(beta), GRPO_AGG[agg])
     nbytes = int(lib().grpo_workspace_bytes(ctypes.byref(shape), S, 1))
     ws, wsn = _workspace(nbytes, workspace, H.device)

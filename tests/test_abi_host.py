@@ -200,3 +200,15 @@ def test_logit_arguments_validation():
     # oversized workspace claim is what fails, with status 4)
     sh = B.make_shape(100, 64, 512, 32, 0, 1.0)
     assert lib.grpo_logp_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, None, ws, 16, None, None) == 4
+
+
+def test_keep_chunk_logits_validation():
+    lib = B.lib()
+    ws = ctypes.c_void_p(1 << 20)
+    sh = B.make_shape(100, 64, 512, 32, 0, 1.0)
+    sh.keep_chunk_logits = 2
+    assert lib.grpo_logp_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, None, ws, 1 << 40, None, None) == 3
+    sh = B.make_shape(100, 64, 512, 32, 1, 1.0, keep_chunk_logits=True)  # fp32 inputs: not supported
+    assert lib.grpo_logp_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, None, ws, 1 << 40, None, None) == 5
+    assert B.grpo_workspace_bytes(110000, 4096, 151936, 8192, 0, num_seqs=2, keep_chunk_logits=True) == \
+        B.grpo_workspace_bytes(110000, 4096, 151936, 8192, 0, num_seqs=2)  # no extra memory

@@ -34,11 +34,11 @@ def sample_rows(c, rng):
     return np.array(sorted(rows))
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
-def test_full_size_sampled(cfg):
+@pytest.mark.parametrize("cfg,keep", [(1, False), (2, False), (3, False), (4, False), (3, True)])
+def test_full_size_sampled(cfg, keep):
     c = make_config(cfg)
     T, D, V, C = c.T, c.D, c.V, c.chunk
-    say(f"full size config {cfg}: T={T} D={D} V={V} chunk={C}")
+    say(f"full size config {cfg}: T={T} D={D} V={V} chunk={C} keep_chunk_logits={keep}")
     rng = np.random.default_rng(cfg)
     rows = sample_rows(c, rng)
     W64 = oracle.widen(c.W, "bf16")
@@ -52,11 +52,11 @@ def test_full_size_sampled(cfg):
 
     H = dev_matrix(c.H, "bf16")
     W = dev_matrix(c.W, "bf16")
-    ws_bytes = grpo_workspace_bytes(T, D, V, C, 0, num_seqs=c.S)
+    ws_bytes = grpo_workspace_bytes(T, D, V, C, 0, num_seqs=c.S, keep_chunk_logits=keep)
     assert ws_bytes <= C * V * 4  # extra memory stays below one chunk's fp32 logits
     before = torch.cuda.memory_allocated()
     got = grpo_loss_fwd_bwd(H, W, torch.from_numpy(c.targets).cuda(), c.cu, torch.from_numpy(old).cuda(),
-                            torch.from_numpy(ref).cuda(), torch.from_numpy(adv).cuda(), C)
+                            torch.from_numpy(ref).cuda(), torch.from_numpy(adv).cuda(), C, keep_chunk_logits=keep)
     torch.cuda.synchronize()
     say(f"  gpu done; extra allocated {(torch.cuda.memory_allocated() - before) / 2**30:.2f} GiB")
 
