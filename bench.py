@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variant", action="store_true",
                     help="skip timing the variant that keeps the chunk's logits (no recompute GEMM)")
+    ap.add_argument("--no-entry-points", action="store_true",
+                    help="skip timing grpo_logp_fwd / grpo_logp_bwd / grpo_ce_loss_fwd_bwd / grpo_advantages")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for HBM counter scaling)")
     return ap.parse_args()
@@ -131,7 +133,8 @@ def main():
     import numpy as np
     import torch
 
-    from rl_fine_tuning_amd import Timer, grpo_advantages, grpo_logp_fwd, grpo_loss_fwd_bwd, grpo_workspace_bytes
+    from rl_fine_tuning_amd import (Timer, grpo_advantages, grpo_ce_loss_fwd_bwd, grpo_logp_bwd, grpo_logp_fwd,
+                                    grpo_loss_fwd_bwd, grpo_workspace_bytes)
     from synth import CONFIGS, make_config
 
     cfg = args.config
@@ -249,6 +252,35 @@ def main():
             "note": "same outputs (logp/loss bitwise, dH within the fp16 rounding of the kept logits); "
                     "not the headline: the pages' backward recomputes the chunk's logits"}
         log(f"keep_chunk_logits variant: {result['variant_keep_chunk_logits']['value']:.0f} tokens/s")
+    if not args.no_entry_points:
+        # The other entry points on the same resident inputs, each timed like the step
+        # (warm-up calls, then `steps` calls between two synchronizations).
+        def timed(fn):
+            for _ in range(args.warmup):
+                fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                fn()
+            torch.cuda.synchronize()
+            return 1e3 * (time.perf_counter() - t0) / args.steps
+        lp_out = torch.empty(T, dtype=torch.float32, device=dev)
+        lse = torch.empty(T, dtype=torch.float32, device=dev)
+        ws_f = torch.empty(grpo_workspace_bytes(T, D, V, C, 0 if case.dtype == "bf16" else 1, with_backward=False),
+                           dtype=torch.uint8, device=dev)
+        ms_f = timed(lambda: grpo_logp_fwd(H, W, targets, C, out=lp_out, workspace=ws_f))
+        _, lse = grpo_logp_fwd(H, W, targets, C, return_lse=True)
+        grad = (old - ref) * 1e-3
+        ms_b = timed(lambda: grpo_logp_bwd(H, W, targets, lse, grad, C, dH=dH, workspace=ws))
+        ms_ce = timed(lambda: grpo_ce_loss_fwd_bwd(H, W, targets, C, dH=dH, workspace=ws, want_logp=False))
+        ms_adv = timed(lambda: grpo_advantages(rewards, G, out=adv))
+        per = lambda ms, k: {"tokens_per_s": T / (ms * 1e-3), "ms": ms,
+                             "mfma_frac": k * T * D * V / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)}
+        result["entry_points"] = {"grpo_logp_fwd": per(ms_f, 2.0), "grpo_logp_bwd": per(ms_b, 4.0),
+                                  "grpo_ce_loss_fwd_bwd": per(ms_ce, 6.0),
+                                  "grpo_advantages": {"us": 1e3 * ms_adv, "sequences": S}}
+        log(f"entry points: logp_fwd {ms_f:.1f} ms, logp_bwd {ms_b:.1f} ms, ce {ms_ce:.1f} ms, "
+            f"advantages {1e3 * ms_adv:.1f} us")
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host")
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_sample_tokens)

@@ -122,7 +122,8 @@ typedef enum {
   GRPO_K_FRAG_COPY = 9,    /* fragment-major copy of a chunk's hidden states (bf16 path) */
   GRPO_K_TRANSPOSE_W = 10, /* transposed copy of W for the dH GEMM (bf16, when it fits) */
   GRPO_K_PROBS_KEPT = 11,  /* probabilities from the kept logits, in place (keep_chunk_logits) */
-  GRPO_K_COUNT = 12
+  GRPO_K_ONEHOT_FIX = 12,  /* exact target entries of the backward's P' - onehot matrix */
+  GRPO_K_COUNT = 13
 } grpo_kernel_id;
 
 typedef struct grpo_timer grpo_timer; /* opaque, owned by the caller */

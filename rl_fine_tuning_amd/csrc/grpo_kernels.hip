@@ -151,6 +151,29 @@ struct GemmArgs {
   int p_ks;           // bf16 PROBS: k steps (ceil(V / 16)) of the fragment-major probabilities
 };
 
+// The backward's logit gradient Gx[t, v] = dL/dx[t, v] = -c_t Q[t, v] with
+// Q = P' - onehot(y_t) wyf_t: P' the probabilities (times 1 - v^2 with a softcap), wyf_t
+// the softcap factor at the target (1 - v_y^2, else 1) and c_t = g_t * dscale.  The buffer
+// holds Q (the target entry rewritten exactly in fp32 by onehot_fix_kernel); -c_t is
+// applied per token by the dH epilogue (and to the tokens' operand of dW).  A token with
+// g_t = 0 or a target outside [0, V) gets c_t = 0.
+struct TokGrad {
+  float c, wyf;
+  int y;
+  bool live;
+};
+__device__ __forceinline__ TokGrad tok_grad(const float* g, const int32_t* targets, const float* zy, int V,
+                                            const LogitMap& lm, int tok, bool ok) {
+  TokGrad r;
+  const float gt = ok ? g[tok] : 0.0f;
+  r.y = ok ? targets[tok] : -1;
+  r.live = gt != 0.0f && r.y >= 0 && r.y < V;
+  r.c = r.live ? gt * lm.dscale : 0.0f;
+  const float ty = (r.live && lm.cap_in > 0.0f) ? zy[tok] / lm.zscale : 0.0f;
+  r.wyf = 1.0f - ty * ty;
+  return r;
+}
+
 // Tile of this workgroup.  Workgroup i runs on XCD i % 8; each XCD owns a contiguous
 // share of one tile axis and walks the other axis group_b tiles at a time.
 __device__ __forceinline__ bool map_tile(const GemmArgs& g, int& ta, int& tb) {
@@ -681,8 +704,8 @@ void gemm_kernel(const GemmArgs g) {
       g.ps[(int64_t)tok * g.tiles_a + tile_a] = S;
     }
   } else if constexpr (KIND == KIND_PROBS) {
-    // P[token, v] = exp(z - lse[token]) (times dv/d(cap_in x) = 1 - v^2 with a softcap) for
-    // v < V, written as 4-element vectors.
+    // P'[token, v] = exp(z - lse[token]) (times 1 - v^2 with a softcap) for v < V, written
+    // as 4-element vectors (target entries then rewritten by onehot_fix_kernel).
     T* P = reinterpret_cast<T*>(g.p);
     const float c1 = g.lm.zscale * kLog2e;
     const bool cap = g.lm.cap_in > 0.0f;
@@ -733,13 +756,8 @@ void gemm_kernel(const GemmArgs g) {
           }
         continue;
       }
-      const float gt = g.g[tok];
-      const int y = g.targets[tok];
-      const bool live = gt != 0.0f && y >= 0 && y < g.V;
-      const float scale = gt * g.lm.dscale;
-      const float ty = live ? g.zy[tok] / g.lm.zscale : 0.0f;
-      const float wyf = g.lm.cap_in > 0.0f ? 1.0f - ty * ty : 1.0f;  // dv/dx at the target
-      const T* wrow = reinterpret_cast<const T*>(g.w) + (int64_t)(live ? y : 0) * g.D;
+      const TokGrad tg = tok_grad(g.g, g.targets, g.zy, g.V, g.lm, tok, true);
+      const bool live = tg.live;
       T* dst = reinterpret_cast<T*>(g.dh) + (int64_t)tok * g.D;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -749,10 +767,8 @@ void gemm_kernel(const GemmArgs g) {
           if (d0 >= g.D) continue;
           float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
           if (live) {
-            float wv[4];
-            load4(wrow + d0, wv);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) o[u] = scale * (wyf * wv[u] - acc[i][j][4 * q + u]);
+            for (int u = 0; u < 4; ++u) o[u] = -tg.c * acc[i][j][4 * q + u];
           }
           store4(dst + d0, o[0], o[1], o[2], o[3]);
         }
@@ -974,10 +990,11 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
       __builtin_amdgcn_sched_barrier(0);
     }
   } else if constexpr (KIND == KIND_PROBS) {
-    // P[token, v] = exp(z - lse[token]) (times 1 - v^2 with a softcap) into the
-    // fragment-major copy used as the dH GEMM's B operand; the vocabulary padding up to the
-    // next 16 is written as zeros.  Rows of the copy past the chunk's tokens are written too
-    // (the dH GEMM ignores them).
+    // P'[token, v] = exp(z - lse[token]) (times 1 - v^2 with a softcap) into the
+    // fragment-major copy used as the B operand of the dH GEMM (the target entries are
+    // then rewritten by onehot_fix_kernel); the vocabulary padding up to the next 16 is
+    // written as zeros.  Rows of the copy past the chunk's tokens are written too (every
+    // consumer ignores them).
     char* P = reinterpret_cast<char*>(g.p);
     const int vrem = g.p_ks * 16 - row_a0;  // uniform; multiple of 16
     const float c1 = g.lm.zscale * kLog2e;
@@ -1004,7 +1021,8 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
       }
     }
   } else {
-    // dH[token, d] = (g / tau) (W[y, d] - acc), or the raw fp32 partial when split.
+    // dH[token, d] = -c acc with acc = sum_v Q[token, v] W[v, d] (+0 rows for tokens without
+    // a gradient), or the raw fp32 partial when split.
     const int drem = g.D - row_a0;  // uniform; multiple of 8
 #pragma unroll
     for (int j = 0; j < kFBW; ++j) {
@@ -1026,13 +1044,8 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
         }
         continue;
       }
-      const float gt = ok ? g.g[tok] : 0.0f;
-      const int y = ok ? g.targets[tok] : 0;
-      const bool live = gt != 0.0f && y >= 0 && y < g.V;
-      const float scale = live ? gt * g.lm.dscale : 0.0f;
-      const float ty = live ? g.zy[tok] / g.lm.zscale : 0.0f;
-      const float wyf = g.lm.cap_in > 0.0f ? 1.0f - ty * ty : 1.0f;  // dv/dx at the target
-      const __bf16* wrow = reinterpret_cast<const __bf16*>(g.w) + (int64_t)(live ? y : 0) * g.D;
+      const TokGrad tg = tok_grad(g.g, g.targets, g.zy, g.V, g.lm, tok, ok);
+      const float nc = -tg.c;
       __bf16* dst = reinterpret_cast<__bf16*>(g.dh) + (int64_t)(ok ? tok : 0) * g.D;
 #pragma unroll
       for (int i = 0; i < kFA; ++i) {
@@ -1040,10 +1053,9 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
         for (int q = 0; q < 4; ++q) {
           if (kEdge && 32 * i + 8 * q >= drem) continue;
           const int d0 = row_a0 + 32 * i + 8 * q + 4 * hi;
-          float wv[4], o[4];
-          load4(wrow + d0, wv);
+          float o[4];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) o[u] = live ? scale * (wyf * wv[u] - acc[i][j][4 * q + u]) : 0.0f;
+          for (int u = 0; u < 4; ++u) o[u] = tg.live ? nc * acc[i][j][4 * q + u] : 0.0f;
           if (ok) store4(dst + d0, o[0], o[1], o[2], o[3]);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -1129,7 +1141,7 @@ __global__ __launch_bounds__(256) void transpose_w_kernel(const __bf16* __restri
 }
 
 // The kept logits of a chunk (d = z - m_tile, fp16, fragment-major) turned into the
-// probabilities in place: p = exp(d + m_tile - lse) (times 1 - v^2, v = z / zscale, with a
+// probabilities in place: P' = exp(d + m_tile - lse) (times 1 - v^2, v = z / zscale, with a
 // softcap), bf16 rounded to nearest even; rows past the chunk's tokens become 0.  One
 // thread per 16-byte unit (8 consecutive vocabulary entries of one token, one tile).
 __global__ __launch_bounds__(256) void probs_from_kept_kernel(uint4* __restrict__ P, int64_t units, int rows,
@@ -1169,6 +1181,36 @@ __global__ __launch_bounds__(256) void probs_from_kept_kernel(uint4* __restrict_
     out = make_uint4(pack_bf16(e[0], e[1]), pack_bf16(e[2], e[3]), pack_bf16(e[4], e[5]), pack_bf16(e[6], e[7]));
   }
   P[u] = out;
+}
+
+// Q[t, y_t] = P'[t, y_t] - wyf_t, computed in fp32 from the target logit and the log-sum-exp
+// and rounded once: for a confident token (P'_y near 1) the difference keeps its relative
+// precision.  One thread per token of the chunk; tokens with a target outside [0, V) are
+// left alone (their rows get no weight).
+template <typename T>
+__global__ __launch_bounds__(256) void onehot_fix_kernel(T* __restrict__ P, int rows, int ks_count, int64_t ldp,
+                                                         const int32_t* __restrict__ targets_c,
+                                                         const float* __restrict__ zy_c,
+                                                         const float* __restrict__ lse_c, int V, LogitMap lm) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= rows) return;
+  const int y = targets_c[t];
+  if (y < 0 || y >= V) return;
+  const float zy = zy_c[t];
+  float p = __builtin_amdgcn_exp2f((zy - lse_c[t]) * kLog2e);
+  float wyf = 1.0f;
+  if (lm.cap_in > 0.0f) {
+    const float v = zy / lm.zscale;
+    wyf = 1.0f - v * v;
+    p *= wyf;
+  }
+  const float q = p - wyf;
+  if constexpr (sizeof(T) == 2) {
+    char* dst = reinterpret_cast<char*>(P) + frag_off(t, y, ks_count);
+    *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(pack_bf16(q, 0.0f) & 0xffffu);
+  } else {
+    P[(int64_t)t * ldp + y] = q;
+  }
 }
 
 // ---------------------------------------------------------------------------- small kernels
@@ -1390,11 +1432,10 @@ __global__ __launch_bounds__(1024) void loss_finalize_kernel(const double* __res
 // Fixed-order sum of the split-vocabulary dH partials, then (g / tau) (W[y] - sum).
 template <typename T>
 __global__ __launch_bounds__(256) void dh_reduce_kernel(const float* __restrict__ part, int ksplit, int rows,
-                                                        int D, int V, LogitMap lm,
-                                                        const float* __restrict__ zy,
+                                                        int D, int V, float dscale,
                                                         const float* __restrict__ g,
                                                         const int32_t* __restrict__ targets,
-                                                        const T* __restrict__ W, T* __restrict__ dh) {
+                                                        T* __restrict__ dh) {
   const int quads = D / 4;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)rows * quads) return;
@@ -1409,13 +1450,9 @@ __global__ __launch_bounds__(256) void dh_reduce_kernel(const float* __restrict_
       const float4 p = *reinterpret_cast<const float4*>(part + ((int64_t)k * rows + tok) * D + d0);
       s[0] += p.x; s[1] += p.y; s[2] += p.z; s[3] += p.w;
     }
-    float wv[4];
-    load4(W + (int64_t)y * D + d0, wv);
-    const float scale = gt * lm.dscale;
-    const float ty = zy[tok] / lm.zscale;
-    const float wyf = lm.cap_in > 0.0f ? 1.0f - ty * ty : 1.0f;  // dv/dx at the target
+    const float nc = -gt * dscale;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) o[u] = scale * (wyf * wv[u] - s[u]);
+    for (int u = 0; u < 4; ++u) o[u] = nc * s[u];
   }
   store4(dh + (int64_t)tok * D + d0, o[0], o[1], o[2], o[3]);
 }
@@ -1566,8 +1603,16 @@ void backward_chunk(Launcher& L, const Plan& p, const T* W, const T* WT, bool us
     gp.lse = lse_c;
     gp.p = P;
     gp.ldp = p.ldp;
+    gp.g = g_c;
+    gp.targets = targets_c;
+    gp.zy = zy_c;
     launch_gemm<T, KIND_PROBS>(L, GRPO_K_PROBS, gp);
   }
+
+  L.run(GRPO_K_ONEHOT_FIX, [&] {
+    hipLaunchKernelGGL((onehot_fix_kernel<T>), dim3(grid1(rows, 256)), dim3(256), 0, L.stream, P, rows,
+                       (int)p.ks_v, p.ldp, targets_c, zy_c, lse_c, (int)p.V, lm);
+  });
 
   // dH^T tiles: hidden x tokens, K = vocabulary, split over the vocabulary if needed.
   const int ks_plan = (k == p.nchunks - 1) ? p.ksplit_tail : p.ksplit_full;
@@ -1604,7 +1649,7 @@ void backward_chunk(Launcher& L, const Plan& p, const T* W, const T* WT, bool us
   if (ksplit > 1) {
     L.run(GRPO_K_DH_REDUCE, [&] {
       hipLaunchKernelGGL((dh_reduce_kernel<T>), dim3(grid1((int64_t)rows * (p.D / 4), 256)), dim3(256), 0,
-                         L.stream, part, ksplit, rows, (int)p.D, (int)p.V, lm, zy_c, g_c, targets_c, W, dH_c);
+                         L.stream, part, ksplit, rows, (int)p.D, (int)p.V, lm.dscale, g_c, targets_c, dH_c);
     });
   }
 }
@@ -1721,7 +1766,8 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, int mode, const gr
       const int64_t units = p.rows_pad * p.ks_v * 2;
       L.run(GRPO_K_PROBS_KEPT, [&] {
         hipLaunchKernelGGL(probs_from_kept_kernel, dim3(grid1(units, 256)), dim3(256), 0, L.stream,
-                           reinterpret_cast<uint4*>(P), units, rows, (int)p.ks_v, pm, (int)p.ntiles_v, lse + t0, lm);
+                           reinterpret_cast<uint4*>(P), units, rows, (int)p.ks_v, pm, (int)p.ntiles_v, lse + t0,
+                           lm);
       });
     }
     backward_chunk<T>(L, p, W, WT, use_wt, Hc, Hf, rows, k, lse + t0, gbuf + t0, targets + t0, dH + t0 * p.D, P,
@@ -1742,7 +1788,7 @@ grpo_status logp_bwd_impl(const Plan& p, const grpo_shape* shape, const T* H, co
   char* Hf = ws + p.off_Hf;
   float* part = reinterpret_cast<float*>(ws + p.off_part);
   float* zy = reinterpret_cast<float*>(ws + p.off_zy);
-  if (lm.cap_in > 0.0f) {  // the softcap's derivative at the target needs the target logits
+  {  // the target logits: the exact target entry of Q (and the softcap factor there)
     L.run(GRPO_K_TARGET_LOGIT, [&] {
       hipLaunchKernelGGL((target_logit_kernel<T>), dim3(grid1(p.T, 4)), dim3(256), 0, L.stream, H, W, targets,
                          (int)p.T, (int)p.D, (int)p.V, lm, zy);

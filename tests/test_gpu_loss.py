@@ -150,3 +150,25 @@ def test_dh_gemm_both_operand_paths(V, chunk, expect_wt):
     tm.close()
     r = check_loss_outputs(k, got)
     say(f"  logp err {r['logp_err']:.2e} dH rel {r['dH_rel']:.2e}")
+
+
+def test_confident_tokens_dH():
+    # Softmax concentrated on the target (p_y near 1): dH = (g/tau)(W[y] - sum p W) is a
+    # small difference of large terms; the target entry is formed in fp32 before rounding.
+    from gpu_cases import rel_l2, host_matrix
+    k = case(101, D=128, V=700, lengths=[200, 150], G=2, chunk=128, w_std=2.0)
+    H64, W64 = k["H64"], k["W64"]
+    z = H64 @ W64.T
+    y = np.argmax(z, axis=1).astype(np.int32)  # every target is its row's argmax
+    lp, _ = oracle.selective_log_softmax(H64, W64, y)
+    assert np.median(np.exp(lp)) > 0.9
+    old = (lp + 0.05).astype(np.float32)
+    out = oracle.grpo_loss_and_grad(H64, W64, y, k["c"].cu, k["mask"], old.astype(np.float64), None,
+                                    k["adv"].astype(np.float64), 1.0, beta=0.0)
+    d = to_device(k)
+    got = grpo_loss_fwd_bwd(d["H"], d["W"], torch.from_numpy(y).cuda(), k["c"].cu, torch.from_numpy(old).cuda(),
+                            None, d["adv"], 128, beta=0.0)
+    dH = oracle.widen(host_matrix(got["dH"], "bf16"), "bf16")
+    e = rel_l2(dH, out["dH"])
+    say(f"confident tokens: median p_y {np.median(np.exp(lp)):.3f}, dH rel L2 {e:.2e}")
+    assert e <= 1e-2

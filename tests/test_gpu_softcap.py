@@ -66,7 +66,7 @@ def test_logp_fwd_bwd_ce_with_softcap(dtype, cap):
     tm = Timer(1024)
     dH = grpo_logp_bwd(d["H"], d["W"], d["targets"], lse, torch.from_numpy(grad).cuda(), chunk, tau, timer=tm, **kw)
     torch.cuda.synchronize()
-    assert tm.read("target_logit")[1] == (1 if cap > 0 else 0)
+    assert tm.read("target_logit")[1] == 1  # the exact target entries need the target logits
     tm.close()
     ref = oracle.logp_backward(k["H64"], k["W64"], y, grad.astype(np.float64), tau, scale=_scale(mul, div),
                                softcap=cap)
