@@ -93,14 +93,19 @@ def logits(H: np.ndarray, W: np.ndarray, temperature: float = 1.0, scale: float 
     return logit_map(H @ W.T, temperature, scale, softcap)[0]
 
 
-def _dH_rows(H_rows, W, y, lse_rows, g_rows, temperature, scale, softcap):
-    """g_t * d logp_t / dH_t for rows with a valid target: the recomputed logits give
-    softmax p; d logp / dz = onehot(y) - p; dz/dx from logit_map; dx/dH = W."""
+def _dx_rows(H_rows, W, y, lse_rows, g_rows, temperature, scale, softcap):
+    """g_t * d logp_t / dx_t (x = the raw lm_head products) for rows with a valid target:
+    the recomputed logits give softmax p; d logp / dz = onehot(y) - p; dz/dx from logit_map."""
     z, dz = logit_map(H_rows @ W.T, temperature, scale, softcap)
     p = np.exp(z - lse_rows[:, None])
     dl = -p
     dl[np.arange(dl.shape[0]), y] += 1.0
-    return g_rows[:, None] * ((dl * dz) @ W)
+    return g_rows[:, None] * (dl * dz)
+
+
+def _dH_rows(H_rows, W, y, lse_rows, g_rows, temperature, scale, softcap):
+    """g_t * d logp_t / dH_t = (g_t d logp_t / dx_t) W, since dx/dH = W."""
+    return _dx_rows(H_rows, W, y, lse_rows, g_rows, temperature, scale, softcap) @ W
 
 
 def selective_log_softmax(H: np.ndarray, W: np.ndarray, targets: np.ndarray,
@@ -248,14 +253,17 @@ def grpo_loss_from_logp(logp, old_logp, ref_logp, adv, cu, mask, clip_eps_low=0.
 
 def grpo_loss_and_grad(H, W, targets, cu, mask, old_logp, ref_logp, adv, temperature=1.0,
                        clip_eps_low=0.2, clip_eps_high=0.2, beta=0.001, agg="seq_mean",
-                       block: int = ROW_BLOCK, scale: float = 1.0, softcap: float = 0.0):
+                       block: int = ROW_BLOCK, scale: float = 1.0, softcap: float = 0.0,
+                       with_dW: bool = False):
     """Loss, log-probs and the gradient of the loss with respect to H.
 
     dH_t = (g_t / temperature) * (W[y_t] - sum_v softmax(z_t)_v W[v]), the
     chain rule through logp_t = z_{t,y_t} - LSE_t, whose derivative with
     respect to z_t is onehot(y_t) - softmax(z_t) ([P4], the recompute
     backward); with a logit scale or softcap the softmax term carries dz/dx (see
-    logit_map).  Rows with g_t = 0 or an out-of-range target are exactly 0.
+    logit_map).  Rows with g_t = 0 or an out-of-range target are exactly 0.  With
+    with_dW, also dW = sum_t (g_t dlogp_t/dx_t)^T H_t, the lm_head gradient a full
+    fine-tune needs (x = H W^T).
     """
     T, D = H.shape
     V = W.shape[0]
@@ -263,6 +271,7 @@ def grpo_loss_and_grad(H, W, targets, cu, mask, old_logp, ref_logp, adv, tempera
     L, ell, g = grpo_loss_from_logp(logp, old_logp, ref_logp, adv, cu, mask, clip_eps_low,
                                     clip_eps_high, beta, agg)
     dH = np.zeros((T, D))
+    dW = np.zeros((V, D)) if with_dW else None
     y_all = np.asarray(targets, dtype=np.int64)
     for r0 in range(0, T, block):
         r1 = min(T, r0 + block)
@@ -271,13 +280,16 @@ def grpo_loss_and_grad(H, W, targets, cu, mask, old_logp, ref_logp, adv, tempera
         live = (g[r0:r1] != 0) & (y >= 0) & (y < V)
         if not live.any():
             continue
-        dH[rows[live]] = _dH_rows(H[r0:r1][live], W, y[live], lse[rows[live]], g[rows[live]],
-                                  temperature, scale, softcap)
-    return dict(loss=L, logp=logp, lse=lse, token_loss=ell, g=g, dH=dH)
+        gx = _dx_rows(H[r0:r1][live], W, y[live], lse[rows[live]], g[rows[live]], temperature, scale,
+                      softcap)
+        dH[rows[live]] = gx @ W
+        if dW is not None:
+            dW += gx.T @ H[r0:r1][live]
+    return dict(loss=L, logp=logp, lse=lse, token_loss=ell, g=g, dH=dH, dW=dW)
 
 
 def logp_backward(H, W, targets, grad_logp, temperature=1.0, block: int = ROW_BLOCK, scale: float = 1.0,
-                  softcap: float = 0.0):
+                  softcap: float = 0.0, with_dW: bool = False):
     """Gradient with respect to H of sum_t grad_logp[t] * logp_t.
 
     The backward of the chunked selective log-softmax ([P4], "Auslagern von
@@ -285,13 +297,14 @@ def logp_backward(H, W, targets, grad_logp, temperature=1.0, block: int = ROW_BL
     the backward recomputes the logits and applies the incoming gradient of
     the log-probabilities, dH_t = (grad_t / temperature) * (W[y_t] - sum_v
     softmax(z_t)_v W[v]).  Rows with grad_t = 0 or an out-of-range target are
-    exactly 0.
+    exactly 0.  With with_dW, returns (dH, dW) with dW the gradient with respect to W.
     """
     T, D = H.shape
     V = W.shape[0]
     g = np.asarray(grad_logp, dtype=np.float64)
     _, lse = selective_log_softmax(H, W, targets, temperature, block, scale, softcap)
     dH = np.zeros((T, D))
+    dW = np.zeros((V, D)) if with_dW else None
     y_all = np.asarray(targets, dtype=np.int64)
     for r0 in range(0, T, block):
         r1 = min(T, r0 + block)
@@ -300,13 +313,16 @@ def logp_backward(H, W, targets, grad_logp, temperature=1.0, block: int = ROW_BL
         live = (g[r0:r1] != 0) & (y >= 0) & (y < V)
         if not live.any():
             continue
-        dH[rows[live]] = _dH_rows(H[r0:r1][live], W, y[live], lse[rows[live]], g[rows[live]],
-                                  temperature, scale, softcap)
-    return dH
+        gx = _dx_rows(H[r0:r1][live], W, y[live], lse[rows[live]], g[rows[live]], temperature, scale,
+                      softcap)
+        dH[rows[live]] = gx @ W
+        if dW is not None:
+            dW += gx.T @ H[r0:r1][live]
+    return (dH, dW) if with_dW else dH
 
 
 def cross_entropy_loss_and_grad(H, W, targets, mask=None, temperature=1.0, block: int = ROW_BLOCK,
-                                scale: float = 1.0, softcap: float = 0.0):
+                                scale: float = 1.0, softcap: float = 0.0, with_dW: bool = False):
     """Chunked cross-entropy (the supervised loss the same chunked log-softmax
     serves): L = -(1/N) sum_t mask_t logp_t with N = sum_t mask_t (L = 0 and
     dH = 0 when N = 0), per-token loss -logp_t, g_t = dL/dlogp_t = -mask_t / N,
@@ -321,8 +337,9 @@ def cross_entropy_loss_and_grad(H, W, targets, mask=None, temperature=1.0, block
     terms = [w[t] * (-logp[t]) for t in range(T) if w[t] != 0]
     L = math.fsum(terms) if terms else 0.0
     g = -w
-    dH = logp_backward(H, W, targets, g, temperature, block, scale, softcap)
-    return dict(loss=L, logp=logp, lse=lse, token_loss=-logp, g=g, dH=dH)
+    out = logp_backward(H, W, targets, g, temperature, block, scale, softcap, with_dW)
+    dH, dW = out if with_dW else (out, None)
+    return dict(loss=L, logp=logp, lse=lse, token_loss=-logp, g=g, dH=dH, dW=dW)
 
 
 def grad_rows(H_rows, W, targets_rows, lse_rows, g_rows, temperature=1.0, scale=1.0, softcap=0.0):

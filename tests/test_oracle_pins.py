@@ -463,3 +463,44 @@ def test_softcapped_cross_entropy_matches_torch_autograd():
     lp, _ = oracle.selective_log_softmax(H, W, y, tau, scale=s, softcap=c)
     ref = torch.log_softmax(z.detach(), dim=1)[torch.arange(11), torch.tensor(y)].numpy()
     np.testing.assert_allclose(lp, ref, rtol=0, atol=1e-13)
+
+
+# ------------------------------------------------------------------ dW
+
+def test_dW_matches_finite_differences_in_W():
+    # GRPO loss with a softcap and a logit scale: d L / d W by central differences
+    H, W, y, cu, mask, old, ref, adv, tau = _case(41, lengths=(3, 4, 2, 3), V=9, D=5)
+    kw = dict(clip_eps_low=0.2, clip_eps_high=0.2, beta=0.1)
+    out = oracle.grpo_loss_and_grad(H, W, y, cu, mask, old, ref, adv, tau, scale=0.8, softcap=3.0, with_dW=True,
+                                    **kw)
+    rho = np.exp(out["logp"] - old)
+    assert np.all(np.abs(rho - 0.8) > 1e-3) and np.all(np.abs(rho - 1.2) > 1e-3)
+
+    def loss(Wx):
+        lp, _ = oracle.selective_log_softmax(H, Wx, y, tau, scale=0.8, softcap=3.0)
+        return oracle.grpo_loss_from_logp(lp, old, ref, adv, cu, mask, **kw)[0]
+
+    h = 1e-6
+    fd = np.zeros_like(W)
+    for v in range(W.shape[0]):
+        for d in range(W.shape[1]):
+            e = np.zeros_like(W)
+            e[v, d] = h
+            fd[v, d] = (loss(W + e) - loss(W - e)) / (2 * h)
+    assert np.linalg.norm(out["dW"] - fd) / np.linalg.norm(fd) < 1e-6
+
+
+def test_dW_cross_entropy_matches_torch_autograd():
+    torch = pytest.importorskip("torch")
+    H, W, y = _tiny(42, T=13, D=6, V=11)
+    tau = 0.7
+    mask = np.ones(13)
+    mask[[2, 9]] = 0
+    out = oracle.cross_entropy_loss_and_grad(H, W, y, mask, tau, with_dW=True)
+    Wt = torch.tensor(W, requires_grad=True)
+    z = torch.tensor(H) @ Wt.T / tau
+    yt = torch.tensor(np.where(mask > 0, y, -100))
+    torch.nn.functional.cross_entropy(z, yt, ignore_index=-100).backward()
+    np.testing.assert_allclose(out["dW"], Wt.grad.numpy(), rtol=0, atol=1e-15)
+    dH, dW = oracle.logp_backward(H, W, y, out["g"], tau, with_dW=True)
+    np.testing.assert_allclose(dW, out["dW"], rtol=0, atol=0)
