@@ -123,7 +123,9 @@ typedef enum {
   GRPO_K_TRANSPOSE_W = 10, /* transposed copy of W for the dH GEMM (bf16, when it fits) */
   GRPO_K_PROBS_KEPT = 11,  /* probabilities from the kept logits, in place (keep_chunk_logits) */
   GRPO_K_ONEHOT_FIX = 12,  /* exact target entries of the backward's P' - onehot matrix */
-  GRPO_K_COUNT = 13
+  GRPO_K_HT_COPY = 13,     /* tokens' operand of the dW GEMM (bf16, when dW is requested) */
+  GRPO_K_DW_GEMM = 14,     /* MFMA GEMM dW (+)= Gx^T H per chunk */
+  GRPO_K_COUNT = 15
 } grpo_kernel_id;
 
 typedef struct grpo_timer grpo_timer; /* opaque, owned by the caller */
@@ -174,14 +176,18 @@ grpo_status grpo_advantages(const float* rewards, int64_t num_seqs, int64_t grou
  *   (ref_logp may be NULL only when beta == 0); adv fp32 [num_seqs].
  *   loss fp64 [1] (written); logp, token_loss fp32 [T] (written when not NULL;
  *   token_loss holds l_t, unweighted); dH [T, D] of shape->dtype (overwritten;
- *   masked tokens get +0 rows); workspace of grpo_workspace_bytes(shape, S, 1) bytes.
+ *   masked tokens get +0 rows); dW fp32 [V, D] (NULL = not computed; bf16 only): the
+ *   gradient with respect to W, dW = sum_t (dL/dx_t)^T H_t with x_t = H_t W^T, overwritten
+ *   (accumulated over the chunks in fixed order; for a full fine-tune, where the lm_head is
+ *   trained: under LoRA it is frozen), one more 2 D V flop GEMM per token;
+ *   workspace of grpo_workspace_bytes(shape, S, 1) bytes.
  * The loss is summed in fp64 in a fixed token order, so it is bitwise independent
  * of chunk_tokens, as are logp and token_loss. */
 grpo_status grpo_loss_fwd_bwd(const grpo_shape* shape, const grpo_loss_params* params,
                               const void* H, const void* W, const int32_t* targets,
                               const int32_t* cu_seqlens, int64_t num_seqs, const uint8_t* mask,
                               const float* old_logp, const float* ref_logp, const float* adv,
-                              double* loss, float* logp, float* token_loss, void* dH,
+                              double* loss, float* logp, float* token_loss, void* dH, float* dW,
                               void* workspace, size_t workspace_bytes, void* stream,
                               grpo_timer* timer);
 
@@ -194,11 +200,12 @@ grpo_status grpo_loss_fwd_bwd(const grpo_shape* shape, const grpo_loss_params* p
  *   H, W, targets, shape as for grpo_logp_fwd; lse fp32 [T]: the log-sum-exp grpo_logp_fwd
  *   returned for the same H, W and temperature; grad_logp fp32 [T] (dL/dlogp; 0 for tokens
  *   that do not contribute); dH [T, D] of shape->dtype (overwritten; +0 rows where
- *   grad_logp is 0 or the target is outside [0, V)); workspace of
- *   grpo_workspace_bytes(shape, 1, 1) bytes. */
+ *   grad_logp is 0 or the target is outside [0, V)); dW fp32 [V, D] as for
+ *   grpo_loss_fwd_bwd (NULL = not computed); workspace of grpo_workspace_bytes(shape, 1, 1)
+ *   bytes. */
 grpo_status grpo_logp_bwd(const grpo_shape* shape, const void* H, const void* W, const int32_t* targets,
-                          const float* lse, const float* grad_logp, void* dH, void* workspace,
-                          size_t workspace_bytes, void* stream, grpo_timer* timer);
+                          const float* lse, const float* grad_logp, void* dH, float* dW,
+                          void* workspace, size_t workspace_bytes, void* stream, grpo_timer* timer);
 
 /* Chunked cross-entropy, forward and backward ([P2] "Unsloth internals", the fused, chunked
  * cross-entropy: the loss over the vocabulary without the [T, V] logits or their gradient):
@@ -206,13 +213,15 @@ grpo_status grpo_logp_bwd(const grpo_shape* shape, const void* H, const void* W,
  *   dH   = the grpo_logp_bwd of g_t = -mask_t / N.
  *   mask uint8 [T] (NULL = every token counts); loss fp64 [1] (written, summed in fp64 in a
  *   fixed token order); logp, token_loss fp32 [T] (written when not NULL; token_loss holds
- *   -logp_t); dH [T, D] of shape->dtype (overwritten); workspace of
- *   grpo_workspace_bytes(shape, 1, 1) bytes.  A counted token whose target is outside [0, V)
+ *   -logp_t); dH [T, D] of shape->dtype (overwritten); dW fp32 [V, D] as for
+ *   grpo_loss_fwd_bwd (NULL = not computed); workspace of grpo_workspace_bytes(shape, 1, 1)
+ *   bytes.  A counted token whose target is outside [0, V)
  *   makes the loss NaN; its dH row is +0. */
 grpo_status grpo_ce_loss_fwd_bwd(const grpo_shape* shape, const void* H, const void* W,
                                  const int32_t* targets, const uint8_t* mask, double* loss,
-                                 float* logp, float* token_loss, void* dH, void* workspace,
-                                 size_t workspace_bytes, void* stream, grpo_timer* timer);
+                                 float* logp, float* token_loss, void* dH, float* dW,
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 grpo_timer* timer);
 
 /* Human-readable name of a status code (static storage). */
 const char* grpo_status_string(grpo_status status);

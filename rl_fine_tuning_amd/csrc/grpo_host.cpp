@@ -128,7 +128,14 @@ grpo_status make_plan(const grpo_shape* s, int64_t S, bool backward, Plan* out) 
   p.off_lse = take(T * 4);
   p.off_pm = take((size_t)p.ntiles_v * C * 4);
   p.off_ps = take((size_t)p.ntiles_v * C * 4);
-  if (bf16) p.off_Hf = take((size_t)p.rows_pad * (size_t)p.ks_d * 16 * 2);
+  // the chunk's fragment-major hidden states; in the backward the same region later holds
+  // the tokens' operand of the dW GEMM ((D rounded up to 256) x rows_pad bf16)
+  if (bf16) {
+    size_t hf = (size_t)p.rows_pad * (size_t)p.ks_d * 16 * 2;
+    const size_t ht = (size_t)cdiv(p.D, kTileA16) * kTileA16 * (size_t)p.rows_pad * 2;
+    if (backward && ht > hf) hf = ht;
+    p.off_Hf = take(hf);
+  }
   if (backward) {
     p.off_g = take(T * 4);
     p.off_wl = take(T * 8);

@@ -62,7 +62,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 // transposed copy W^T [D, ldt] with the direct-to-LDS loads of the logits GEMMs.
 // KIND_LSES (bf16): the LSE epilogue that also keeps the chunk's logits, as d = z - (tile
 // max) in fp16, in the probabilities buffer (the variant without the recompute GEMM).
-enum Kind { KIND_LSE = 0, KIND_PROBS = 1, KIND_DH = 2, KIND_DHT = 3, KIND_LSES = 4 };
+// KIND_DW (bf16): dW += Gx^T H_c, A = Q^T transposed from the chunk's fragment-major Q.
+enum Kind { KIND_LSE = 0, KIND_PROBS = 1, KIND_DH = 2, KIND_DHT = 3, KIND_LSES = 4, KIND_DW = 5 };
 
 // Byte offset of 16-byte chunk c of row r inside a [256 rows x 8 chunks] LDS tile.
 __device__ __forceinline__ int lds_off(int r, int c) {
@@ -141,6 +142,8 @@ struct GemmArgs {
   // DH
   const float* g;         // [b_rows]
   const float* zy;        // [b_rows]: target logits (the softcap's W[y] factor)
+  float* dw;              // DW: [V, D] fp32
+  int accumulate;         // DW: add to dw (later chunks) instead of overwriting it
   const int32_t* targets; // [b_rows]
   const void* w;          // W, for the W[y] term
   void* dh;               // [b_rows, D] (ksplit == 1)
@@ -450,6 +453,47 @@ struct TransTileA {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         *reinterpret_cast<uint2*>(lds_stage + lds_off2(128 * p + 4 * q + ((t + r) & 3), c) + 8 * h) = o[t];
+    }
+  }
+};
+
+// A operand of the dW GEMM: Q^T (rows = vocabulary, k = the chunk's tokens) from the
+// chunk's fragment-major Q (rows = tokens, 16-byte units of 8 vocabulary entries): thread i
+// takes tokens k0 + 4 (i % 8) .. + 3 of vocabulary rows 8 (i / 8) .. + 7 of the tile (four
+// 16-byte units, 64 contiguous bytes), transposes the 4 x 8 block in registers and writes
+// eight 8-byte half chunks, one per vocabulary row.  Columns past the padded vocabulary
+// read as 0; token rows past the chunk hold finite values that the zero rows of the
+// tokens' operand cancel.
+struct TransTileQ {
+  uint4 v[4];
+  const char* Q;
+  int ks_count, v0, vpad, tq, vg;
+  __device__ __forceinline__ void init(const void* Q_, int ks_count_, int row0, int tid) {
+    Q = reinterpret_cast<const char*>(Q_);
+    ks_count = ks_count_;
+    vpad = ks_count_ * 16;
+    tq = tid & 7;
+    vg = tid >> 3;
+    v0 = row0 + 8 * vg;
+  }
+  // Stages at or past kend (the ring's look-ahead past the last one) read nothing; the last
+  // stage's tokens stay below the copy's rows (rounded up to 256).
+  __device__ __forceinline__ void load(int k0, int kend) {
+    const bool in = v0 < vpad && k0 < kend;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = in ? *reinterpret_cast<const uint4*>(Q + frag_off(k0 + 4 * tq + e, v0, ks_count))
+                : make_uint4(0u, 0u, 0u, 0u);
+  }
+  __device__ __forceinline__ void store(char* lds_stage) const {
+    const int c = tq >> 1, h = tq & 1;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int sh = 16 * (r & 1);
+      const uint32_t e0 = (u4get(v[0], r >> 1) >> sh) & 0xffffu, e1 = (u4get(v[1], r >> 1) >> sh) & 0xffffu;
+      const uint32_t e2 = (u4get(v[2], r >> 1) >> sh) & 0xffffu, e3 = (u4get(v[3], r >> 1) >> sh) & 0xffffu;
+      *reinterpret_cast<uint2*>(lds_stage + lds_off2(8 * vg + r, c) + 8 * h) =
+          make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
     }
   }
 };
@@ -792,7 +836,7 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  constexpr bool kTrans = KIND == KIND_DH;  // A transposed in registers
+  constexpr bool kTrans = KIND == KIND_DH || KIND == KIND_DW;  // A transposed in registers
   const int row_a0 = tile_a * kTA;
   const int row_b0 = tb * kTB;
   const int k_begin = ks * g.k_len;
@@ -812,9 +856,11 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
   const char* Bw =
       reinterpret_cast<const char*>(g.b) + (int64_t)tb * g.b_ks * kFB * 1024 + kFBW * w * 1024 + lane * 16;
   const int ks0 = k_begin >> 4;
-  using ATile = typename std::conditional<kTrans, TransTileA, DmaTileA>::type;
+  using ATile = typename std::conditional<
+      KIND == KIND_DW, TransTileQ, typename std::conditional<kTrans, TransTileA, DmaTileA>::type>::type;
   ATile at;
-  if constexpr (kTrans) at.init(A, g.lda, row_a0, tid);
+  if constexpr (KIND == KIND_DW) at.init(g.a, g.p_ks, row_a0, tid);
+  else if constexpr (kTrans) at.init(A, g.lda, row_a0, tid);
   else at.init(A, g.lda, row_a0, g.a_rows, tid);
 
   if (nk > 0) {
@@ -1020,6 +1066,25 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  } else if constexpr (KIND == KIND_DW) {
+    // dW[v, d] = acc (first chunk) or dW[v, d] + acc, fp32; acc = sum_t Q[t, v] (-c_t H[t, d]).
+    float* dw = g.dw;
+#pragma unroll
+    for (int j = 0; j < kFBW; ++j) {
+      const int d = row_b0 + 64 * w + 32 * j + col;
+      if (d >= g.D) continue;
+#pragma unroll
+      for (int i = 0; i < kFA; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int v = row_a0 + 32 * i + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (kEdge && v >= g.V) continue;
+          float* p = dw + (int64_t)v * g.D + d;
+          *p = g.accumulate ? *p + acc[i][j][r] : acc[i][j][r];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   } else {
     // dH[token, d] = -c acc with acc = sum_v Q[token, v] W[v, d] (+0 rows for tokens without
     // a gradient), or the raw fp32 partial when split.
@@ -1213,6 +1278,42 @@ __global__ __launch_bounds__(256) void onehot_fix_kernel(T* __restrict__ P, int 
   }
 }
 
+// Tokens' operand of the dW GEMM: (-c_t H[t, :])^T of the chunk in the fragment-major
+// layout with rows = hidden units and k = tokens: [d / 256][t / 16][(d % 256) / 32][lane]
+// [8 tokens], lane = d % 32 + 32 ((t % 16) / 8).  Tokens past the chunk, tokens without a
+// gradient and hidden units past D are 0.  One thread per 16-byte unit.
+__global__ __launch_bounds__(256) void ht_copy_kernel(const __bf16* __restrict__ Hc, int rows, int D,
+                                                      int ks_count, int64_t units, const float* __restrict__ g_c,
+                                                      const int32_t* __restrict__ targets_c, int V, float dscale,
+                                                      uint4* __restrict__ out) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= units) return;
+  const int l = (int)(u & 63);
+  const int64_t fr = u >> 6;
+  const int fb = (int)(fr % kFB);
+  const int64_t rest = fr / kFB;
+  const int kstep = (int)(rest % ks_count);
+  const int db = (int)(rest / ks_count);
+  const int d = db * kTB + fb * 32 + (l & 31);
+  const int t0 = kstep * 16 + 8 * (l >> 5);
+  float e[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int t = t0 + k;
+    float x = 0.0f;
+    if (d < D && t < rows) {
+      const float gt = g_c[t];
+      const int y = targets_c[t];
+      if (gt != 0.0f && y >= 0 && y < V) {
+        const uint32_t hv = *reinterpret_cast<const uint16_t*>(Hc + (int64_t)t * D + d);
+        x = -gt * dscale * __uint_as_float(hv << 16);
+      }
+    }
+    e[k] = x;
+  }
+  out[u] = make_uint4(pack_bf16(e[0], e[1]), pack_bf16(e[2], e[3]), pack_bf16(e[4], e[5]), pack_bf16(e[6], e[7]));
+}
+
 // ---------------------------------------------------------------------------- small kernels
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -1340,6 +1441,11 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   if (a.token_loss) a.token_loss[t] = ell;
   a.g[t] = counted ? w * dell : 0.0f;
   a.wl[t] = w64 != 0.0 ? w64 * (double)ell : 0.0;
+}
+
+// x[0, n) = 0 (a kernel rather than a memset, so that the call can be captured in a graph).
+__global__ __launch_bounds__(256) void zero_fill_kernel(float* __restrict__ x, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) x[i] = 0.0f;
 }
 
 // cu = {0, T}: the whole stream as one sequence (cross-entropy).
@@ -1595,9 +1701,9 @@ grpo_status logp_impl(const Plan& p, const grpo_shape* shape, const T* H, const 
 // (dH GEMM, split over the vocabulary when the chunk is too small to fill the GPU).  Hf
 // holds the chunk's fragment-major hidden states (bf16).
 template <typename T>
-void backward_chunk(Launcher& L, const Plan& p, const T* W, const T* WT, bool use_wt, const T* Hc, const char* Hf,
+void backward_chunk(Launcher& L, const Plan& p, const T* W, const T* WT, bool use_wt, const T* Hc, char* Hf,
                     int rows, int64_t k, const float* lse_c, const float* g_c, const int32_t* targets_c, T* dH_c,
-                    T* P, float* part, const LogitMap& lm, const float* zy_c, bool probs_ready = false) {
+                    T* P, float* part, const LogitMap& lm, const float* zy_c, bool probs_ready, float* dW) {
   if (!probs_ready) {
     GemmArgs gp = logits_args<T>(p, W, Hc, Hf, rows, lm);
     gp.lse = lse_c;
@@ -1652,6 +1758,41 @@ void backward_chunk(Launcher& L, const Plan& p, const T* W, const T* WT, bool us
                          L.stream, part, ksplit, rows, (int)p.D, (int)p.V, lm.dscale, g_c, targets_c, dH_c);
     });
   }
+  if constexpr (sizeof(T) == 2) {
+    if (dW) {
+      // dW (+)= Gx^T H_c: the tokens' operand (-c H_c)^T replaces the chunk's hidden-state
+      // copy (no longer needed once the recompute GEMM has run), then the dW GEMM with the
+      // vocabulary as rows, the hidden units as columns and the chunk's tokens as K.
+      const int ks_t = (int)(p.rows_pad / 16);
+      const int64_t units = cdiv(p.D, kTileB16) * ks_t * kFB * 64;
+      L.run(GRPO_K_HT_COPY, [&] {
+        hipLaunchKernelGGL(ht_copy_kernel, dim3(grid1(units, 256)), dim3(256), 0, L.stream,
+                           reinterpret_cast<const __bf16*>(Hc), rows, (int)p.D, ks_t, units, g_c, targets_c,
+                           (int)p.V, lm.dscale, reinterpret_cast<uint4*>(Hf));
+      });
+      GemmArgs gw = {};
+      gw.a = P;
+      gw.b = Hf;
+      gw.a_rows = (int)p.V;
+      gw.b_rows = (int)p.D;
+      gw.K = rows;
+      gw.k_len = rows;
+      gw.tiles_a_base = (int)p.ntiles_v;
+      gw.tiles_a = (int)p.ntiles_v;
+      gw.tiles_b = (int)cdiv(p.D, kTileB16);
+      gw.xcd_axis = 0;
+      gw.group_b = 4;
+      gw.b_ks = ks_t;
+      gw.p_ks = (int)p.ks_v;
+      gw.V = (int)p.V;
+      gw.D = (int)p.D;
+      gw.ksplit = 1;
+      gw.lm = lm;
+      gw.dw = dW;
+      gw.accumulate = k > 0;
+      launch_gemm<T, KIND_DW>(L, GRPO_K_DW_GEMM, gw);
+    }
+  }
 }
 
 // W^T for the dH GEMM, once per call, when the plan has room for it (bf16).
@@ -1675,7 +1816,7 @@ template <typename T>
 grpo_status loss_impl(const Plan& p, const grpo_shape* shape, int mode, const grpo_loss_params* prm, const T* H,
                       const T* W, const int32_t* targets, const int32_t* cu_host, const uint8_t* mask,
                       const float* old_logp, const float* ref_logp, const float* adv, double* loss,
-                      float* logp, float* token_loss, T* dH, char* ws, Launcher& L) {
+                      float* logp, float* token_loss, T* dH, float* dW, char* ws, Launcher& L) {
   const LogitMap lm = make_logit_map(shape);
   float* zy = reinterpret_cast<float*>(ws + p.off_zy);
   float* lse = reinterpret_cast<float*>(ws + p.off_lse);
@@ -1771,8 +1912,10 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, int mode, const gr
       });
     }
     backward_chunk<T>(L, p, W, WT, use_wt, Hc, Hf, rows, k, lse + t0, gbuf + t0, targets + t0, dH + t0 * p.D, P,
-                      part, lm, zy + t0, keep);
+                      part, lm, zy + t0, keep, dW);
   }
+  if (dW && p.nchunks == 0)  // no tokens: the gradient is 0
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(1024), dim3(256), 0, L.stream, dW, (int64_t)p.V * p.D);
   L.run(GRPO_K_LOSS_FINALIZE, [&] {
     hipLaunchKernelGGL(loss_finalize_kernel, dim3(1), dim3(1024), 0, L.stream, wl, (int)p.T, loss);
   });
@@ -1782,7 +1925,7 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, int mode, const gr
 // Backward of grpo_logp_fwd: dH = (grad / tau) (W[y] - P W) per chunk, from the forward's lse.
 template <typename T>
 grpo_status logp_bwd_impl(const Plan& p, const grpo_shape* shape, const T* H, const T* W, const int32_t* targets,
-                          const float* lse, const float* grad, T* dH, char* ws, Launcher& L) {
+                          const float* lse, const float* grad, T* dH, float* dW, char* ws, Launcher& L) {
   const LogitMap lm = make_logit_map(shape);
   T* P = reinterpret_cast<T*>(ws + p.off_P);
   char* Hf = ws + p.off_Hf;
@@ -1802,7 +1945,7 @@ grpo_status logp_bwd_impl(const Plan& p, const grpo_shape* shape, const T* H, co
     const T* Hc = H + t0 * p.D;
     if constexpr (sizeof(T) == 2) enqueue_frag_copy(L, p, Hc, rows, Hf);
     backward_chunk<T>(L, p, W, WT, use_wt, Hc, Hf, rows, k, lse + t0, grad + t0, targets + t0, dH + t0 * p.D, P,
-                      part, lm, zy + t0);
+                      part, lm, zy + t0, false, dW);
   }
   return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_E_HIP;
 }
@@ -1855,8 +1998,8 @@ grpo_status grpo_advantages(const float* rewards, int64_t num_seqs, int64_t grou
 grpo_status grpo_loss_fwd_bwd(const grpo_shape* shape, const grpo_loss_params* params, const void* H,
                               const void* W, const int32_t* targets, const int32_t* cu_seqlens, int64_t num_seqs,
                               const uint8_t* mask, const float* old_logp, const float* ref_logp, const float* adv,
-                              double* loss, float* logp, float* token_loss, void* dH, void* workspace,
-                              size_t workspace_bytes, void* stream, grpo_timer* timer) {
+                              double* loss, float* logp, float* token_loss, void* dH, float* dW,
+                              void* workspace, size_t workspace_bytes, void* stream, grpo_timer* timer) {
   grpo_status st = validate_shape(shape);
   if (st != GRPO_OK) return st;
   st = validate_loss_params(params);
@@ -1867,6 +2010,7 @@ grpo_status grpo_loss_fwd_bwd(const grpo_shape* shape, const grpo_loss_params* p
   st = validate_cu(cu_seqlens, num_seqs, shape->T);
   if (st != GRPO_OK) return st;
   if (!aligned16(H) || !aligned16(W) || !aligned16(dH)) return GRPO_E_UNSUPPORTED;
+  if (dW && shape->dtype != GRPO_BF16) return GRPO_E_UNSUPPORTED;
   Plan p;
   st = make_plan(shape, num_seqs, true, &p);
   if (st != GRPO_OK) return st;
@@ -1877,41 +2021,48 @@ grpo_status grpo_loss_fwd_bwd(const grpo_shape* shape, const grpo_loss_params* p
   const float* ref = params->beta != 0.0f ? ref_logp : nullptr;
   if (p.dtype == GRPO_BF16)
     return loss_impl<__bf16>(p, shape, 1, params, (const __bf16*)H, (const __bf16*)W, targets, cu_seqlens, mask,
-                             old_logp, ref, adv, loss, logp, token_loss, (__bf16*)dH, ws, L);
+                             old_logp, ref, adv, loss, logp, token_loss, (__bf16*)dH, dW, ws, L);
   return loss_impl<float>(p, shape, 1, params, (const float*)H, (const float*)W, targets, cu_seqlens, mask,
-                          old_logp, ref, adv, loss, logp, token_loss, (float*)dH, ws, L);
+                          old_logp, ref, adv, loss, logp, token_loss, (float*)dH, nullptr, ws, L);
 }
 
 grpo_status grpo_logp_bwd(const grpo_shape* shape, const void* H, const void* W, const int32_t* targets,
-                          const float* lse, const float* grad_logp, void* dH, void* workspace, size_t workspace_bytes,
-                          void* stream, grpo_timer* timer) {
+                          const float* lse, const float* grad_logp, void* dH, float* dW, void* workspace,
+                          size_t workspace_bytes, void* stream, grpo_timer* timer) {
   Plan p;
   grpo_status st = make_plan(shape, 1, true, &p);
   if (st != GRPO_OK) return st;
   if (!W) return GRPO_E_NULL;
   if (p.T > 0 && (!H || !targets || !lse || !grad_logp || !dH)) return GRPO_E_NULL;
   if (!aligned16(H) || !aligned16(W) || !aligned16(dH)) return GRPO_E_UNSUPPORTED;
+  if (dW && shape->dtype != GRPO_BF16) return GRPO_E_UNSUPPORTED;
   if (!ws_ok(p, workspace, workspace_bytes)) return GRPO_E_WORKSPACE;
-  if (p.T == 0) return GRPO_OK;
+  if (p.T == 0 && !dW) return GRPO_OK;  // nothing to do
   (void)hipGetLastError();
   Launcher L{reinterpret_cast<hipStream_t>(stream), timer};
+  if (p.T == 0) {  // no tokens: dH is empty and the gradient of W is 0
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(1024), dim3(256), 0, L.stream, dW, (int64_t)p.V * p.D);
+    return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_E_HIP;
+  }
   char* ws = reinterpret_cast<char*>(workspace);
   if (p.dtype == GRPO_BF16)
     return logp_bwd_impl<__bf16>(p, shape, (const __bf16*)H, (const __bf16*)W, targets, lse, grad_logp,
-                                 (__bf16*)dH, ws, L);
-  return logp_bwd_impl<float>(p, shape, (const float*)H, (const float*)W, targets, lse, grad_logp, (float*)dH, ws,
-                              L);
+                                 (__bf16*)dH, dW, ws, L);
+  return logp_bwd_impl<float>(p, shape, (const float*)H, (const float*)W, targets, lse, grad_logp, (float*)dH,
+                              nullptr, ws, L);
 }
 
 grpo_status grpo_ce_loss_fwd_bwd(const grpo_shape* shape, const void* H, const void* W, const int32_t* targets,
                                  const uint8_t* mask, double* loss, float* logp, float* token_loss, void* dH,
-                                 void* workspace, size_t workspace_bytes, void* stream, grpo_timer* timer) {
+                                 float* dW, void* workspace, size_t workspace_bytes, void* stream,
+                                 grpo_timer* timer) {
   Plan p;
   grpo_status st = make_plan(shape, 1, true, &p);
   if (st != GRPO_OK) return st;
   if (!loss || !W) return GRPO_E_NULL;
   if (p.T > 0 && (!H || !targets || !dH)) return GRPO_E_NULL;
   if (!aligned16(H) || !aligned16(W) || !aligned16(dH)) return GRPO_E_UNSUPPORTED;
+  if (dW && shape->dtype != GRPO_BF16) return GRPO_E_UNSUPPORTED;
   if (!ws_ok(p, workspace, workspace_bytes)) return GRPO_E_WORKSPACE;
   (void)hipGetLastError();
   Launcher L{reinterpret_cast<hipStream_t>(stream), timer};
@@ -1919,9 +2070,9 @@ grpo_status grpo_ce_loss_fwd_bwd(const grpo_shape* shape, const void* H, const v
   // one sequence spanning the stream (its bounds are written on the device): token-mean weights
   if (p.dtype == GRPO_BF16)
     return loss_impl<__bf16>(p, shape, 2, nullptr, (const __bf16*)H, (const __bf16*)W, targets, nullptr, mask,
-                             nullptr, nullptr, nullptr, loss, logp, token_loss, (__bf16*)dH, ws, L);
+                             nullptr, nullptr, nullptr, loss, logp, token_loss, (__bf16*)dH, dW, ws, L);
   return loss_impl<float>(p, shape, 2, nullptr, (const float*)H, (const float*)W, targets, nullptr, mask, nullptr,
-                          nullptr, nullptr, loss, logp, token_loss, (float*)dH, ws, L);
+                          nullptr, nullptr, loss, logp, token_loss, (float*)dH, nullptr, ws, L);
 }
 
 grpo_status grpo_debug_token_index(const int32_t* cu_seqlens, int64_t num_seqs, int64_t T, int64_t chunk_tokens,

@@ -18,7 +18,8 @@ GRPO_BF16, GRPO_F32 = 0, 1
 GRPO_AGG = {"seq_mean": 0, "token_mean": 1}
 GRPO_STD = {"unbiased": 0, "population": 1}
 KERNELS = ["target_logit", "logits_lse", "merge", "probs", "dh_gemm", "dh_reduce", "token_index",
-           "loss_finalize", "advantages", "frag_copy", "transpose_w", "probs_kept", "onehot_fix"]
+           "loss_finalize", "advantages", "frag_copy", "transpose_w", "probs_kept", "onehot_fix", "ht_copy",
+           "dw_gemm"]
 KERNEL_ID = {k: i for i, k in enumerate(KERNELS)}
 
 
@@ -61,11 +62,11 @@ def lib() -> ctypes.CDLL:
         L.grpo_advantages.argtypes = [vp, i64, i64, i32, f32, vp, vp]
         L.grpo_advantages.restype = ctypes.c_int
         L.grpo_loss_fwd_bwd.argtypes = [sp, ctypes.POINTER(GrpoLossParams), vp, vp, vp, vp, i64, vp, vp,
-                                        vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+                                        vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
         L.grpo_loss_fwd_bwd.restype = ctypes.c_int
-        L.grpo_logp_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+        L.grpo_logp_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
         L.grpo_logp_bwd.restype = ctypes.c_int
-        L.grpo_ce_loss_fwd_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+        L.grpo_ce_loss_fwd_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
         L.grpo_ce_loss_fwd_bwd.restype = ctypes.c_int
         L.grpo_status_string.argtypes = [ctypes.c_int]
         L.grpo_status_string.restype = ctypes.c_char_p
@@ -194,8 +195,9 @@ def grpo_logp_fwd(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, chunk
 def grpo_logp_bwd(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: torch.Tensor,
                   grad_logp: torch.Tensor, chunk_tokens: int, temperature: float = 1.0, *,
                   logit_scale_multiply=0.0, logit_scale_divide=0.0, logit_softcapping=0.0, dH=None,
-                  workspace=None, stream=None, timer: Timer | None = None) -> torch.Tensor:
-    """dH of sum_t grad_logp[t] * logp_t, recomputing each chunk's logits from the forward's lse."""
+                  dW=None, workspace=None, stream=None, timer: Timer | None = None):
+    """dH of sum_t grad_logp[t] * logp_t, recomputing each chunk's logits from the forward's lse.
+    With dW (an fp32 [V, D] tensor, or True to allocate one) returns (dH, dW)."""
     for t, n in ((H, "H"), (W, "W"), (targets, "targets"), (lse, "lse"), (grad_logp, "grad_logp")):
         _dev(t, n)
     T, D = H.shape
@@ -206,17 +208,22 @@ def grpo_logp_bwd(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: 
     ws, wsn = _workspace(nbytes, workspace, H.device)
     if dH is None:
         dH = torch.empty_like(H)
+    want_dW = dW is not None and dW is not False
+    if dW is True:
+        dW = torch.empty(V, D, dtype=torch.float32, device=H.device)
     st = lib().grpo_logp_bwd(ctypes.byref(shape), _ptr(H), _ptr(W), _ptr(targets), _ptr(lse), _ptr(grad_logp),
-                             _ptr(dH), _ptr(ws), wsn, _stream(stream), timer.handle if timer else None)
+                             _ptr(dH), _ptr(dW) if want_dW else None, _ptr(ws), wsn, _stream(stream),
+                             timer.handle if timer else None)
     _check(st, "grpo_logp_bwd")
-    return dH
+    return (dH, dW) if want_dW else dH
 
 
 def grpo_ce_loss_fwd_bwd(H, W, targets, chunk_tokens, *, temperature=1.0, logit_scale_multiply=0.0,
                          logit_scale_divide=0.0, logit_softcapping=0.0, keep_chunk_logits=False, mask=None,
-                         want_logp=True, want_token_loss=False, dH=None, workspace=None, stream=None,
+                         want_logp=True, want_token_loss=False, dH=None, dW=None, workspace=None, stream=None,
                          timer: Timer | None = None):
-    """Mean cross-entropy over the unmasked tokens, per-token logp, and dL/dH."""
+    """Mean cross-entropy over the unmasked tokens, per-token logp, dL/dH and (with dW: an
+    fp32 [V, D] tensor, or True to allocate one) dL/dW."""
     for t, n in ((H, "H"), (W, "W"), (targets, "targets")):
         _dev(t, n)
     if mask is not None:
@@ -233,11 +240,13 @@ def grpo_ce_loss_fwd_bwd(H, W, targets, chunk_tokens, *, temperature=1.0, logit_
     tl = torch.empty(T, dtype=torch.float32, device=dev) if want_token_loss else None
     if dH is None:
         dH = torch.empty_like(H)
+    if dW is True:
+        dW = torch.empty(V, D, dtype=torch.float32, device=dev)
     st = lib().grpo_ce_loss_fwd_bwd(ctypes.byref(shape), _ptr(H), _ptr(W), _ptr(targets), _ptr(mask), _ptr(loss),
-                                    _ptr(logp), _ptr(tl), _ptr(dH), _ptr(ws), wsn, _stream(stream),
-                                    timer.handle if timer else None)
+                                    _ptr(logp), _ptr(tl), _ptr(dH), _ptr(dW) if dW is not None else None, _ptr(ws),
+                                    wsn, _stream(stream), timer.handle if timer else None)
     _check(st, "grpo_ce_loss_fwd_bwd")
-    return dict(loss=loss, logp=logp, token_loss=tl, dH=dH)
+    return dict(loss=loss, logp=logp, token_loss=tl, dH=dH, dW=dW)
 
 
 def grpo_advantages(rewards: torch.Tensor, group_size: int, std_mode: str = "unbiased", eps: float = 1e-4,
@@ -253,8 +262,8 @@ def grpo_advantages(rewards: torch.Tensor, group_size: int, std_mode: str = "unb
 def grpo_loss_fwd_bwd(H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk_tokens, *,
                       temperature=1.0, logit_scale_multiply=0.0, logit_scale_divide=0.0, logit_softcapping=0.0,
                       keep_chunk_logits=False, clip_eps_low=0.2, clip_eps_high=0.2, beta=0.001, agg="seq_mean",
-                      mask=None, want_logp=True, want_token_loss=True, dH=None, workspace=None, stream=None,
-                      timer: Timer | None = None):
+                      mask=None, want_logp=True, want_token_loss=True, dH=None, dW=None, workspace=None,
+                      stream=None, timer: Timer | None = None):
     """GRPO loss, per-token logp and objective, and dL/dH.  cu_seqlens is a host int32 array/tensor."""
     for t, n in ((H, "H"), (W, "W"), (targets, "targets"), (old_logp, "old_logp"), (adv, "adv")):
         _dev(t, n)
@@ -277,12 +286,15 @@ def grpo_loss_fwd_bwd(H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk_
     tl = torch.empty(T, dtype=torch.float32, device=dev) if want_token_loss else None
     if dH is None:
         dH = torch.empty_like(H)
+    if dW is True:
+        dW = torch.empty(V, D, dtype=torch.float32, device=dev)
     st = lib().grpo_loss_fwd_bwd(ctypes.byref(shape), ctypes.byref(params), _ptr(H), _ptr(W), _ptr(targets),
                                  ctypes.c_void_p(cu.data_ptr()), S, _ptr(mask), _ptr(old_logp), _ptr(ref_logp),
-                                 _ptr(adv), _ptr(loss), _ptr(logp), _ptr(tl), _ptr(dH), _ptr(ws), wsn,
-                                 _stream(stream), timer.handle if timer else None)
+                                 _ptr(adv), _ptr(loss), _ptr(logp), _ptr(tl), _ptr(dH),
+                                 _ptr(dW) if dW is not None else None, _ptr(ws), wsn, _stream(stream),
+                                 timer.handle if timer else None)
     _check(st, "grpo_loss_fwd_bwd")
-    return dict(loss=loss, logp=logp, token_loss=tl, dH=dH)
+    return dict(loss=loss, logp=logp, token_loss=tl, dH=dH, dW=dW)
 
 
 def grpo_debug_token_index(cu_seqlens, T: int, chunk_tokens: int, device="cuda", stream=None):

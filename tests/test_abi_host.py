@@ -88,10 +88,10 @@ def test_loss_validation():
     good = B.GrpoLossParams(0.2, 0.2, 0.001, 0)
 
     def call(sh=None, prm=good, cu_p=cup, S=3, ref=FAKE, ws_bytes=1 << 40, H=FAKE, dH=FAKE, old=FAKE,
-             adv=FAKE, loss=FAKE):
+             adv=FAKE, loss=FAKE, dW=None):
         sh = sh or shape(T=T)
         return lib.grpo_loss_fwd_bwd(ctypes.byref(sh), ctypes.byref(prm), H, FAKE, FAKE, cu_p, S, None, old,
-                                     ref, adv, loss, None, None, dH, FAKE, ws_bytes, None, None)
+                                     ref, adv, loss, None, None, dH, dW, FAKE, ws_bytes, None, None)
 
     assert call(ws_bytes=16) == 4
     assert call(H=None) == 1
@@ -116,6 +116,7 @@ def test_loss_validation():
     assert call(cu_p=bad.ctypes.data_as(ctypes.c_void_p)) == 2     # cu[S] != T
     assert call(sh=shape(T=T, tau=0.0)) == 3
     assert call(dH=ctypes.c_void_p((1 << 20) + 4)) == 5
+    assert call(sh=shape(T=T, dtype=1), dW=FAKE) == 5  # dW: bf16 only
 
 
 def test_advantages_validation():
@@ -149,11 +150,11 @@ def test_logp_bwd_validation():
     lib = B.lib()
     ws = ctypes.c_void_p(1 << 20)
 
-    def f(sh=None, H=FAKE, W=FAKE, y=FAKE, lse=FAKE, g=FAKE, dH=FAKE, wsp=ws, n=1 << 40):
+    def f(sh=None, H=FAKE, W=FAKE, y=FAKE, lse=FAKE, g=FAKE, dH=FAKE, wsp=ws, n=1 << 40, dW=None):
         sh = sh or shape()
-        return lib.grpo_logp_bwd(ctypes.byref(sh), H, W, y, lse, g, dH, wsp, n, None, None)
+        return lib.grpo_logp_bwd(ctypes.byref(sh), H, W, y, lse, g, dH, dW, wsp, n, None, None)
 
-    assert lib.grpo_logp_bwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, 1 << 40, None, None) == 1
+    assert lib.grpo_logp_bwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, ws, 1 << 40, None, None) == 1
     for k in ("H", "W", "y", "lse", "g", "dH"):
         assert f(**{k: None}) == 1, k
     assert f(shape(tau=0.0)) == 3
@@ -162,6 +163,7 @@ def test_logp_bwd_validation():
     assert f(n=16) == 4
     assert f(wsp=ctypes.c_void_p((1 << 20) + 16)) == 4
     assert f(shape(T=0), H=None, y=None, lse=None, g=None, dH=None) == 0  # nothing to do
+    assert f(shape(dtype=1, D=64), dW=FAKE) == 5  # dW: bf16 only
 
 
 def test_ce_loss_validation():
@@ -169,8 +171,8 @@ def test_ce_loss_validation():
 
     def f(sh=None, H=FAKE, W=FAKE, y=FAKE, loss=FAKE, dH=FAKE, n=1 << 40, wsp=FAKE):
         sh = sh or shape()
-        return lib.grpo_ce_loss_fwd_bwd(ctypes.byref(sh), H, W, y, None, loss, None, None, dH, wsp, n, None,
-                                         None)
+        return lib.grpo_ce_loss_fwd_bwd(ctypes.byref(sh), H, W, y, None, loss, None, None, dH, None, wsp, n,
+                                         None, None)
 
     for k in ("H", "W", "y", "loss", "dH"):
         assert f(**{k: None}) == 1, k
