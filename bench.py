@@ -274,10 +274,27 @@ def main():
         ms_b = timed(lambda: grpo_logp_bwd(H, W, targets, lse, grad, C, dH=dH, workspace=ws))
         ms_ce = timed(lambda: grpo_ce_loss_fwd_bwd(H, W, targets, C, dH=dH, workspace=ws, want_logp=False))
         ms_adv = timed(lambda: grpo_advantages(rewards, G, out=adv))
+        ms_dw, dw_tf = None, None
+        if case.dtype == "bf16":
+            dW = torch.empty(V, D, dtype=torch.float32, device=dev)
+            tmw = Timer(4096)
+            def step_dw():
+                grpo_advantages(rewards, G, out=adv)
+                grpo_loss_fwd_bwd(H, W, targets, cu, old, ref, adv, C, dH=dH, dW=dW, workspace=ws,
+                                  want_logp=False, want_token_loss=False, timer=tmw)
+            step_dw()
+            tmw.reset()
+            ms_dw = timed(step_dw)
+            ms_k, n_k, _ = tmw.read("dw_gemm")
+            dw_tf = gemm_flops["dh_gemm"] * (n_k / nchunks) / (ms_k * 1e-3) / 1e12 if ms_k else None
+            tmw.close()
+            del dW
         per = lambda ms, k: {"tokens_per_s": T / (ms * 1e-3), "ms": ms,
                              "mfma_frac": k * T * D * V / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)}
         result["entry_points"] = {"grpo_logp_fwd": per(ms_f, 2.0), "grpo_logp_bwd": per(ms_b, 4.0),
                                   "grpo_ce_loss_fwd_bwd": per(ms_ce, 6.0),
+                                  "grpo_loss_fwd_bwd_with_dW": dict(per(ms_dw, 8.0), dw_gemm_tflops=dw_tf)
+                                  if ms_dw else None,
                                   "grpo_advantages": {"us": 1e3 * ms_adv, "sequences": S}}
         log(f"entry points: logp_fwd {ms_f:.1f} ms, logp_bwd {ms_b:.1f} ms, ce {ms_ce:.1f} ms, "
             f"advantages {1e3 * ms_adv:.1f} us")
