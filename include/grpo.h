@@ -31,7 +31,8 @@
  *    hipStream_t passed as void* (NULL = the null stream).  Every call only
  *    enqueues work on `stream`; none synchronizes the host (except the timer
  *    read-out), none allocates device memory, and none keeps a pointer after it
- *    returns.  The caller owns every buffer, including the workspace.
+ *    returns ([host] arrays are read during the call, into kernel arguments).
+ *    The caller owns every buffer, including the workspace.
  *  - Row-major layouts: H[T, D], W[V, D] (the nn.Linear [out, in] layout), dH[T, D].
  *    Row t of H predicts targets[t]; the caller applies any causal shift.
  *  - Sequences are contiguous runs of the flattened stream given by cu_seqlens;

@@ -1448,6 +1448,18 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(float* __restrict__ x, i
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) x[i] = 0.0f;
 }
 
+// Sequence offsets uploaded by value: each launch carries up to 256 of them in its kernel
+// arguments, which the runtime copies at launch, so the host array is never read after the
+// call returns and no pageable-memory copy (which may synchronize the host) is needed.
+constexpr int kCuPerLaunch = 256;
+struct CuPiece {
+  int32_t v[kCuPerLaunch];
+  int32_t first, n;
+};
+__global__ __launch_bounds__(256) void upload_cu_kernel(const CuPiece piece, int32_t* __restrict__ cu) {
+  if ((int)threadIdx.x < piece.n) cu[piece.first + threadIdx.x] = piece.v[threadIdx.x];
+}
+
 // cu = {0, T}: the whole stream as one sequence (cross-entropy).
 __global__ void whole_stream_cu_kernel(int32_t* cu, int T) {
   if (threadIdx.x == 0) {
@@ -1836,9 +1848,14 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, int mode, const gr
 
   if (mode == 2) {
     hipLaunchKernelGGL(whole_stream_cu_kernel, dim3(1), dim3(64), 0, L.stream, cu, (int)p.T);
-  } else if (hipMemcpyAsync(cu, cu_host, sizeof(int32_t) * (S + 1), hipMemcpyHostToDevice, L.stream) !=
-             hipSuccess) {
-    return GRPO_E_HIP;
+  } else {
+    for (int first = 0; first < S + 1; first += kCuPerLaunch) {
+      CuPiece piece;
+      piece.first = first;
+      piece.n = S + 1 - first < kCuPerLaunch ? S + 1 - first : kCuPerLaunch;
+      for (int i = 0; i < piece.n; ++i) piece.v[i] = cu_host[first + i];
+      hipLaunchKernelGGL(upload_cu_kernel, dim3(1), dim3(256), 0, L.stream, piece, cu);
+    }
   }
   L.run(GRPO_K_TOKEN_INDEX, [&] {
     if (p.T > 0)
@@ -2088,8 +2105,13 @@ grpo_status grpo_debug_token_index(const int32_t* cu_seqlens, int64_t num_seqs, 
   (void)hipGetLastError();
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   int32_t* cu = reinterpret_cast<int32_t*>(workspace);
-  if (hipMemcpyAsync(cu, cu_seqlens, sizeof(int32_t) * (num_seqs + 1), hipMemcpyHostToDevice, s) != hipSuccess)
-    return GRPO_E_HIP;
+  for (int64_t first = 0; first < num_seqs + 1; first += kCuPerLaunch) {
+    CuPiece piece;
+    piece.first = (int32_t)first;
+    piece.n = (int32_t)(num_seqs + 1 - first < kCuPerLaunch ? num_seqs + 1 - first : kCuPerLaunch);
+    for (int i = 0; i < piece.n; ++i) piece.v[i] = cu_seqlens[first + i];
+    hipLaunchKernelGGL(upload_cu_kernel, dim3(1), dim3(256), 0, s, piece, cu);
+  }
   hipLaunchKernelGGL(token_index_kernel, dim3(grid1(T, 256)), dim3(256), 0, s, cu, (int)num_seqs, (int)T,
                      (int)(chunk_tokens > INT32_MAX ? INT32_MAX : chunk_tokens), seq_id, chunk_id, pos);
   return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_E_HIP;

@@ -172,3 +172,14 @@ def test_confident_tokens_dH():
     e = rel_l2(dH, out["dH"])
     say(f"confident tokens: median p_y {np.median(np.exp(lp)):.3f}, dH rel L2 {e:.2e}")
     assert e <= 1e-2
+
+
+def test_many_sequences_seq_mean():
+    # 600 short sequences (several uploads of the sequence offsets), seq-mean weights
+    rng = np.random.default_rng(131)
+    lengths = rng.integers(1, 6, 600).tolist()
+    k = case(131, D=64, V=500, lengths=lengths, G=4, chunk=256, old_std=0.2, mask_frac=0.1)
+    say(f"loss with {len(lengths)} sequences, T={k['T']}")
+    got = run_loss(k, 256)
+    torch.cuda.synchronize()
+    check_loss_outputs(k, got)

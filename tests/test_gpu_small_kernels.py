@@ -33,7 +33,7 @@ def test_advantages_worked_example():
 
 
 @pytest.mark.parametrize("lengths,chunk", [([5, 0, 7, 1, 0, 13], 4), ([55000, 55000], 8192),
-                                           ([1] * 300, 7), ([1000], 1000)])
+                                           ([1] * 300, 7), ([1000], 1000), ([0, 3] * 400, 16)])
 def test_token_index_bit_exact(lengths, chunk):
     cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
     T = int(cu[-1])
