@@ -159,7 +159,9 @@ def main():
     ref = (logp0.double() + torch.from_numpy(case.noise_ref).to(dev)).float()
     del logp0
     ws_bytes = grpo_workspace_bytes(T, D, V, C, 0 if case.dtype == "bf16" else 1, num_seqs=S)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    # one buffer also serves the entry-point timings (the dW call may lay it out differently)
+    ws_dw = grpo_workspace_bytes(T, D, V, C, 0, num_seqs=S, with_dW=True) if case.dtype == "bf16" else 0
+    ws = torch.empty(max(ws_bytes, ws_dw), dtype=torch.uint8, device=dev)
     dH = torch.empty_like(H)
     adv = torch.empty(S, dtype=torch.float32, device=dev)
     cu = case.cu
@@ -197,7 +199,7 @@ def main():
                   "dh_gemm": sum(2.0 * r * D * V for r in rows)}
     kernels = {}
     for k in ("target_logit", "logits_lse", "merge", "probs", "dh_gemm", "dh_reduce", "token_index",
-              "loss_finalize", "frag_copy", "transpose_w"):
+              "loss_finalize", "frag_copy", "transpose_w", "w_copy", "onehot_fix"):
         ms, n, dropped = timer.read(k)
         kernels[k] = {"ms_total": ms, "launches": n}
     dominant = max(gemm_flops, key=lambda k: kernels[k]["ms_total"])
@@ -227,7 +229,7 @@ def main():
                      "traffic": measured_traffic(dominant, cfg == 3 and C == 8192),
                      "traffic_unit": "bytes per launch (HBM-side: L2 fills from the fabric + writes)",
                      "avg_launch_ms": dk["ms_total"] / max(1, dk["launches"]),
-                     "flops_per_launch_avg": gemm_flops[dominant] / nchunks},
+                     "flops_per_launch_avg": gemm_flops[dominant] * args.steps / max(1, dk["launches"])},
         "kernels": kernels,
         "workspace_bytes": ws_bytes,
         "peak_extra_bytes": peak_extra,
@@ -285,8 +287,9 @@ def main():
             step_dw()
             tmw.reset()
             ms_dw = timed(step_dw)
-            ms_k, n_k, _ = tmw.read("dw_gemm")
-            dw_tf = gemm_flops["dh_gemm"] * (n_k / nchunks) / (ms_k * 1e-3) / 1e12 if ms_k else None
+            ms_k, _, _ = tmw.read("dw_gemm")
+            calls = tmw.read("loss_finalize")[1]  # one per call
+            dw_tf = gemm_flops["dh_gemm"] * calls / (ms_k * 1e-3) / 1e12 if ms_k else None
             tmw.close()
             del dW
         per = lambda ms, k: {"tokens_per_s": T / (ms * 1e-3), "ms": ms,

@@ -121,23 +121,35 @@ typedef enum {
   GRPO_K_LOSS_FINALIZE = 7,/* fixed-order fp64 sum of the per-token loss terms */
   GRPO_K_ADVANTAGES = 8,
   GRPO_K_FRAG_COPY = 9,    /* fragment-major copy of a chunk's hidden states (bf16 path) */
-  GRPO_K_TRANSPOSE_W = 10, /* transposed copy of W for the dH GEMM (bf16, when it fits) */
+  GRPO_K_TRANSPOSE_W = 10, /* fragment-major W^T for the dH GEMM (bf16, when it fits) */
   GRPO_K_PROBS_KEPT = 11,  /* probabilities from the kept logits, in place (keep_chunk_logits) */
   GRPO_K_ONEHOT_FIX = 12,  /* exact target entries of the backward's P' - onehot matrix */
   GRPO_K_HT_COPY = 13,     /* tokens' operand of the dW GEMM (bf16, when dW is requested) */
   GRPO_K_DW_GEMM = 14,     /* MFMA GEMM dW (+)= Gx^T H per chunk */
-  GRPO_K_COUNT = 15
+  GRPO_K_W_COPY = 15,      /* fragment-major W for the logits GEMMs (bf16, when it fits) */
+  GRPO_K_COUNT = 16
 } grpo_kernel_id;
 
 typedef struct grpo_timer grpo_timer; /* opaque, owned by the caller */
 
-/* Bytes of workspace that grpo_logp_fwd (with_backward = 0) or grpo_loss_fwd_bwd
- * (with_backward = 1) needs for this shape and num_seqs sequences.  Returns 0 for an
+/* Bytes of workspace that grpo_logp_fwd (with_backward = 0), the backward entry points
+ * (with_backward = 1) or the backward entry points given a dW output (with_backward = 2)
+ * need for this shape and num_seqs sequences.  Returns 0 for an
  * invalid shape.  Bounded by chunk_tokens * V * 4 (one chunk's fp32 logits) plus
- * O(T + chunk_tokens * (V / 128 + D)) bytes of per-token state.  For bf16 the
- * backward also keeps a transposed copy of W (D * V * 2 bytes) when the total then
- * stays within chunk_tokens * V * 4. */
+ * O(T + chunk_tokens * (V / 128 + D)) bytes of per-token state.  For bf16 the workspace
+ * may also hold fragment-major copies of W^T (for the dH GEMM) and of W (for the logits
+ * GEMMs), about D * V * 2 bytes each, and the backward may run over slices of a chunk's
+ * tokens (not with dW): the library takes the largest of these layouts that keeps the
+ * total within chunk_tokens * V * 4 (grpo_plan_info reports the choice). */
 size_t grpo_workspace_bytes(const grpo_shape* shape, int64_t num_seqs, int with_backward);
+
+/* The workspace layout behind grpo_workspace_bytes for the same arguments (host only, no
+ * HIP call): info[0] = 1 if the dH GEMM reads a fragment-major copy of W^T, info[1] = 1 if
+ * the logits GEMMs read a fragment-major copy of W, info[2] = tokens per backward slice
+ * (>= the chunk's tokens when the backward of a chunk runs in one pass; 0 without the
+ * backward), info[3] = workspace bytes.  GRPO_E_NULL if info is NULL; the shape errors of
+ * grpo_workspace_bytes otherwise (info untouched). */
+grpo_status grpo_plan_info(const grpo_shape* shape, int64_t num_seqs, int with_backward, int64_t info[4]);
 
 /* Per-token log-probabilities of the targets ([P4]: chunked hidden-state selective
  * log-softmax): logp[t] = z[t, y_t] - logsumexp_v z[t, v], z = H W^T / temperature,
@@ -181,7 +193,7 @@ grpo_status grpo_advantages(const float* rewards, int64_t num_seqs, int64_t grou
  *   gradient with respect to W, dW = sum_t (dL/dx_t)^T H_t with x_t = H_t W^T, overwritten
  *   (accumulated over the chunks in fixed order; for a full fine-tune, where the lm_head is
  *   trained: under LoRA it is frozen), one more 2 D V flop GEMM per token;
- *   workspace of grpo_workspace_bytes(shape, S, 1) bytes.
+ *   workspace of grpo_workspace_bytes(shape, S, 1) bytes (S, 2 with dW).
  * The loss is summed in fp64 in a fixed token order, so it is bitwise independent
  * of chunk_tokens, as are logp and token_loss. */
 grpo_status grpo_loss_fwd_bwd(const grpo_shape* shape, const grpo_loss_params* params,
@@ -203,7 +215,7 @@ grpo_status grpo_loss_fwd_bwd(const grpo_shape* shape, const grpo_loss_params* p
  *   that do not contribute); dH [T, D] of shape->dtype (overwritten; +0 rows where
  *   grad_logp is 0 or the target is outside [0, V)); dW fp32 [V, D] as for
  *   grpo_loss_fwd_bwd (NULL = not computed); workspace of grpo_workspace_bytes(shape, 1, 1)
- *   bytes. */
+ *   bytes (1, 2 with dW). */
 grpo_status grpo_logp_bwd(const grpo_shape* shape, const void* H, const void* W, const int32_t* targets,
                           const float* lse, const float* grad_logp, void* dH, float* dW,
                           void* workspace, size_t workspace_bytes, void* stream, grpo_timer* timer);
@@ -216,7 +228,7 @@ grpo_status grpo_logp_bwd(const grpo_shape* shape, const void* H, const void* W,
  *   fixed token order); logp, token_loss fp32 [T] (written when not NULL; token_loss holds
  *   -logp_t); dH [T, D] of shape->dtype (overwritten); dW fp32 [V, D] as for
  *   grpo_loss_fwd_bwd (NULL = not computed); workspace of grpo_workspace_bytes(shape, 1, 1)
- *   bytes.  A counted token whose target is outside [0, V)
+ *   bytes (1, 2 with dW).  A counted token whose target is outside [0, V)
  *   makes the loss NaN; its dH row is +0. */
 grpo_status grpo_ce_loss_fwd_bwd(const grpo_shape* shape, const void* H, const void* W,
                                  const int32_t* targets, const uint8_t* mask, double* loss,

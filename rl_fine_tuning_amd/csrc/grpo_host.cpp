@@ -10,6 +10,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <initializer_list>
+
 #include "grpo_plan.h"
 
 namespace grpo {
@@ -95,7 +97,7 @@ int dh_ksplit(int64_t chunk_rows, int64_t D, int64_t V, int32_t dtype) {
   return best;
 }
 
-grpo_status make_plan(const grpo_shape* s, int64_t S, bool backward, Plan* out) {
+grpo_status make_plan(const grpo_shape* s, int64_t S, bool backward, Plan* out, bool dW) {
   grpo_status st = validate_shape(s);
   if (st != GRPO_OK) return st;
   if (backward && (S < 1 || S > INT32_MAX - 1)) return GRPO_E_SHAPE;
@@ -136,34 +138,71 @@ grpo_status make_plan(const grpo_shape* s, int64_t S, bool backward, Plan* out) 
     if (backward && ht > hf) hf = ht;
     p.off_Hf = take(hf);
   }
-  if (backward) {
+  const size_t bound = C * (size_t)p.V * 4;  // one chunk's fp32 logits
+  // Fragment-major copies of W for the bf16 GEMMs: W (rows = vocabulary) for the logits
+  // GEMMs and W^T (rows = hidden units) for the dH GEMM.  They make every direct-to-LDS
+  // load of the A operand one contiguous kilobyte, and are used when the workspace
+  // still fits in one chunk's fp32 logits.
+  const size_t wf = bf16 ? align_up((size_t)p.ntiles_v * kTileA16 * (size_t)p.ks_d * 16 * 2) : 0;
+  const size_t wt = bf16 ? align_up((size_t)cdiv(p.D, kTileA16) * kTileA16 * (size_t)p.ks_v * 16 * 2) : 0;
+  if (!backward) {
+    if (bf16 && p.nchunks > 0 && off + wf <= bound) {
+      p.use_wf = true;
+      p.off_Wf = take(wf);
+    }
+  } else {
     p.off_g = take(T * 4);
     p.off_wl = take(T * 8);
     p.off_seq = take(T * 4);
     p.off_cu = take((size_t)(S + 1) * 4);
     p.off_cnt = take((size_t)S * 4);
     p.off_wseq = take((size_t)S * 8);
-    p.off_P = bf16 ? take((size_t)p.rows_pad * (size_t)p.ks_v * 16 * 2) : take(C * (size_t)p.ldp * p.esize);
-    if (p.nchunks > 0) {
-      p.ksplit_full = dh_ksplit(p.C, p.D, p.V, p.dtype);
-      const int64_t tail = p.T - (p.nchunks - 1) * p.C;
-      p.ksplit_tail = dh_ksplit(tail, p.D, p.V, p.dtype);
+    const int64_t tail = p.nchunks > 0 ? p.T - (p.nchunks - 1) * p.C : 0;
+    // dH partials when the backward of a chunk runs over slices of `rows` tokens: the
+    // largest over the slices of a full chunk and of the last chunk.
+    auto part_bytes = [&](int64_t rows) {
+      size_t part = 0;
+      for (int64_t n : {p.C, tail}) {
+        for (int64_t r0 = 0; r0 < n; r0 += rows) {
+          const int64_t sr = n - r0 < rows ? n - r0 : rows;
+          const int ks = dh_ksplit(sr, p.D, p.V, p.dtype);
+          if (ks > 1 && (size_t)ks * sr * p.D * 4 > part) part = (size_t)ks * sr * p.D * 4;
+        }
+      }
+      return part;
+    };
+    auto prob_bytes = [&](int64_t rows) {
+      return bf16 ? (size_t)rows * (size_t)p.ks_v * 16 * 2 : C * (size_t)p.ldp * p.esize;
+    };
+    // Largest layout that fits: both copies with the whole chunk per backward pass; both
+    // copies with the backward in two token slices (not with kept logits, which fill the
+    // whole chunk's matrix in the forward, nor with dW, whose GEMM would read and write
+    // the fp32 [V, D] gradient once more per slice); W^T only; neither.
+    const int64_t full = bf16 ? p.rows_pad : (p.C > 0 ? p.C : 1);
+    const int64_t half = bf16 ? cdiv(p.rows_pad / kTileB16, 2) * kTileB16 : full;
+    const bool keep = s->keep_chunk_logits != 0;
+    struct Layout { int64_t rows; bool wt, wf; };
+    const Layout options[4] = {{full, true, true}, {half, true, true}, {full, true, false}, {full, false, false}};
+    Layout pick = options[3];
+    for (const Layout& o : options) {
+      if (!bf16 || p.nchunks == 0) break;
+      if (o.rows != full && (keep || dW || o.rows >= full)) continue;
+      if (off + align_up(prob_bytes(o.rows)) + align_up(part_bytes(o.rows)) + (o.wt ? wt : 0) + (o.wf ? wf : 0) <=
+          bound) {
+        pick = o;
+        break;
+      }
     }
-    size_t part = 0;
-    if (p.ksplit_full > 1) part = (size_t)p.ksplit_full * C * (size_t)p.D * 4;
-    const size_t tail_rows = p.nchunks > 0 ? (size_t)(p.T - (p.nchunks - 1) * p.C) : 0;
-    if (p.ksplit_tail > 1) {
-      const size_t tpart = (size_t)p.ksplit_tail * tail_rows * (size_t)p.D * 4;
-      if (tpart > part) part = tpart;
-    }
-    p.off_part = take(part);
-    // A transposed copy of W for the dH GEMM's direct-to-LDS loads, only when the whole
-    // workspace still fits in one chunk's fp32 logits.
-    p.ldt = cdiv(p.V, 8) * 8;
-    const size_t wt = align_up((size_t)p.D * (size_t)p.ldt * 2);
-    if (bf16 && p.nchunks > 0 && off + wt <= C * (size_t)p.V * 4) {
+    p.bwd_rows = pick.rows;
+    p.off_P = take(prob_bytes(pick.rows));
+    p.off_part = take(p.nchunks > 0 ? part_bytes(pick.rows) : 0);
+    if (pick.wt) {
       p.use_wt = true;
       p.off_WT = take(wt);
+    }
+    if (pick.wf) {
+      p.use_wf = true;
+      p.off_Wf = take(wf);
     }
   }
   p.total = off;
@@ -177,8 +216,20 @@ extern "C" {
 
 size_t grpo_workspace_bytes(const grpo_shape* shape, int64_t num_seqs, int with_backward) {
   grpo::Plan p;
-  if (grpo::make_plan(shape, num_seqs, with_backward != 0, &p) != GRPO_OK) return 0;
+  if (grpo::make_plan(shape, num_seqs, with_backward != 0, &p, with_backward == 2) != GRPO_OK) return 0;
   return p.total;
+}
+
+grpo_status grpo_plan_info(const grpo_shape* shape, int64_t num_seqs, int with_backward, int64_t info[4]) {
+  if (!info) return GRPO_E_NULL;
+  grpo::Plan p;
+  const grpo_status st = grpo::make_plan(shape, num_seqs, with_backward != 0, &p, with_backward == 2);
+  if (st != GRPO_OK) return st;
+  info[0] = p.use_wt ? 1 : 0;
+  info[1] = p.use_wf ? 1 : 0;
+  info[2] = p.bwd_rows;
+  info[3] = (int64_t)p.total;
+  return GRPO_OK;
 }
 
 const char* grpo_status_string(grpo_status s) {

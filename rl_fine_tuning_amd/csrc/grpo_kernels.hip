@@ -59,7 +59,7 @@ constexpr int kTileBytes = kTile * kRowBytes;    // one operand, one stage: 32 K
 constexpr float kLog2e = 1.4426950408889634f;
 
 // KIND_DH reads W for the dH GEMM transposed on the fly; KIND_DHT (bf16) reads a
-// transposed copy W^T [D, ldt] with the direct-to-LDS loads of the logits GEMMs.
+// fragment-major copy of W^T with direct-to-LDS loads.
 // KIND_LSES (bf16): the LSE epilogue that also keeps the chunk's logits, as d = z - (tile
 // max) in fp16, in the probabilities buffer (the variant without the recompute GEMM).
 // KIND_DW (bf16): dW += Gx^T H_c, A = Q^T transposed from the chunk's fragment-major Q.
@@ -119,7 +119,8 @@ __device__ __forceinline__ float tanh_fast(float a) {
 }
 
 struct GemmArgs {
-  const void* a;      // LSE / PROBS: W [V, D].  DH: W [V, D], read transposed
+  const void* a;      // LSE / PROBS: W [V, D] or its fragment-major copy.  DH: W [V, D], read
+                      // transposed.  DHT: the fragment-major copy of W^T
   const void* b;      // LSE / PROBS: hidden-state chunk [rows, D].  DH: probabilities [rows, ldp]
   int64_t lda, ldb;   // row strides (elements)
   int a_rows;         // rows of the MFMA A operand: V (LSE / PROBS) or D (DH)
@@ -150,7 +151,8 @@ struct GemmArgs {
   float* part;            // [ksplit][b_rows][D] (ksplit > 1)
   int D;
   int ksplit;
-  int b_ks;           // bf16: k steps (ceil(K / 16)) of the fragment-major B copy
+  int b_ks;           // bf16: k steps (ceil(K / 16)) of the fragment-major B copy (and A copy)
+  int a_frag;         // bf16 LSE / PROBS / LSES: A is the fragment-major copy of W
   int p_ks;           // bf16 PROBS: k steps (ceil(V / 16)) of the fragment-major probabilities
 };
 
@@ -393,6 +395,34 @@ struct DmaTileA {
   }
 };
 
+// Fragment-major bf16 A operand (the copies of W and W^T) moved straight into the ring:
+// with the layout [row / 256][k / 16][(row % 256) / 32][lane][8 elements], one ring stage
+// of a 256-row tile (two k steps) is 16 KB of consecutive bytes, so wave w issues kDmaA
+// loads of one contiguous kilobyte each (fragments 4 w .. 4 w + 3 of the stage, k step
+// first), whole cache lines.  The stage in LDS keeps that order: fragment f of k step kk at
+// (8 kk + f) KB, lane l's 16 bytes at 16 l.  The buffer range ends with the tile's last k
+// step, so loads past K read zeros; stages at or past `kend` (the split's end, a multiple
+// of the stage) read zeros too.
+struct DmaFragA {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t lane_off;  // 16 l
+  int w;              // wave index (uniform)
+  __device__ __forceinline__ void init(const void* Af, int ks_count, int tile, int tid) {
+    const int64_t bytes = (int64_t)ks_count * kFA * 1024;
+    rsrc = make_rsrc(reinterpret_cast<const char*>(Af) + (int64_t)tile * bytes, bytes);
+    w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    lane_off = (uint32_t)((tid & 63) * 16);
+  }
+  __device__ __forceinline__ void issue(char* lds_stage, int k0, int kend) const {
+    const uint32_t v = k0 < kend ? lane_off : kOOB;
+    const uint32_t base = (uint32_t)(k0 >> 4) * (kFA * 1024);
+#pragma unroll
+    for (int j = 0; j < kDmaA; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(lds_stage + (kDmaA * w + j) * 1024), 16, v,
+                                               base + (uint32_t)((kDmaA * w + j) * 1024), 0, 0);
+  }
+};
+
 // Transposed A operand of the dH GEMM (W read as W^T): lane (h = lane % 2, q = lane / 2)
 // of wave c loads vocabulary rows 8c + 4h .. + 3 of the stage at hidden columns
 // d0 + 128 p + 4q .. + 3 (p = 0, 1), transposes each 4 x 4 block in registers and
@@ -505,6 +535,13 @@ __device__ __forceinline__ void a_frags(const char* As, int kk, int lane, bf16x8
 #pragma unroll
   for (int f = 0; f < kFA; ++f)
     a[f] = *reinterpret_cast<const bf16x8*>(As + lds_off2(f * 32 + (lane & 31), c));
+}
+
+// The same from a stage filled by DmaFragA: one contiguous kilobyte per fragment.
+__device__ __forceinline__ void a_frags_f(const char* As, int kk, int lane, bf16x8 (&a)[kFA]) {
+#pragma unroll
+  for (int f = 0; f < kFA; ++f)
+    a[f] = *reinterpret_cast<const bf16x8*>(As + (kk * kFA + f) * 1024 + lane * 16);
 }
 
 // This wave's B fragments of one stage (2 k steps x 2 fragments) from the fragment-major
@@ -831,7 +868,7 @@ void gemm_kernel(const GemmArgs g) {
 // The tile body is instantiated per kind of tile, so that the common case (a tile inside
 // the matrix, unsplit K) has straight-line epilogues: kEdge marks the last tile along the
 // vocabulary (LSE / PROBS) or hidden (DH) axis, kSplit a dH tile of a split vocabulary.
-template <int KIND, bool kEdge, bool kSplit, bool kCap>
+template <int KIND, bool kEdge, bool kSplit, bool kCap, bool kFragA>
 __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int ks, int tile_a, int tb) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -857,11 +894,18 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
       reinterpret_cast<const char*>(g.b) + (int64_t)tb * g.b_ks * kFB * 1024 + kFBW * w * 1024 + lane * 16;
   const int ks0 = k_begin >> 4;
   using ATile = typename std::conditional<
-      KIND == KIND_DW, TransTileQ, typename std::conditional<kTrans, TransTileA, DmaTileA>::type>::type;
+      KIND == KIND_DW, TransTileQ,
+      typename std::conditional<kTrans, TransTileA,
+                                typename std::conditional<kFragA, DmaFragA, DmaTileA>::type>::type>::type;
   ATile at;
   if constexpr (KIND == KIND_DW) at.init(g.a, g.p_ks, row_a0, tid);
   else if constexpr (kTrans) at.init(A, g.lda, row_a0, tid);
+  else if constexpr (kFragA) at.init(g.a, g.b_ks, tile_a, tid);
   else at.init(A, g.lda, row_a0, g.a_rows, tid);
+  auto afr = [&](const char* As, int kk, bf16x8 (&a)[kFA]) {
+    if constexpr (kFragA) a_frags_f(As, kk, lane, a);
+    else a_frags(As, kk, lane, a);
+  };
 
   if (nk > 0) {
 #pragma unroll
@@ -881,7 +925,7 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
     __builtin_amdgcn_s_waitcnt(kWaitAll);
     __builtin_amdgcn_s_barrier();
     bf16x8 a0[kFA], a1[kFA];
-    a_frags(smem, 0, lane, a0);
+    afr(smem, 0, a0);
     int slot = 0;
     // loads issued per iteration after A stage kt + 1 (two iterations ago) that may still
     // be in flight when it is waited for: its iteration's B loads and two full iterations
@@ -897,7 +941,7 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
       if constexpr (kTrans) at.load(kf, k_end);
       else at.issue(sf, kf, k_end);
       b_load(Bw, ks0 + 2 * (kt + 3), g.b_ks, nxt);
-      a_frags(sc, 1, lane, a1);
+      afr(sc, 1, a1);
       mma16(a0, cur[0], acc);
       // instruction classes: 0x8 MFMA, 0x20 VMEM read, 0x100 DS read, 0x200 DS write
       if constexpr (kTrans) {
@@ -926,7 +970,7 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
       __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0(kTrans ? 28 : kVmAfterA));
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      a_frags(sn, 0, lane, a0);
+      afr(sn, 0, a0);
       mma16(a1, cur[1], acc);
       if constexpr (kTrans) at.store(sf);
 #pragma unroll
@@ -1143,19 +1187,31 @@ void gemm16_kernel(const GemmArgs g) {
   }
   const bool edge = (tile_a + 1) * kTA > (kDH ? g.D : g.V);
   if constexpr (kDH) {
+    constexpr bool kFrag = KIND == KIND_DHT;
     if (g.ksplit > 1) {
-      if (edge) gemm16_tile<KIND, true, true, false>(g, smem, ks, tile_a, tb);
-      else gemm16_tile<KIND, false, true, false>(g, smem, ks, tile_a, tb);
+      if (edge) gemm16_tile<KIND, true, true, false, kFrag>(g, smem, ks, tile_a, tb);
+      else gemm16_tile<KIND, false, true, false, kFrag>(g, smem, ks, tile_a, tb);
     } else {
-      if (edge) gemm16_tile<KIND, true, false, false>(g, smem, ks, tile_a, tb);
-      else gemm16_tile<KIND, false, false, false>(g, smem, ks, tile_a, tb);
+      if (edge) gemm16_tile<KIND, true, false, false, kFrag>(g, smem, ks, tile_a, tb);
+      else gemm16_tile<KIND, false, false, false, kFrag>(g, smem, ks, tile_a, tb);
+    }
+  } else if constexpr (KIND == KIND_DW) {
+    if (edge) gemm16_tile<KIND, true, false, false, false>(g, smem, ks, tile_a, tb);
+    else gemm16_tile<KIND, false, false, false, false>(g, smem, ks, tile_a, tb);
+  } else if (g.a_frag) {
+    if (g.lm.cap_in > 0.0f) {
+      if (edge) gemm16_tile<KIND, true, false, true, true>(g, smem, ks, tile_a, tb);
+      else gemm16_tile<KIND, false, false, true, true>(g, smem, ks, tile_a, tb);
+    } else {
+      if (edge) gemm16_tile<KIND, true, false, false, true>(g, smem, ks, tile_a, tb);
+      else gemm16_tile<KIND, false, false, false, true>(g, smem, ks, tile_a, tb);
     }
   } else if (g.lm.cap_in > 0.0f) {
-    if (edge) gemm16_tile<KIND, true, false, true>(g, smem, ks, tile_a, tb);
-    else gemm16_tile<KIND, false, false, true>(g, smem, ks, tile_a, tb);
+    if (edge) gemm16_tile<KIND, true, false, true, false>(g, smem, ks, tile_a, tb);
+    else gemm16_tile<KIND, false, false, true, false>(g, smem, ks, tile_a, tb);
   } else {
-    if (edge) gemm16_tile<KIND, true, false, false>(g, smem, ks, tile_a, tb);
-    else gemm16_tile<KIND, false, false, false>(g, smem, ks, tile_a, tb);
+    if (edge) gemm16_tile<KIND, true, false, false, false>(g, smem, ks, tile_a, tb);
+    else gemm16_tile<KIND, false, false, false, false>(g, smem, ks, tile_a, tb);
   }
 }
 
@@ -1178,21 +1234,23 @@ __global__ __launch_bounds__(256) void frag_copy_kernel(const __bf16* __restrict
   out[u] = v;
 }
 
-// W^T [D, ldt] from W [V, D] (bf16), zeros in columns V .. ldt - 1: each thread moves an
-// 8 x 8 block (8 vocabulary rows x 8 hidden columns), transposed in registers.  Lane
-// l = 8 bv + bd of a wave covers vocabulary rows 8 bv .. and hidden columns 8 bd .. of
-// the wave's 64 x 64 block, so the reads (lanes along d) and the writes (lanes along v)
-// both move 128 contiguous bytes per 8 lanes.
-__global__ __launch_bounds__(256) void transpose_w_kernel(const __bf16* __restrict__ W, int V, int D, int ldt,
-                                                          __bf16* __restrict__ WT) {
+// Fragment-major W^T (rows = hidden units, k = vocabulary; ks_v k steps, D rounded up to
+// 256 rows) from W [V, D] (bf16), zeros past V and past D: each thread moves an 8 x 8 block
+// (8 vocabulary rows x 8 hidden columns), transposed in registers.  Lane l = 8 bv + bd of
+// a wave covers vocabulary rows 8 bv .. and hidden columns 8 bd .. of the wave's 64 x 64
+// block: the reads (lanes along d) move 128 contiguous bytes per 8 lanes, and each write
+// is one 16-byte unit of the copy (8 consecutive vocabulary entries of one hidden unit).
+__global__ __launch_bounds__(256) void transpose_w_kernel(const __bf16* __restrict__ W, int V, int D, int ks_v,
+                                                          char* __restrict__ WTf) {
   const int lane = threadIdx.x & 63;
   const int v0 = blockIdx.x * 256 + (threadIdx.x >> 6) * 64 + 8 * (lane >> 3);
   const int d0 = blockIdx.y * 64 + 8 * (lane & 7);
-  if (v0 >= ldt || d0 >= D) return;
+  if (v0 >= 16 * ks_v || d0 >= (D + kTA - 1) / kTA * kTA) return;
   uint4 r[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    r[i] = v0 + i < V ? *reinterpret_cast<const uint4*>(W + (int64_t)(v0 + i) * D + d0) : make_uint4(0, 0, 0, 0);
+    r[i] = v0 + i < V && d0 < D ? *reinterpret_cast<const uint4*>(W + (int64_t)(v0 + i) * D + d0)
+                                : make_uint4(0, 0, 0, 0);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     uint32_t o[4];
@@ -1201,7 +1259,7 @@ __global__ __launch_bounds__(256) void transpose_w_kernel(const __bf16* __restri
       const uint32_t a = u4get(r[2 * m], j >> 1), b = u4get(r[2 * m + 1], j >> 1);
       o[m] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
     }
-    *reinterpret_cast<uint4*>(WT + (int64_t)(d0 + j) * ldt + v0) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(WTf + frag_off(d0 + j, v0, ks_v)) = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 
@@ -1644,12 +1702,50 @@ inline void enqueue_frag_copy(Launcher& L, const Plan& p, const __bf16* Hc, int 
   });
 }
 
-// Arguments shared by the two logits GEMMs of a chunk (W rows x tokens, K = D).
+// The plan's fragment-major copies of W, made once per call (bf16): W^T for the dH GEMM
+// (else it transposes W tiles in registers) and W for the logits GEMMs (else they read W
+// row-major).
 template <typename T>
-GemmArgs logits_args(const Plan& p, const T* W, const T* Hc, const char* Hf, int rows, const LogitMap& lm) {
+struct WCopies {
+  const T* WT = nullptr;
+  const char* Wf = nullptr;
+};
+
+template <typename T>
+WCopies<T> prepare_w(Launcher& L, const Plan& p, const T* W, char* ws) {
+  WCopies<T> c;
+  if constexpr (sizeof(T) == 2) {
+    if (p.T == 0) return c;
+    if (p.use_wt) {
+      c.WT = reinterpret_cast<const T*>(ws + p.off_WT);
+      L.run(GRPO_K_TRANSPOSE_W, [&] {
+        hipLaunchKernelGGL(transpose_w_kernel, dim3(grid1(16 * p.ks_v, 256), grid1(cdiv(p.D, kTileA16) * kTileA16, 64)),
+                           dim3(256), 0, L.stream, reinterpret_cast<const __bf16*>(W), (int)p.V, (int)p.D,
+                           (int)p.ks_v, ws + p.off_WT);
+      });
+    }
+    if (p.use_wf) {
+      c.Wf = ws + p.off_Wf;
+      const int64_t units = p.ntiles_v * p.ks_d * kFB * 64;
+      L.run(GRPO_K_W_COPY, [&] {
+        hipLaunchKernelGGL(frag_copy_kernel, dim3(grid1(units, 256)), dim3(256), 0, L.stream,
+                           reinterpret_cast<const __bf16*>(W), (int)p.V, (int)p.D, (int)p.ks_d, units,
+                           reinterpret_cast<uint4*>(ws + p.off_Wf));
+      });
+    }
+  }
+  return c;
+}
+
+// Arguments shared by the two logits GEMMs of a chunk (W rows x tokens, K = D); Wf is the
+// fragment-major copy of W or nullptr.
+template <typename T>
+GemmArgs logits_args(const Plan& p, const T* W, const char* Wf, const T* Hc, const char* Hf, int rows,
+                     const LogitMap& lm) {
   GemmArgs g = {};
   const bool bf16 = sizeof(T) == 2;
-  g.a = W;
+  g.a = Wf ? static_cast<const void*>(Wf) : static_cast<const void*>(W);
+  g.a_frag = Wf != nullptr;
   g.b = bf16 ? static_cast<const void*>(Hf) : static_cast<const void*>(Hc);
   g.lda = p.D;
   g.ldb = p.D;
@@ -1684,11 +1780,12 @@ grpo_status logp_impl(const Plan& p, const grpo_shape* shape, const T* H, const 
     hipLaunchKernelGGL((target_logit_kernel<T>), dim3(grid1(p.T, 4)), dim3(256), 0, L.stream, H, W, targets,
                        (int)p.T, (int)p.D, (int)p.V, lm, zy);
   });
+  const WCopies<T> wc = prepare_w<T>(L, p, W, ws);
   for (int64_t k = 0; k < p.nchunks; ++k) {
     const int64_t t0 = k * p.C;
     const int rows = (int)(p.T - t0 < p.C ? p.T - t0 : p.C);
     if constexpr (sizeof(T) == 2) enqueue_frag_copy(L, p, H + t0 * p.D, rows, Hf);
-    GemmArgs g = logits_args<T>(p, W, H + t0 * p.D, Hf, rows, lm);
+    GemmArgs g = logits_args<T>(p, W, wc.Wf, H + t0 * p.D, Hf, rows, lm);
     g.pm = pm;
     g.ps = ps;
     launch_gemm<T, KIND_LSE>(L, GRPO_K_LOGITS_LSE, g);
@@ -1708,118 +1805,122 @@ grpo_status logp_impl(const Plan& p, const grpo_shape* shape, const T* H, const 
   return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_E_HIP;
 }
 
-// Backward of one chunk: the softmax probabilities (recomputed by the PROBS GEMM from the
-// forward's log-sum-exp, unless P already holds them), then dH = g (z'_y W[y] - P' W)
-// (dH GEMM, split over the vocabulary when the chunk is too small to fill the GPU).  Hf
-// holds the chunk's fragment-major hidden states (bf16).
+// Backward of one chunk, over slices of at most p.bwd_rows tokens (the plan's size of the
+// probability buffer): the softmax probabilities (recomputed by the PROBS GEMM from the
+// forward's log-sum-exp, unless P already holds the whole chunk's), then
+// dH = g (z'_y W[y] - P' W) (dH GEMM, split over the vocabulary when the slice is too small
+// to fill the GPU) and, if requested, dW (+)= Gx^T H.  Hf holds the chunk's fragment-major
+// hidden states (bf16).
 template <typename T>
-void backward_chunk(Launcher& L, const Plan& p, const T* W, const T* WT, bool use_wt, const T* Hc, char* Hf,
-                    int rows, int64_t k, const float* lse_c, const float* g_c, const int32_t* targets_c, T* dH_c,
-                    T* P, float* part, const LogitMap& lm, const float* zy_c, bool probs_ready, float* dW) {
-  if (!probs_ready) {
-    GemmArgs gp = logits_args<T>(p, W, Hc, Hf, rows, lm);
-    gp.lse = lse_c;
-    gp.p = P;
-    gp.ldp = p.ldp;
-    gp.g = g_c;
-    gp.targets = targets_c;
-    gp.zy = zy_c;
-    launch_gemm<T, KIND_PROBS>(L, GRPO_K_PROBS, gp);
-  }
-
-  L.run(GRPO_K_ONEHOT_FIX, [&] {
-    hipLaunchKernelGGL((onehot_fix_kernel<T>), dim3(grid1(rows, 256)), dim3(256), 0, L.stream, P, rows,
-                       (int)p.ks_v, p.ldp, targets_c, zy_c, lse_c, (int)p.V, lm);
-  });
-
-  // dH^T tiles: hidden x tokens, K = vocabulary, split over the vocabulary if needed.
-  const int ks_plan = (k == p.nchunks - 1) ? p.ksplit_tail : p.ksplit_full;
-  const int k_len = (int)(cdiv(cdiv(p.V, ks_plan), p.bk) * p.bk);
-  const int ksplit = (int)cdiv(p.V, k_len);
-  GemmArgs gd = {};
-  gd.a = use_wt ? WT : W;
-  gd.b = P;
-  gd.lda = use_wt ? p.ldt : p.D;
-  gd.ldb = p.ldp;
-  gd.a_rows = (int)p.D;
-  gd.b_rows = rows;
-  gd.K = (int)p.V;
-  gd.k_len = k_len;
+void backward_chunk(Launcher& L, const Plan& p, const T* W, const WCopies<T>& wc, const T* Hc, char* Hf, int rows,
+                    int64_t k, const float* lse_c, const float* g_c, const int32_t* targets_c, T* dH_c, T* P,
+                    float* part, const LogitMap& lm, const float* zy_c, bool probs_ready, float* dW) {
   const bool bf16 = sizeof(T) == 2;
-  gd.tiles_a_base = (int)cdiv(p.D, bf16 ? kTileA16 : kTile);
-  gd.tiles_a = gd.tiles_a_base * ksplit;
-  gd.tiles_b = (int)cdiv(rows, bf16 ? kTileB16 : kTile);
-  gd.xcd_axis = 1;
-  gd.group_b = bf16 ? 4 : 2;  // 8 W^T tiles x 4 token tiles per XCD round (bf16)
-  gd.b_ks = (int)p.ks_v;
-  gd.lm = lm;
-  gd.zy = zy_c;
-  gd.g = g_c;
-  gd.targets = targets_c;
-  gd.w = W;
-  gd.dh = dH_c;
-  gd.part = part;
-  gd.V = (int)p.V;
-  gd.D = (int)p.D;
-  gd.ksplit = ksplit;
-  if (use_wt) launch_gemm<T, KIND_DHT>(L, GRPO_K_DH_GEMM, gd);
-  else launch_gemm<T, KIND_DH>(L, GRPO_K_DH_GEMM, gd);
-  if (ksplit > 1) {
-    L.run(GRPO_K_DH_REDUCE, [&] {
-      hipLaunchKernelGGL((dh_reduce_kernel<T>), dim3(grid1((int64_t)rows * (p.D / 4), 256)), dim3(256), 0,
-                         L.stream, part, ksplit, rows, (int)p.D, (int)p.V, lm.dscale, g_c, targets_c, dH_c);
+  const int srows = (int)(p.bwd_rows < rows ? p.bwd_rows : rows);
+  for (int r0 = 0; r0 < rows; r0 += srows) {
+    const int sr = rows - r0 < srows ? rows - r0 : srows;
+    const float* lse_s = lse_c + r0;
+    const float* g_s = g_c + r0;
+    const int32_t* targets_s = targets_c + r0;
+    const float* zy_s = zy_c + r0;
+    const T* Hs = Hc + (int64_t)r0 * p.D;
+    T* dH_s = dH_c + (int64_t)r0 * p.D;
+    if (!probs_ready) {
+      const char* Hf_s = Hf;
+      if constexpr (sizeof(T) == 2) {
+        // the previous slice's dW operand replaced the chunk's hidden-state copy
+        if (dW && r0 > 0) enqueue_frag_copy(L, p, Hc, rows, Hf);
+        Hf_s = Hf + (int64_t)(r0 / kTileB16) * p.ks_d * kFB * 1024;
+      }
+      GemmArgs gp = logits_args<T>(p, W, wc.Wf, Hs, Hf_s, sr, lm);
+      gp.lse = lse_s;
+      gp.p = P;
+      gp.ldp = p.ldp;
+      gp.g = g_s;
+      gp.targets = targets_s;
+      gp.zy = zy_s;
+      launch_gemm<T, KIND_PROBS>(L, GRPO_K_PROBS, gp);
+    }
+
+    L.run(GRPO_K_ONEHOT_FIX, [&] {
+      hipLaunchKernelGGL((onehot_fix_kernel<T>), dim3(grid1(sr, 256)), dim3(256), 0, L.stream, P, sr, (int)p.ks_v,
+                         p.ldp, targets_s, zy_s, lse_s, (int)p.V, lm);
     });
-  }
-  if constexpr (sizeof(T) == 2) {
-    if (dW) {
-      // dW (+)= Gx^T H_c: the tokens' operand (-c H_c)^T replaces the chunk's hidden-state
-      // copy (no longer needed once the recompute GEMM has run), then the dW GEMM with the
-      // vocabulary as rows, the hidden units as columns and the chunk's tokens as K.
-      const int ks_t = (int)(p.rows_pad / 16);
-      const int64_t units = cdiv(p.D, kTileB16) * ks_t * kFB * 64;
-      L.run(GRPO_K_HT_COPY, [&] {
-        hipLaunchKernelGGL(ht_copy_kernel, dim3(grid1(units, 256)), dim3(256), 0, L.stream,
-                           reinterpret_cast<const __bf16*>(Hc), rows, (int)p.D, ks_t, units, g_c, targets_c,
-                           (int)p.V, lm.dscale, reinterpret_cast<uint4*>(Hf));
+
+    // dH^T tiles: hidden x tokens, K = vocabulary, split over the vocabulary if needed.
+    const int ks_plan = dh_ksplit(sr, p.D, p.V, p.dtype);
+    const int k_len = (int)(cdiv(cdiv(p.V, ks_plan), p.bk) * p.bk);
+    const int ksplit = (int)cdiv(p.V, k_len);
+    GemmArgs gd = {};
+    gd.a = wc.WT ? static_cast<const void*>(wc.WT) : static_cast<const void*>(W);
+    gd.b = P;
+    gd.lda = p.D;
+    gd.ldb = p.ldp;
+    gd.a_rows = (int)p.D;
+    gd.b_rows = sr;
+    gd.K = (int)p.V;
+    gd.k_len = k_len;
+    gd.tiles_a_base = (int)cdiv(p.D, bf16 ? kTileA16 : kTile);
+    gd.tiles_a = gd.tiles_a_base * ksplit;
+    gd.tiles_b = (int)cdiv(sr, bf16 ? kTileB16 : kTile);
+    gd.xcd_axis = 1;
+    gd.group_b = bf16 ? 4 : 2;  // 8 W^T tiles x 4 token tiles per XCD round (bf16)
+    gd.b_ks = (int)p.ks_v;
+    gd.lm = lm;
+    gd.zy = zy_s;
+    gd.g = g_s;
+    gd.targets = targets_s;
+    gd.w = W;
+    gd.dh = dH_s;
+    gd.part = part;
+    gd.V = (int)p.V;
+    gd.D = (int)p.D;
+    gd.ksplit = ksplit;
+    if (wc.WT) launch_gemm<T, KIND_DHT>(L, GRPO_K_DH_GEMM, gd);
+    else launch_gemm<T, KIND_DH>(L, GRPO_K_DH_GEMM, gd);
+    if (ksplit > 1) {
+      L.run(GRPO_K_DH_REDUCE, [&] {
+        hipLaunchKernelGGL((dh_reduce_kernel<T>), dim3(grid1((int64_t)sr * (p.D / 4), 256)), dim3(256), 0,
+                           L.stream, part, ksplit, sr, (int)p.D, (int)p.V, lm.dscale, g_s, targets_s, dH_s);
       });
-      GemmArgs gw = {};
-      gw.a = P;
-      gw.b = Hf;
-      gw.a_rows = (int)p.V;
-      gw.b_rows = (int)p.D;
-      gw.K = rows;
-      gw.k_len = rows;
-      gw.tiles_a_base = (int)p.ntiles_v;
-      gw.tiles_a = (int)p.ntiles_v;
-      gw.tiles_b = (int)cdiv(p.D, kTileB16);
-      gw.xcd_axis = 0;
-      gw.group_b = 4;
-      gw.b_ks = ks_t;
-      gw.p_ks = (int)p.ks_v;
-      gw.V = (int)p.V;
-      gw.D = (int)p.D;
-      gw.ksplit = 1;
-      gw.lm = lm;
-      gw.dw = dW;
-      gw.accumulate = k > 0;
-      launch_gemm<T, KIND_DW>(L, GRPO_K_DW_GEMM, gw);
+    }
+    if constexpr (sizeof(T) == 2) {
+      if (dW) {
+        // dW (+)= Gx^T H: the tokens' operand (-c H)^T of the slice replaces the chunk's
+        // hidden-state copy (no longer needed once the slice's recompute GEMM has run), then
+        // the dW GEMM with the vocabulary as rows, the hidden units as columns and the
+        // slice's tokens as K.
+        const int ks_t = (int)(cdiv(sr, kTileB16) * kTileB16 / 16);
+        const int64_t units = cdiv(p.D, kTileB16) * ks_t * kFB * 64;
+        L.run(GRPO_K_HT_COPY, [&] {
+          hipLaunchKernelGGL(ht_copy_kernel, dim3(grid1(units, 256)), dim3(256), 0, L.stream,
+                             reinterpret_cast<const __bf16*>(Hs), sr, (int)p.D, ks_t, units, g_s, targets_s,
+                             (int)p.V, lm.dscale, reinterpret_cast<uint4*>(Hf));
+        });
+        GemmArgs gw = {};
+        gw.a = P;
+        gw.b = Hf;
+        gw.a_rows = (int)p.V;
+        gw.b_rows = (int)p.D;
+        gw.K = sr;
+        gw.k_len = sr;
+        gw.tiles_a_base = (int)p.ntiles_v;
+        gw.tiles_a = (int)p.ntiles_v;
+        gw.tiles_b = (int)cdiv(p.D, kTileB16);
+        gw.xcd_axis = 0;
+        gw.group_b = 4;
+        gw.b_ks = ks_t;
+        gw.p_ks = (int)p.ks_v;
+        gw.V = (int)p.V;
+        gw.D = (int)p.D;
+        gw.ksplit = 1;
+        gw.lm = lm;
+        gw.dw = dW;
+        gw.accumulate = k > 0 || r0 > 0;
+        launch_gemm<T, KIND_DW>(L, GRPO_K_DW_GEMM, gw);
+      }
     }
   }
-}
-
-// W^T for the dH GEMM, once per call, when the plan has room for it (bf16).
-template <typename T>
-const T* maybe_transpose_w(Launcher& L, const Plan& p, const T* W, char* ws, bool& use_wt) {
-  use_wt = sizeof(T) == 2 && p.use_wt && p.T > 0;
-  const T* WT = reinterpret_cast<const T*>(ws + p.off_WT);
-  if (use_wt) {
-    L.run(GRPO_K_TRANSPOSE_W, [&] {
-      hipLaunchKernelGGL(transpose_w_kernel, dim3(grid1(p.ldt, 256), grid1(p.D, 64)), dim3(256), 0, L.stream,
-                         reinterpret_cast<const __bf16*>(W), (int)p.V, (int)p.D, (int)p.ldt,
-                         reinterpret_cast<__bf16*>(const_cast<T*>(WT)));
-    });
-  }
-  return WT;
 }
 
 // Loss forward + backward.  mode 1: GRPO objective; mode 2: cross-entropy (prm, old_logp,
@@ -1864,22 +1965,20 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, int mode, const gr
     hipLaunchKernelGGL(seq_count_kernel, dim3(S), dim3(256), 0, L.stream, cu, mask, cnt);
     hipLaunchKernelGGL(seq_weight_kernel, dim3(1), dim3(256), 0, L.stream, cnt, S, agg, wseq);
   });
-  bool use_wt = false;
-  const T* WT = nullptr;
   if (p.T > 0) {
     L.run(GRPO_K_TARGET_LOGIT, [&] {
       hipLaunchKernelGGL((target_logit_kernel<T>), dim3(grid1(p.T, 4)), dim3(256), 0, L.stream, H, W, targets,
                          (int)p.T, (int)p.D, (int)p.V, lm, zy);
     });
-    WT = maybe_transpose_w<T>(L, p, W, ws, use_wt);
   }
+  const WCopies<T> wc = prepare_w<T>(L, p, W, ws);
   for (int64_t k = 0; k < p.nchunks; ++k) {
     const int64_t t0 = k * p.C;
     const int rows = (int)(p.T - t0 < p.C ? p.T - t0 : p.C);
     const T* Hc = H + t0 * p.D;
     if constexpr (sizeof(T) == 2) enqueue_frag_copy(L, p, Hc, rows, Hf);
     const bool keep = sizeof(T) == 2 && shape->keep_chunk_logits;
-    GemmArgs gl = logits_args<T>(p, W, Hc, Hf, rows, lm);
+    GemmArgs gl = logits_args<T>(p, W, wc.Wf, Hc, Hf, rows, lm);
     gl.pm = pm;
     gl.ps = ps;
     if constexpr (sizeof(T) == 2) {
@@ -1928,7 +2027,7 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, int mode, const gr
                            lm);
       });
     }
-    backward_chunk<T>(L, p, W, WT, use_wt, Hc, Hf, rows, k, lse + t0, gbuf + t0, targets + t0, dH + t0 * p.D, P,
+    backward_chunk<T>(L, p, W, wc, Hc, Hf, rows, k, lse + t0, gbuf + t0, targets + t0, dH + t0 * p.D, P,
                       part, lm, zy + t0, keep, dW);
   }
   if (dW && p.nchunks == 0)  // no tokens: the gradient is 0
@@ -1954,14 +2053,13 @@ grpo_status logp_bwd_impl(const Plan& p, const grpo_shape* shape, const T* H, co
                          (int)p.T, (int)p.D, (int)p.V, lm, zy);
     });
   }
-  bool use_wt = false;
-  const T* WT = p.T > 0 ? maybe_transpose_w<T>(L, p, W, ws, use_wt) : nullptr;
+  const WCopies<T> wc = prepare_w<T>(L, p, W, ws);
   for (int64_t k = 0; k < p.nchunks; ++k) {
     const int64_t t0 = k * p.C;
     const int rows = (int)(p.T - t0 < p.C ? p.T - t0 : p.C);
     const T* Hc = H + t0 * p.D;
     if constexpr (sizeof(T) == 2) enqueue_frag_copy(L, p, Hc, rows, Hf);
-    backward_chunk<T>(L, p, W, WT, use_wt, Hc, Hf, rows, k, lse + t0, grad + t0, targets + t0, dH + t0 * p.D, P,
+    backward_chunk<T>(L, p, W, wc, Hc, Hf, rows, k, lse + t0, grad + t0, targets + t0, dH + t0 * p.D, P,
                       part, lm, zy + t0, false, dW);
   }
   return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_E_HIP;
@@ -2029,7 +2127,7 @@ grpo_status grpo_loss_fwd_bwd(const grpo_shape* shape, const grpo_loss_params* p
   if (!aligned16(H) || !aligned16(W) || !aligned16(dH)) return GRPO_E_UNSUPPORTED;
   if (dW && shape->dtype != GRPO_BF16) return GRPO_E_UNSUPPORTED;
   Plan p;
-  st = make_plan(shape, num_seqs, true, &p);
+  st = make_plan(shape, num_seqs, true, &p, dW != nullptr);
   if (st != GRPO_OK) return st;
   if (!ws_ok(p, workspace, workspace_bytes)) return GRPO_E_WORKSPACE;
   (void)hipGetLastError();
@@ -2047,7 +2145,7 @@ grpo_status grpo_logp_bwd(const grpo_shape* shape, const void* H, const void* W,
                           const float* lse, const float* grad_logp, void* dH, float* dW, void* workspace,
                           size_t workspace_bytes, void* stream, grpo_timer* timer) {
   Plan p;
-  grpo_status st = make_plan(shape, 1, true, &p);
+  grpo_status st = make_plan(shape, 1, true, &p, dW != nullptr);
   if (st != GRPO_OK) return st;
   if (!W) return GRPO_E_NULL;
   if (p.T > 0 && (!H || !targets || !lse || !grad_logp || !dH)) return GRPO_E_NULL;
@@ -2074,7 +2172,7 @@ grpo_status grpo_ce_loss_fwd_bwd(const grpo_shape* shape, const void* H, const v
                                  float* dW, void* workspace, size_t workspace_bytes, void* stream,
                                  grpo_timer* timer) {
   Plan p;
-  grpo_status st = make_plan(shape, 1, true, &p);
+  grpo_status st = make_plan(shape, 1, true, &p, dW != nullptr);
   if (st != GRPO_OK) return st;
   if (!loss || !W) return GRPO_E_NULL;
   if (p.T > 0 && (!H || !targets || !dH)) return GRPO_E_NULL;

@@ -33,17 +33,16 @@ struct Plan {
   int esize = 0, bk = 0;
   int64_t ntiles_v = 0;   // vocabulary tiles = (max, sum-exp) partials per token
   int64_t ldp = 0;        // fp32: row stride (elements) of the chunk probability matrix
-  int64_t rows_pad = 0;   // bf16: chunk rows rounded up to the 512-row tile
+  int64_t rows_pad = 0;   // bf16: chunk rows rounded up to the 256-row tile
   int64_t ks_d = 0;       // bf16: k steps of 16 over D (fragment-major hidden states)
   int64_t ks_v = 0;       // bf16: k steps of 16 over V (fragment-major probabilities)
-  int64_t ldt = 0;        // bf16: row stride of the transposed W copy (V rounded up to 8)
-  bool use_wt = false;    // bf16: the dH GEMM reads W^T from the workspace
-  int ksplit_full = 1;    // dH vocabulary split for a full chunk
-  int ksplit_tail = 1;    // ... and for the last, shorter chunk
+  bool use_wt = false;    // bf16: the dH GEMM reads a fragment-major W^T from the workspace
+  bool use_wf = false;    // bf16: the logits GEMMs read a fragment-major W from the workspace
+  int64_t bwd_rows = 0;   // tokens per backward slice (bf16: a multiple of 256; >= C when unsliced)
   bool backward = false;
   size_t off_zy = 0, off_lse = 0, off_pm = 0, off_ps = 0;
   size_t off_g = 0, off_wl = 0, off_seq = 0, off_cu = 0, off_cnt = 0, off_wseq = 0;
-  size_t off_P = 0, off_part = 0, off_Hf = 0, off_WT = 0;
+  size_t off_P = 0, off_part = 0, off_Hf = 0, off_WT = 0, off_Wf = 0;
   size_t total = 0;
 };
 
@@ -56,10 +55,13 @@ struct LogitMap {
 };
 LogitMap make_logit_map(const grpo_shape* s);  // s already validated
 
+// Vocabulary split of the dH GEMM for a backward slice of `rows` tokens.
+int dh_ksplit(int64_t rows, int64_t D, int64_t V, int32_t dtype);
+
 grpo_status validate_shape(const grpo_shape* s);
 grpo_status validate_loss_params(const grpo_loss_params* p);
 grpo_status validate_cu(const int32_t* cu, int64_t S, int64_t T);
-grpo_status make_plan(const grpo_shape* s, int64_t S, bool backward, Plan* out);
+grpo_status make_plan(const grpo_shape* s, int64_t S, bool backward, Plan* out, bool dW = false);
 int dh_ksplit(int64_t chunk_rows, int64_t D, int64_t V, int32_t dtype);
 bool aligned16(const void* p);
 

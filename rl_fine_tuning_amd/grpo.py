@@ -19,7 +19,7 @@ GRPO_AGG = {"seq_mean": 0, "token_mean": 1}
 GRPO_STD = {"unbiased": 0, "population": 1}
 KERNELS = ["target_logit", "logits_lse", "merge", "probs", "dh_gemm", "dh_reduce", "token_index",
            "loss_finalize", "advantages", "frag_copy", "transpose_w", "probs_kept", "onehot_fix", "ht_copy",
-           "dw_gemm"]
+           "dw_gemm", "w_copy"]
 KERNEL_ID = {k: i for i, k in enumerate(KERNELS)}
 
 
@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
         sp = ctypes.POINTER(GrpoShape)
         L.grpo_workspace_bytes.argtypes = [sp, i64, ctypes.c_int]
         L.grpo_workspace_bytes.restype = sz
+        L.grpo_plan_info.argtypes = [sp, i64, ctypes.c_int, ctypes.POINTER(i64)]
+        L.grpo_plan_info.restype = ctypes.c_int
         L.grpo_logp_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
         L.grpo_logp_fwd.restype = ctypes.c_int
         L.grpo_advantages.argtypes = [vp, i64, i64, i32, f32, vp, vp]
@@ -125,11 +127,29 @@ def make_shape(T, D, V, chunk_tokens, dtype, temperature=1.0, logit_scale_multip
                      int(bool(keep_chunk_logits)))
 
 
+def _bwd_mode(with_backward, with_dW):
+    return 2 if with_dW else int(bool(with_backward))
+
+
 def grpo_workspace_bytes(T, D, V, chunk_tokens, dtype=GRPO_BF16, temperature=1.0, num_seqs=1,
-                         with_backward=True, logit_softcapping=0.0, keep_chunk_logits=False) -> int:
+                         with_backward=True, logit_softcapping=0.0, keep_chunk_logits=False,
+                         with_dW=False) -> int:
     shape = make_shape(T, D, V, chunk_tokens, dtype, temperature, logit_softcapping=logit_softcapping,
                        keep_chunk_logits=keep_chunk_logits)
-    return int(lib().grpo_workspace_bytes(ctypes.byref(shape), int(num_seqs), int(bool(with_backward))))
+    return int(lib().grpo_workspace_bytes(ctypes.byref(shape), int(num_seqs), _bwd_mode(with_backward, with_dW)))
+
+
+def grpo_plan_info(T, D, V, chunk_tokens, dtype=GRPO_BF16, temperature=1.0, num_seqs=1, with_backward=True,
+                   logit_softcapping=0.0, keep_chunk_logits=False, with_dW=False) -> dict:
+    """The library's workspace layout for a call: which fragment-major copies of W it keeps,
+    the tokens per backward slice and the workspace bytes."""
+    shape = make_shape(T, D, V, chunk_tokens, dtype, temperature, logit_softcapping=logit_softcapping,
+                       keep_chunk_logits=keep_chunk_logits)
+    info = (ctypes.c_int64 * 4)()
+    st = lib().grpo_plan_info(ctypes.byref(shape), int(num_seqs), _bwd_mode(with_backward, with_dW), info)
+    _check(st, "grpo_plan_info")
+    return dict(w_transposed_copy=bool(info[0]), w_copy=bool(info[1]), backward_slice_tokens=int(info[2]),
+                workspace_bytes=int(info[3]))
 
 
 def _workspace(nbytes, workspace, device):
@@ -204,7 +224,7 @@ def grpo_logp_bwd(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: 
     V = W.shape[0]
     shape = make_shape(T, D, V, chunk_tokens, _dtype_code(H), temperature, logit_scale_multiply,
                        logit_scale_divide, logit_softcapping)
-    nbytes = int(lib().grpo_workspace_bytes(ctypes.byref(shape), 1, 1))
+    nbytes = int(lib().grpo_workspace_bytes(ctypes.byref(shape), 1, 2 if dW is not None and dW is not False else 1))
     ws, wsn = _workspace(nbytes, workspace, H.device)
     if dH is None:
         dH = torch.empty_like(H)
@@ -232,7 +252,7 @@ def grpo_ce_loss_fwd_bwd(H, W, targets, chunk_tokens, *, temperature=1.0, logit_
     V = W.shape[0]
     shape = make_shape(T, D, V, chunk_tokens, _dtype_code(H), temperature, logit_scale_multiply,
                        logit_scale_divide, logit_softcapping, keep_chunk_logits)
-    nbytes = int(lib().grpo_workspace_bytes(ctypes.byref(shape), 1, 1))
+    nbytes = int(lib().grpo_workspace_bytes(ctypes.byref(shape), 1, 2 if dW is not None and dW is not False else 1))
     ws, wsn = _workspace(nbytes, workspace, H.device)
     dev = H.device
     loss = torch.empty(1, dtype=torch.float64, device=dev)
@@ -243,7 +263,7 @@ def grpo_ce_loss_fwd_bwd(H, W, targets, chunk_tokens, *, temperature=1.0, logit_
     if dW is True:
         dW = torch.empty(V, D, dtype=torch.float32, device=dev)
     st = lib().grpo_ce_loss_fwd_bwd(ctypes.byref(shape), _ptr(H), _ptr(W), _ptr(targets), _ptr(mask), _ptr(loss),
-                                    _ptr(logp), _ptr(tl), _ptr(dH), _ptr(dW) if dW is not None else None, _ptr(ws),
+                                    _ptr(logp), _ptr(tl), _ptr(dH), _ptr(dW) if dW is not None and dW is not False else None, _ptr(ws),
                                     wsn, _stream(stream), timer.handle if timer else None)
     _check(st, "grpo_ce_loss_fwd_bwd")
     return dict(loss=loss, logp=logp, token_loss=tl, dH=dH, dW=dW)
@@ -278,7 +298,7 @@ def grpo_loss_fwd_bwd(H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk_
     shape = make_shape(T, D, V, chunk_tokens, _dtype_code(H), temperature, logit_scale_multiply,
                        logit_scale_divide, logit_softcapping, keep_chunk_logits)
     params = GrpoLossParams(float(clip_eps_low), float(clip_eps_high), float(beta), GRPO_AGG[agg])
-    nbytes = int(lib().grpo_workspace_bytes(ctypes.byref(shape), S, 1))
+    nbytes = int(lib().grpo_workspace_bytes(ctypes.byref(shape), S, 2 if dW is not None and dW is not False else 1))
     ws, wsn = _workspace(nbytes, workspace, H.device)
     dev = H.device
     loss = torch.empty(1, dtype=torch.float64, device=dev)
@@ -291,7 +311,7 @@ def grpo_loss_fwd_bwd(H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk_
     st = lib().grpo_loss_fwd_bwd(ctypes.byref(shape), ctypes.byref(params), _ptr(H), _ptr(W), _ptr(targets),
                                  ctypes.c_void_p(cu.data_ptr()), S, _ptr(mask), _ptr(old_logp), _ptr(ref_logp),
                                  _ptr(adv), _ptr(loss), _ptr(logp), _ptr(tl), _ptr(dH),
-                                 _ptr(dW) if dW is not None else None, _ptr(ws), wsn, _stream(stream),
+                                 _ptr(dW) if dW is not None and dW is not False else None, _ptr(ws), wsn, _stream(stream),
                                  timer.handle if timer else None)
     _check(st, "grpo_loss_fwd_bwd")
     return dict(loss=loss, logp=logp, token_loss=tl, dH=dH, dW=dW)

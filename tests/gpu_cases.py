@@ -19,6 +19,17 @@ LOSS_RTOL = 1e-4
 DH_REL_L2 = 1e-2
 
 
+def backward_passes(T, D, V, chunk, num_seqs=1, dtype=0, keep=False, dW=False):
+    """Backward passes (PROBS / dH launches) of a call: each chunk's tokens in slices of the
+    plan's size, and the plan itself."""
+    from rl_fine_tuning_amd import grpo_plan_info
+    info = grpo_plan_info(T, D, V, chunk, dtype=dtype, num_seqs=num_seqs, keep_chunk_logits=keep, with_dW=dW)
+    C = min(chunk, T)
+    s = info["backward_slice_tokens"]
+    n = sum(-(-min(C, T - t0) // s) for t0 in range(0, T, C)) if T > 0 else 0
+    return n, info
+
+
 def say(msg):
     print(f"[gpu-case] {msg}", flush=True)
     sys.stdout.flush()

@@ -55,6 +55,43 @@ def test_workspace_bound_one_chunk_of_logits():
     assert B.grpo_workspace_bytes(10, 63, 512, 32) == 0  # D not a multiple of 8 for bf16
 
 
+def test_plan_layouts():
+    # The layout grpo_workspace_bytes sizes: the largest of (both fragment-major copies of W,
+    # whole-chunk backward), (both copies, backward in two token slices; not with kept
+    # logits), (W^T only), (neither) that stays within one chunk's fp32 logits.
+    info = B.grpo_plan_info(110000, 4096, 151936, 8192, num_seqs=2)       # Qwen3-8B-shaped, 110K
+    assert info["w_transposed_copy"] and info["w_copy"] and info["backward_slice_tokens"] == 4096
+    assert info["workspace_bytes"] == B.grpo_workspace_bytes(110000, 4096, 151936, 8192, num_seqs=2)
+    assert info["workspace_bytes"] <= 8192 * 151936 * 4
+    # with dW the backward takes whole chunks (a slice would read and write the fp32 dW again)
+    info = B.grpo_plan_info(110000, 4096, 151936, 8192, num_seqs=2, with_dW=True)
+    assert info["w_transposed_copy"] and not info["w_copy"] and info["backward_slice_tokens"] == 8192
+    assert info["workspace_bytes"] <= 8192 * 151936 * 4
+    # with kept logits the chunk's matrix is filled whole in the forward: no slices, W^T only
+    info = B.grpo_plan_info(110000, 4096, 151936, 8192, num_seqs=2, keep_chunk_logits=True)
+    assert info["w_transposed_copy"] and not info["w_copy"] and info["backward_slice_tokens"] == 8192
+    info = B.grpo_plan_info(40960, 1536, 151936, 4096, num_seqs=64)       # both copies, whole chunks
+    assert info["w_transposed_copy"] and info["w_copy"] and info["backward_slice_tokens"] == 4096
+    info = B.grpo_plan_info(20480, 4096, 128256, 2048, num_seqs=4)        # no room for either copy
+    assert not info["w_transposed_copy"] and not info["w_copy"] and info["backward_slice_tokens"] == 2048
+    info = B.grpo_plan_info(380000, 2880, 201088, 8192, num_seqs=4)
+    assert info["w_transposed_copy"] and info["w_copy"] and info["backward_slice_tokens"] == 8192
+    # the forward alone keeps the copy of W when it fits; fp32 inputs keep no copies
+    info = B.grpo_plan_info(110000, 4096, 151936, 8192, with_backward=False)
+    assert info["w_copy"] and not info["w_transposed_copy"] and info["backward_slice_tokens"] == 0
+    info = B.grpo_plan_info(4096, 256, 10000, 1024, dtype=1, num_seqs=2)
+    assert not info["w_copy"] and not info["w_transposed_copy"] and info["backward_slice_tokens"] == 1024
+    for T, D, V, C in [(110000, 4096, 151936, 8192), (1024, 264, 10000, 512), (701, 264, 999, 128)]:
+        for keep in (False, True):
+            for dW in (False, True):
+                i = B.grpo_plan_info(T, D, V, C, num_seqs=2, keep_chunk_logits=keep, with_dW=dW)
+                assert i["backward_slice_tokens"] % 256 == 0 and i["backward_slice_tokens"] > 0
+                if keep or dW:
+                    assert i["backward_slice_tokens"] >= min(T, C)
+    with pytest.raises(B.GrpoError):
+        B.grpo_plan_info(10, 63, 512, 32)
+
+
 def test_logp_fwd_validation():
     lib = B.lib()
     s = shape()
@@ -212,5 +249,6 @@ def test_keep_chunk_logits_validation():
     assert lib.grpo_logp_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, None, ws, 1 << 40, None, None) == 3
     sh = B.make_shape(100, 64, 512, 32, 1, 1.0, keep_chunk_logits=True)  # fp32 inputs: not supported
     assert lib.grpo_logp_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, None, ws, 1 << 40, None, None) == 5
-    assert B.grpo_workspace_bytes(110000, 4096, 151936, 8192, 0, num_seqs=2, keep_chunk_logits=True) == \
-        B.grpo_workspace_bytes(110000, 4096, 151936, 8192, 0, num_seqs=2)  # no extra memory
+    # keeping the logits needs no memory beyond the same bound: one chunk's fp32 logits
+    for (T, D, V, C) in [(110000, 4096, 151936, 8192), (40960, 1536, 151936, 4096), (380000, 2880, 201088, 8192)]:
+        assert 0 < B.grpo_workspace_bytes(T, D, V, C, 0, num_seqs=2, keep_chunk_logits=True) <= C * V * 4

@@ -8,7 +8,7 @@ import torch
 import oracle
 from rl_fine_tuning_amd import Timer, grpo_ce_loss_fwd_bwd, grpo_loss_fwd_bwd
 
-from gpu_cases import DH_REL_L2, case, check_loss_outputs, host_matrix, rel_l2, say, to_device
+from gpu_cases import DH_REL_L2, backward_passes, case, check_loss_outputs, host_matrix, rel_l2, say, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -18,6 +18,8 @@ pytestmark = pytest.mark.gpu
     (264, 999, [700, 1], 128, 1.0, 0.0),              # in-register W^T, ragged tail
     (1024, 32000, [1500, 548], 4096, 1.0, 0.0),       # one chunk, several tiles each way
     (256, 1000, [300, 212], 512, 0.7, 3.0),           # softcap
+    (256, 10000, [1200, 848], 2048, 1.0, 0.0),        # copies of W and W^T (room in one 2048-token chunk)
+    (256, 10000, [1200, 848], 2048, 0.7, 3.0),        # the same with a softcap
 ])
 def test_grpo_loss_keeping_chunk_logits(D, V, lengths, chunk, tau, cap):
     say(f"keep logits D={D} V={V} T={sum(lengths)} chunk={chunk} tau={tau} cap={cap}")
@@ -32,6 +34,9 @@ def test_grpo_loss_keeping_chunk_logits(D, V, lengths, chunk, tau, cap):
     torch.cuda.synchronize()
     nchunks = -(-k["T"] // chunk)
     assert tm.read("probs")[1] == 0 and tm.read("probs_kept")[1] == nchunks
+    npass, info = backward_passes(k["T"], D, V, chunk, num_seqs=len(lengths), keep=True)
+    say(f"  plan {info}")
+    assert npass == nchunks and tm.read("w_copy")[1] == int(info["w_copy"])
     tm.close()
     r = check_loss_outputs(k, kept)
     say(f"  logp err {r['logp_err']:.2e} dH rel {r['dH_rel']:.2e} loss {r['loss']:.6e} vs {r['loss_ref']:.6e}")

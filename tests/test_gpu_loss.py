@@ -8,7 +8,7 @@ import oracle
 from rl_fine_tuning_amd import grpo_logp_fwd, grpo_loss_fwd_bwd
 from synth import make_config
 
-from gpu_cases import case, check_loss_outputs, dev_matrix, f32, say, to_device
+from gpu_cases import backward_passes, case, check_loss_outputs, dev_matrix, f32, say, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -147,6 +147,10 @@ def test_dh_gemm_both_operand_paths(V, chunk, expect_wt):
                             temperature=k["tau"], mask=d["mask"], timer=tm, **prm)
     torch.cuda.synchronize()
     assert tm.read("transpose_w")[1] == expect_wt
+    npass, info = backward_passes(k["T"], 256, V, chunk, num_seqs=3)
+    say(f"  plan {info}, backward passes {npass}")
+    assert tm.read("w_copy")[1] == int(info["w_copy"])
+    assert tm.read("probs")[1] == npass and tm.read("dh_gemm")[1] == npass
     tm.close()
     r = check_loss_outputs(k, got)
     say(f"  logp err {r['logp_err']:.2e} dH rel {r['dH_rel']:.2e}")
