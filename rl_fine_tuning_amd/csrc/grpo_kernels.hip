@@ -129,7 +129,7 @@ struct GemmArgs {
   int k_len;          // DH: vocabulary entries per split; otherwise K
   int tiles_a_base;   // A tiles before the split factor
   int tiles_a, tiles_b;
-  int xcd_axis;       // 0: tiles_a are shared out over XCDs; 1: tiles_b
+  int xcd_a;          // XCD grid: tiles_a in xcd_a ranges, tiles_b in 8 / xcd_a (xcd_a = 1, 2, 4, 8)
   int group_b;        // B tiles walked together
   LogitMap lm;
   // LSE outputs: [tiles_a][b_rows]
@@ -183,17 +183,16 @@ __device__ __forceinline__ TokGrad tok_grad(const float* g, const int32_t* targe
 // share of one tile axis and walks the other axis group_b tiles at a time.
 __device__ __forceinline__ bool map_tile(const GemmArgs& g, int& ta, int& tb) {
   const int bid = blockIdx.x;
-  const int xcd = bid & 7;
+  const int xcd = bid & 7;  // workgroups go to the 8 XCDs in turn
   const int local = bid >> 3;
-  int a_lo = 0, na = g.tiles_a, b_lo = 0, nb = g.tiles_b;
-  if (g.xcd_axis == 0) {
-    a_lo = (int)((int64_t)xcd * g.tiles_a / 8);
-    na = (int)((int64_t)(xcd + 1) * g.tiles_a / 8) - a_lo;
-  } else {
-    b_lo = (int)((int64_t)xcd * g.tiles_b / 8);
-    nb = (int)((int64_t)(xcd + 1) * g.tiles_b / 8) - b_lo;
-  }
+  const int xb_parts = 8 / g.xcd_a;
+  const int xa = xcd % g.xcd_a, xb = xcd / g.xcd_a;
+  const int a_lo = (int)((int64_t)xa * g.tiles_a / g.xcd_a);
+  const int na = (int)((int64_t)(xa + 1) * g.tiles_a / g.xcd_a) - a_lo;
+  const int b_lo = (int)((int64_t)xb * g.tiles_b / xb_parts);
+  const int nb = (int)((int64_t)(xb + 1) * g.tiles_b / xb_parts) - b_lo;
   if (local >= na * nb) return false;
+  // within the XCD: groups of group_b B tiles, each walked with all of the XCD's A tiles
   const int gsz = g.group_b * na;
   const int grp = local / gsz;
   const int r = local - grp * gsz;
@@ -1683,9 +1682,8 @@ inline int grid1(int64_t n, int per) { return (int)((n + per - 1) / per); }
 
 template <typename T, int KIND>
 void launch_gemm(Launcher& L, int kid, const GemmArgs& g) {
-  int per_xcd;
-  if (g.xcd_axis == 0) per_xcd = (int)cdiv(g.tiles_a, 8) * g.tiles_b;
-  else per_xcd = g.tiles_a * (int)cdiv(g.tiles_b, 8);
+  // the largest share of one XCD (the ranges of map_tile differ by at most one tile)
+  const int per_xcd = (int)cdiv(g.tiles_a, g.xcd_a) * (int)cdiv(g.tiles_b, 8 / g.xcd_a);
   const int blocks = 8 * per_xcd;
   if constexpr (sizeof(T) == 2)
     L.run(kid, [&] { hipLaunchKernelGGL((gemm16_kernel<KIND>), dim3(blocks), dim3(kThreads), 0, L.stream, g); });
@@ -1756,7 +1754,7 @@ GemmArgs logits_args(const Plan& p, const T* W, const char* Wf, const T* Hc, con
   g.tiles_a_base = (int)p.ntiles_v;
   g.tiles_a = (int)p.ntiles_v;
   g.tiles_b = (int)cdiv(rows, bf16 ? kTileB16 : kTile);
-  g.xcd_axis = 0;
+  g.xcd_a = 8;  // each XCD a share of the vocabulary tiles
   g.group_b = 8;  // B tiles walked together
   g.lm = lm;
   g.V = (int)p.V;
@@ -1863,8 +1861,13 @@ void backward_chunk(Launcher& L, const Plan& p, const T* W, const WCopies<T>& wc
     gd.tiles_a_base = (int)cdiv(p.D, bf16 ? kTileA16 : kTile);
     gd.tiles_a = gd.tiles_a_base * ksplit;
     gd.tiles_b = (int)cdiv(sr, bf16 ? kTileB16 : kTile);
-    gd.xcd_axis = 1;
     gd.group_b = bf16 ? 4 : 2;  // 8 W^T tiles x 4 token tiles per XCD round (bf16)
+    // XCD grid: each XCD takes at least group_b token tiles where there are enough (a slice of
+    // 16 token tiles: 2 x 4 XCDs, 8 hidden x 4 token tiles each), the hidden tiles split over
+    // the rest, so the 32 workgroups of an XCD share as many operand rows as they can.
+    int xb = 8;
+    while (xb > 1 && gd.tiles_b / xb < gd.group_b) xb >>= 1;
+    gd.xcd_a = 8 / xb;
     gd.b_ks = (int)p.ks_v;
     gd.lm = lm;
     gd.zy = zy_s;
@@ -1907,7 +1910,7 @@ void backward_chunk(Launcher& L, const Plan& p, const T* W, const WCopies<T>& wc
         gw.tiles_a_base = (int)p.ntiles_v;
         gw.tiles_a = (int)p.ntiles_v;
         gw.tiles_b = (int)cdiv(p.D, kTileB16);
-        gw.xcd_axis = 0;
+        gw.xcd_a = 8;
         gw.group_b = 4;
         gw.b_ks = ks_t;
         gw.p_ks = (int)p.ks_v;
