@@ -187,3 +187,34 @@ def test_many_sequences_seq_mean():
     got = run_loss(k, 256)
     torch.cuda.synchronize()
     check_loss_outputs(k, got)
+
+
+def test_sliced_backward_uneven_slices_match_whole_chunks():
+    # chunk 700 -> chunks of 700, 700, 100 tokens; the layout with both copies of W runs the
+    # backward in slices of 512 tokens (512 + 188, 512 + 188, 100), sequence boundaries
+    # inside slices.  Against the oracle, and against one whole-chunk pass: loss, logp and
+    # token_loss bitwise (row-local, the loss summed in a fixed token order); dH to fp32
+    # rounding (the dH GEMM's vocabulary split depends on the slice's token count).
+    from rl_fine_tuning_amd import Timer
+    k = case(53, D=256, V=10000, lengths=[600, 333, 567], G=3, chunk=700, old_std=0.3, ref_std=0.3,
+             mask_frac=0.1, bad_targets=(9,))
+    say("loss sliced backward, chunk 700 (slices 512 + 188) vs chunk 1500 (one pass)")
+    npass, info = backward_passes(k["T"], 256, 10000, 700, num_seqs=3)
+    assert info["backward_slice_tokens"] == 512 and npass == 5
+    d = to_device(k)
+    kw = dict(temperature=k["tau"], mask=d["mask"], **k["prm"])
+    tm = Timer(256)
+    a = grpo_loss_fwd_bwd(d["H"], d["W"], d["targets"], k["c"].cu, d["old"], d["ref"], d["adv"], 700, timer=tm, **kw)
+    torch.cuda.synchronize()
+    assert tm.read("probs")[1] == 5 and tm.read("dh_gemm")[1] == 5 and tm.read("w_copy")[1] == 1
+    tm.close()
+    check_loss_outputs(k, a)
+    whole = backward_passes(k["T"], 256, 10000, 1500, num_seqs=3)[1]
+    assert whole["backward_slice_tokens"] >= 1500
+    b = grpo_loss_fwd_bwd(d["H"], d["W"], d["targets"], k["c"].cu, d["old"], d["ref"], d["adv"], 1500, **kw)
+    torch.cuda.synchronize()
+    for name in ("loss", "logp", "token_loss"):  # bit patterns: the invalid target's logp is NaN
+        bits = torch.int64 if a[name].dtype == torch.float64 else torch.int32
+        assert torch.equal(a[name].view(bits), b[name].view(bits)), name
+    rel = (a["dH"].float() - b["dH"].float()).norm() / b["dH"].float().norm()
+    assert rel.item() <= 1e-3, rel.item()
