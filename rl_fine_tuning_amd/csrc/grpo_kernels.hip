@@ -1814,7 +1814,7 @@ void backward_chunk(Launcher& L, const Plan& p, const T* W, const WCopies<T>& wc
                     int64_t k, const float* lse_c, const float* g_c, const int32_t* targets_c, T* dH_c, T* P,
                     float* part, const LogitMap& lm, const float* zy_c, bool probs_ready, float* dW) {
   const bool bf16 = sizeof(T) == 2;
-  const int srows = (int)(p.bwd_rows < rows ? p.bwd_rows : rows);
+  const int srows = (int)(p.bwd_rows > 0 && p.bwd_rows < rows ? p.bwd_rows : rows);
   for (int r0 = 0; r0 < rows; r0 += srows) {
     const int sr = rows - r0 < srows ? rows - r0 : srows;
     const float* lse_s = lse_c + r0;
