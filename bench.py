@@ -94,6 +94,66 @@ def measured_traffic(kernel, workload_is_profiled):
     return (float(m.group(1)) * ff + float(m.group(2)) * wf) * 1024.0
 
 
+def box_peak():
+    """CU count and max shader clock of the gfx950 agent from rocminfo, and the dense bf16
+    MFMA peak they imply (4096 flop per clock per CU); None where rocminfo is unavailable."""
+    import re
+    import subprocess
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except Exception:
+        return None
+    for agent in out.split("Agent ")[1:]:
+        if "gfx950" not in agent:
+            continue
+        cu = re.search(r"Compute Unit:\s+(\d+)", agent)
+        clk = re.search(r"Max Clock Freq\. \(MHz\):\s+(\d+)", agent)
+        if cu and clk:
+            cus, mhz = int(cu.group(1)), int(clk.group(1))
+            return {"compute_units": cus, "max_sclk_mhz": mhz, "bf16_dense_tflops": cus * mhz * 1e6 * 4096 / 1e12}
+    return None
+
+
+class ClockSampler:
+    """Samples the shader clock (rocm-smi) and the socket power (amd-smi) from a helper
+    thread, each read in a child process, while the timed steps run."""
+
+    def __init__(self):
+        import threading
+        self.sclk, self.power = [], []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        import re
+        import subprocess
+        while not self._stop.is_set():
+            try:
+                out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=10).stdout
+                m = re.search(r"sclk clock level: \d+: \((\d+)Mhz\)", out)
+                if m and not self._stop.is_set():
+                    self.sclk.append(int(m.group(1)))
+                out = subprocess.run(["amd-smi", "metric", "-p"], capture_output=True, text=True, timeout=10).stdout
+                m = re.search(r"SOCKET_POWER:\s+(\d+)\s*W", out)
+                if m and not self._stop.is_set():
+                    self.power.append(int(m.group(1)))
+            except Exception:
+                return
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join(timeout=30)
+
+    def summary(self):
+        avg = lambda v: sum(v) / len(v) if v else None
+        return {"sclk_mhz_avg": avg(self.sclk), "sclk_samples": len(self.sclk),
+                "socket_power_w_avg": avg(self.power), "power_samples": len(self.power)}
+
+
 def cpu_baseline(case, n_tokens):
     """The fp64 oracle, as it stands, on the first n_tokens tokens of the workload."""
     import numpy as np
@@ -115,9 +175,24 @@ def cpu_baseline(case, n_tokens):
     t0 = time.perf_counter()
     oracle.grpo_loss_and_grad(H, W, y, cu, np.ones(n, np.uint8), old, ref, adv)
     dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"first {n} tokens of the workload, full fwd+bwd (logp, loss, dH) in fp64 numpy; "
-                      f"{dt:.1f} s"}
+    res = {"value": n / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+           "sample": f"first {n} tokens of the workload, full fwd+bwd (logp, loss, dH) in fp64 numpy; "
+                     f"{dt:.1f} s"}
+    # the same on one thread, on a smaller sample
+    n1 = min(64, n)
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            oracle.grpo_loss_and_grad(H[:n1], W, y[:n1], np.array([0, n1], dtype=np.int64), np.ones(n1, np.uint8),
+                                      old[:n1], ref[:n1], adv)
+            dt1 = time.perf_counter() - t0
+        res["value_1thread"] = n1 / dt1
+        res["sample_1thread"] = f"first {n1} tokens, one BLAS thread; {dt1:.1f} s"
+    except Exception as e:  # threadpoolctl missing: no one-thread figure
+        res["value_1thread"] = None
+        res["sample_1thread"] = f"not measured ({type(e).__name__})"
+    return res
 
 
 def main():
@@ -179,12 +254,18 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
     timer = Timer(16384)
+    peak_box = box_peak()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        out = step(timer)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    with ClockSampler() as clocks:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            evs[i].record()
+            out = step(timer)
+        evs[args.steps].record()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     log(f"timed {args.steps} steps in {elapsed:.3f} s")
     peak_extra = torch.cuda.max_memory_allocated() - base_mem
     loss = float(out["loss"].cpu()[0])
@@ -208,6 +289,24 @@ def main():
     for k in gemm_flops:
         kk = kernels[k]
         kk["tflops"] = gemm_flops[k] * args.steps / (kk["ms_total"] * 1e-3) / 1e12 if kk["ms_total"] else None
+    # the streaming kernels: algorithmic bytes per step (read + written) over their event time
+    ntv, ks_d, ks_v = -(-V // 256), -(-D // 16), -(-V // 16)
+    esz = 2 if case.dtype == "bf16" else 4
+    stream_bytes = {
+        # per token: the (max, sum-exp) partials of every vocabulary tile, zy / old / ref / advantage /
+        # sequence weight read, lse / g / weighted loss written
+        "merge": T * (8 * ntv + 44),
+        "target_logit": T * (2 * D * esz + 8),             # the token's row of H and W[y]
+        "frag_copy": sum(r * D * esz + -(-r // 256) * 256 * ks_d * 32 for r in rows),
+        "w_copy": V * D * esz + ntv * 256 * ks_d * 32,
+        "transpose_w": V * D * esz + -(-D // 256) * 256 * ks_v * 32,
+    }
+    streaming = {}
+    for k, b in stream_bytes.items():
+        kk = kernels[k]
+        if kk["launches"] and kk["ms_total"]:
+            streaming[k] = {"bytes_per_step": b, "ms_per_step": kk["ms_total"] / args.steps,
+                            "GB_per_s": b * args.steps / (kk["ms_total"] * 1e-3) / 1e9}
     result = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -231,6 +330,12 @@ def main():
                      "avg_launch_ms": dk["ms_total"] / max(1, dk["launches"]),
                      "flops_per_launch_avg": gemm_flops[dominant] * args.steps / max(1, dk["launches"])},
         "kernels": kernels,
+        "streaming_kernels": streaming,
+        "step_ms": {"median": step_ms[len(step_ms) // 2], "min": step_ms[0], "max": step_ms[-1],
+                    "source": "HIP events around each timed step"},
+        "clocks": dict(clocks.summary(), box=peak_box,
+                       note="sampled with rocm-smi / amd-smi during the timed steps; the roofline peak stays "
+                            "the published 2.5 PFLOP/s"),
         "workspace_bytes": ws_bytes,
         "peak_extra_bytes": peak_extra,
         "loss": loss,

@@ -1436,30 +1436,34 @@ struct MergeArgs {
   double* wl;
 };
 
+// Two (max, sum-exp) pairs as one: M = max, S = S1 e^(M1 - M) + S2 e^(M2 - M) (an empty
+// pair has M = -inf and S = 0).  Symmetric in its arguments, bit for bit.
+__device__ __forceinline__ void lse_combine(float& M, float& S, float M2, float S2) {
+  const float Mn = fmaxf(M, M2);
+  S = (M > -INFINITY ? S * expf(M - Mn) : 0.0f) + (M2 > -INFINITY ? S2 * expf(M2 - Mn) : 0.0f);
+  M = Mn;
+}
+
 // Merge of the vocabulary tiles' (max, sum-exp) partials, stored token-major; then, for
-// the loss, the per-token GRPO terms.  16 lanes share a token: lane j takes tiles j,
-// j + 16, ... in order and the 16 partial sums combine in a fixed butterfly, so the
+// the loss, the per-token GRPO terms.  One wave per token: lane l folds tiles l, l + 64,
+// ... in order into a running pair (one pass over the partials), then the 64 pairs
+// combine in a fixed butterfly (both lanes of a step compute the same bits), so the
 // result depends on the vocabulary size only, never on the chunking.
 __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
-  const int j = blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int sub = threadIdx.x & 15;
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const bool valid = j < a.rows;
   const float* pm = a.pm + (int64_t)(valid ? j : 0) * a.ntiles;
   const float* ps = a.ps + (int64_t)(valid ? j : 0) * a.ntiles;
-  float M = -INFINITY;
+  float M = -INFINITY, S = 0.0f;
   if (valid)
-    for (int i = sub; i < a.ntiles; i += 16) M = fmaxf(M, pm[i]);
+    for (int i = lane; i < a.ntiles; i += 64) lse_combine(M, S, pm[i], ps[i]);
 #pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 16));
-  float S = 0.0f;
-  if (valid)
-    for (int i = sub; i < a.ntiles; i += 16) {
-      const float m = pm[i];
-      if (m > -INFINITY) S += ps[i] * expf(m - M);
-    }
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) S += __shfl_xor(S, m, 16);
-  if (!valid || sub != 0) return;
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float M2 = __shfl_xor(M, m), S2 = __shfl_xor(S, m);
+    lse_combine(M, S, M2, S2);
+  }
+  if (!valid || lane != 0) return;
   const int64_t t = a.t0 + j;
   const float lse = M + logf(S);
   const float lp = a.zy[t] - lse;
@@ -1797,7 +1801,7 @@ grpo_status logp_impl(const Plan& p, const grpo_shape* shape, const T* H, const 
     m.lse = lse;
     m.logp = logp;
     L.run(GRPO_K_MERGE, [&] {
-      hipLaunchKernelGGL(merge_kernel, dim3(grid1(rows, 16)), dim3(256), 0, L.stream, m);
+      hipLaunchKernelGGL(merge_kernel, dim3(grid1(rows, 4)), dim3(256), 0, L.stream, m);
     });
   }
   return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_E_HIP;
@@ -2020,7 +2024,7 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, int mode, const gr
     m.g = gbuf;
     m.wl = wl;
     L.run(GRPO_K_MERGE, [&] {
-      hipLaunchKernelGGL(merge_kernel, dim3(grid1(rows, 16)), dim3(256), 0, L.stream, m);
+      hipLaunchKernelGGL(merge_kernel, dim3(grid1(rows, 4)), dim3(256), 0, L.stream, m);
     });
     if (keep) {
       const int64_t units = p.rows_pad * p.ks_v * 2;
