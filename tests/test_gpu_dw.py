@@ -18,6 +18,7 @@ pytestmark = pytest.mark.gpu
     (256, 1000, [300, 212], 128, 1.0, 3.0, False),        # softcap, 4 chunks, ragged tail
     (512, 3000, [700, 324], 1024, 1.0, 0.0, True),        # kept logits
     (256, 10000, [300, 400, 324], 512, 1.0, 0.0, False),  # W^T copy (without dW this shape's backward runs in slices)
+    (256, 10000, [1200, 848], 2048, 1.0, 0.0, False),     # copies of W and W^T, one 2048-token chunk
 ])
 def test_grpo_loss_dW(D, V, lengths, chunk, tau, cap, keep):
     say(f"dW grpo D={D} V={V} T={sum(lengths)} chunk={chunk} tau={tau} cap={cap} keep={keep}")
