@@ -32,8 +32,8 @@ METRIC = "GRPO logp+loss fwd+bwd tokens/s at 1 GPU; % of bf16 MFMA peak"
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--chunk", type=int, default=0, help="override the workload's chunk tokens")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
