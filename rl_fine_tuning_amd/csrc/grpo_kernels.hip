@@ -86,6 +86,13 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
 __device__ __forceinline__ float f16_lo(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xffffu)); }
 __device__ __forceinline__ float f16_hi(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16)); }
 
+// The low (hi = false) or high 16-bit halves of x and y as one word, x's half in the low
+// 16 bits: v_perm_b32 picks bytes of the 64-bit pair whose bytes 0-3 are its second
+// operand (x here) and bytes 4-7 its first (y).
+__device__ __forceinline__ uint32_t halves(uint32_t x, uint32_t y, bool hi) {
+  return __builtin_amdgcn_perm(y, x, hi ? 0x07060302u : 0x05040100u);
+}
+
 __device__ __forceinline__ uint32_t u4get(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
@@ -466,10 +473,7 @@ struct TransTileA {
       for (int i = 0; i < 4; ++i) {
         const uint32_t a0 = (i < 2) ? v[p][0].x : v[p][0].y, a1 = (i < 2) ? v[p][1].x : v[p][1].y;
         const uint32_t a2 = (i < 2) ? v[p][2].x : v[p][2].y, a3 = (i < 2) ? v[p][3].x : v[p][3].y;
-        if (i & 1)
-          o[i] = make_uint2((a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u));
-        else
-          o[i] = make_uint2((a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16));
+        o[i] = make_uint2(halves(a0, a1, i & 1), halves(a2, a3, i & 1));
       }
       if (r & 1) {
         const uint2 t0 = o[0];
@@ -518,11 +522,9 @@ struct TransTileQ {
     const int c = tq >> 1, h = tq & 1;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      const int sh = 16 * (r & 1);
-      const uint32_t e0 = (u4get(v[0], r >> 1) >> sh) & 0xffffu, e1 = (u4get(v[1], r >> 1) >> sh) & 0xffffu;
-      const uint32_t e2 = (u4get(v[2], r >> 1) >> sh) & 0xffffu, e3 = (u4get(v[3], r >> 1) >> sh) & 0xffffu;
-      *reinterpret_cast<uint2*>(lds_stage + lds_off2(8 * vg + r, c) + 8 * h) =
-          make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
+      const uint32_t w0 = halves(u4get(v[0], r >> 1), u4get(v[1], r >> 1), r & 1);
+      const uint32_t w1 = halves(u4get(v[2], r >> 1), u4get(v[3], r >> 1), r & 1);
+      *reinterpret_cast<uint2*>(lds_stage + lds_off2(8 * vg + r, c) + 8 * h) = make_uint2(w0, w1);
     }
   }
 };
