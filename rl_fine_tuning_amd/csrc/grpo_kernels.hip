@@ -336,8 +336,11 @@ struct TransTile<float> {
 // B rows 64 w .. 64 w + 63 and all 256 A rows).  Only the A tile goes through LDS,
 // a 4-stage ring of 32 bf16 of K per stage (16 KB); each wave streams its own B rows
 // from global memory straight into registers, from a fragment-major copy of B in which
-// every 32-row x 16-k MFMA operand fragment is one contiguous 1 KB block.  Per 32 of K
-// a workgroup moves 32 KB from L2 (16 KB of A, 4 x 4 KB of B) for 4.2 MFLOP.
+// every 32-row x 16-k MFMA operand fragment is one contiguous 1 KB block.  The A tile
+// enters the ring by direct-to-LDS loads from the same layout when the workspace holds a
+// fragment-major copy of W (or W^T) (DmaFragA), else from row-major W (DmaTileA) or
+// transposed in registers on the way (TransTileA, TransTileQ).  Per 32 of K a workgroup
+// moves 32 KB from L2 (16 KB of A, 4 x 4 KB of B) for 4.2 MFLOP.
 constexpr int kTA = kTileA16;           // A rows per workgroup
 constexpr int kTB = kTileB16;           // B rows per workgroup
 constexpr int kFB = kTB / 32;           // B fragments (32 rows) per tile
