@@ -218,3 +218,16 @@ def test_sliced_backward_uneven_slices_match_whole_chunks():
         assert torch.equal(a[name].view(bits), b[name].view(bits)), name
     rel = (a["dH"].float() - b["dH"].float()).norm() / b["dH"].float().norm()
     assert rel.item() <= 1e-3, rel.item()
+
+
+@pytest.mark.parametrize("agg", ["seq_mean", "token_mean"])
+def test_empty_sequences(agg):
+    # zero-length sequences (repeated offsets, one at the end of the stream) still count in S
+    # for the per-sequence mean, and get no tokens; chunk boundaries fall next to them
+    k = case(141, D=128, V=900, lengths=[300, 0, 200, 0, 156, 0], G=2, chunk=200, old_std=0.2, mask_frac=0.1,
+             agg=agg)
+    assert (np.diff(k["c"].cu) == 0).sum() == 3
+    say(f"loss with empty sequences ({agg}), T={k['T']}")
+    got = run_loss(k, 200)
+    torch.cuda.synchronize()
+    check_loss_outputs(k, got)
