@@ -217,7 +217,8 @@ def grpo_logp_bwd(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: 
                   logit_scale_multiply=0.0, logit_scale_divide=0.0, logit_softcapping=0.0, dH=None,
                   dW=None, workspace=None, stream=None, timer: Timer | None = None):
     """dH of sum_t grad_logp[t] * logp_t, recomputing each chunk's logits from the forward's lse.
-    With dW (an fp32 [V, D] tensor, or True to allocate one) returns (dH, dW)."""
+    With dW (an fp32 [V, D] tensor, or True to allocate one) returns (dH, dW).  A caller's
+    workspace must hold grpo_workspace_bytes(..., with_dW=bool(dW)) bytes."""
     for t, n in ((H, "H"), (W, "W"), (targets, "targets"), (lse, "lse"), (grad_logp, "grad_logp")):
         _dev(t, n)
     T, D = H.shape
@@ -243,7 +244,8 @@ def grpo_ce_loss_fwd_bwd(H, W, targets, chunk_tokens, *, temperature=1.0, logit_
                          want_logp=True, want_token_loss=False, dH=None, dW=None, workspace=None, stream=None,
                          timer: Timer | None = None):
     """Mean cross-entropy over the unmasked tokens, per-token logp, dL/dH and (with dW: an
-    fp32 [V, D] tensor, or True to allocate one) dL/dW."""
+    fp32 [V, D] tensor, or True to allocate one) dL/dW.  A caller's workspace must hold
+    grpo_workspace_bytes(..., with_dW=bool(dW)) bytes."""
     for t, n in ((H, "H"), (W, "W"), (targets, "targets")):
         _dev(t, n)
     if mask is not None:
@@ -284,7 +286,9 @@ def grpo_loss_fwd_bwd(H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk_
                       keep_chunk_logits=False, clip_eps_low=0.2, clip_eps_high=0.2, beta=0.001, agg="seq_mean",
                       mask=None, want_logp=True, want_token_loss=True, dH=None, dW=None, workspace=None,
                       stream=None, timer: Timer | None = None):
-    """GRPO loss, per-token logp and objective, and dL/dH.  cu_seqlens is a host int32 array/tensor."""
+    """GRPO loss, per-token logp and objective, and dL/dH (and dL/dW with dW: an fp32 [V, D]
+    tensor, or True to allocate one).  cu_seqlens is a host int32 array/tensor.  A caller's
+    workspace must hold grpo_workspace_bytes(..., num_seqs=S, with_dW=bool(dW)) bytes."""
     for t, n in ((H, "H"), (W, "W"), (targets, "targets"), (old_logp, "old_logp"), (adv, "adv")):
         _dev(t, n)
     if ref_logp is not None:
