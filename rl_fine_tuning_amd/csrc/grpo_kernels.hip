@@ -1219,31 +1219,41 @@ void gemm16_kernel(const GemmArgs g) {
   }
 }
 
-// Fragment-major copy of `rows` rows of a row-major bf16 matrix [rows, K] (ld = K):
-// one thread per 16-byte unit; rows past `rows` and k past K are zero.
+// Fragment-major copy of `rows` rows of a row-major bf16 matrix [rows, K] (ld = K), rows
+// past `rows` and k past K zero.  A block moves 32 rows (one fragment row group) x 8 k steps
+// (128 elements) through LDS: reads of 128 contiguous bytes per 8 lanes, then per k step
+// one contiguous kilobyte of the copy per wave.  The LDS tile keeps row r's 16-byte chunk c
+// at chunk c ^ (r % 16), so the column-wise reads of the write phase spread over the banks.
 __global__ __launch_bounds__(256) void frag_copy_kernel(const __bf16* __restrict__ X, int rows, int K, int ks_count,
-                                                        int64_t units, uint4* __restrict__ out) {
-  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (u >= units) return;
-  const int l = (int)(u & 63);
-  const int64_t fr = u >> 6;
-  const int fb = (int)(fr % kFB);
-  const int64_t rest = fr / kFB;
-  const int kstep = (int)(rest % ks_count);
-  const int tb = (int)(rest / ks_count);
-  const int row = tb * kTB + fb * 32 + (l & 31);
-  const int k = kstep * 16 + 8 * (l >> 5);
-  uint4 v = make_uint4(0u, 0u, 0u, 0u);
-  if (row < rows && k < K) v = *reinterpret_cast<const uint4*>(X + (int64_t)row * K + k);
-  out[u] = v;
+                                                        char* __restrict__ out) {
+  __shared__ uint4 tile[32 * 16];
+  const int tid = threadIdx.x;
+  const int rg = blockIdx.x;               // 32-row group: tile rg / 8, fragment rg % 8
+  const int ks0 = blockIdx.y * 8;          // first k step of the block
+  {
+    const int r = tid >> 3, seg = tid & 7;
+    const int row = rg * 32 + r;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = seg + 8 * h;
+      const int k = ks0 * 16 + 8 * c;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (row < rows && k < K) v = *reinterpret_cast<const uint4*>(X + (int64_t)row * K + k);
+      tile[r * 16 + (c ^ (r & 15))] = v;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int u = tid + 256 * h;           // unit of the block: k step u / 64, lane u % 64
+    const int ks = ks0 + (u >> 6);
+    if (ks >= ks_count) continue;
+    const int lane = u & 63, r = lane & 31, c = 2 * (u >> 6) + (lane >> 5);
+    const int64_t frag = ((int64_t)(rg >> 3) * ks_count + ks) * kFB + (rg & 7);
+    *reinterpret_cast<uint4*>(out + frag * 1024 + lane * 16) = tile[r * 16 + (c ^ (r & 15))];
+  }
 }
 
-// Fragment-major W^T (rows = hidden units, k = vocabulary; ks_v k steps, D rounded up to
-// 256 rows) from W [V, D] (bf16), zeros past V and past D: each thread moves an 8 x 8 block
-// (8 vocabulary rows x 8 hidden columns), transposed in registers.  Lane l = 8 bv + bd of
-// a wave covers vocabulary rows 8 bv .. and hidden columns 8 bd .. of the wave's 64 x 64
-// block: the reads (lanes along d) move 128 contiguous bytes per 8 lanes, and each write
-// is one 16-byte unit of the copy (8 consecutive vocabulary entries of one hidden unit).
 __global__ __launch_bounds__(256) void transpose_w_kernel(const __bf16* __restrict__ W, int V, int D, int ks_v,
                                                           char* __restrict__ WTf) {
   const int lane = threadIdx.x & 63;
@@ -1702,10 +1712,9 @@ void launch_gemm(Launcher& L, int kid, const GemmArgs& g) {
 
 // Tokens' operand of the bf16 logits GEMMs: the fragment-major copy of the chunk's rows.
 inline void enqueue_frag_copy(Launcher& L, const Plan& p, const __bf16* Hc, int rows, char* Hf) {
-  const int64_t units = p.rows_pad / kTileB16 * p.ks_d * kFB * 64;
   L.run(GRPO_K_FRAG_COPY, [&] {
-    hipLaunchKernelGGL(frag_copy_kernel, dim3(grid1(units, 256)), dim3(256), 0, L.stream, Hc, rows, (int)p.D,
-                       (int)p.ks_d, units, reinterpret_cast<uint4*>(Hf));
+    hipLaunchKernelGGL(frag_copy_kernel, dim3((int)(p.rows_pad / 32), grid1(p.ks_d, 8)), dim3(256), 0, L.stream, Hc,
+                       rows, (int)p.D, (int)p.ks_d, Hf);
   });
 }
 
@@ -1733,11 +1742,10 @@ WCopies<T> prepare_w(Launcher& L, const Plan& p, const T* W, char* ws) {
     }
     if (p.use_wf) {
       c.Wf = ws + p.off_Wf;
-      const int64_t units = p.ntiles_v * p.ks_d * kFB * 64;
       L.run(GRPO_K_W_COPY, [&] {
-        hipLaunchKernelGGL(frag_copy_kernel, dim3(grid1(units, 256)), dim3(256), 0, L.stream,
-                           reinterpret_cast<const __bf16*>(W), (int)p.V, (int)p.D, (int)p.ks_d, units,
-                           reinterpret_cast<uint4*>(ws + p.off_Wf));
+        hipLaunchKernelGGL(frag_copy_kernel, dim3((int)(p.ntiles_v * kTileA16 / 32), grid1(p.ks_d, 8)), dim3(256), 0,
+                           L.stream, reinterpret_cast<const __bf16*>(W), (int)p.V, (int)p.D, (int)p.ks_d,
+                           ws + p.off_Wf);
       });
     }
   }
