@@ -42,6 +42,9 @@ def parse():
                     help="skip timing the variant that keeps the chunk's logits (no recompute GEMM)")
     ap.add_argument("--no-entry-points", action="store_true",
                     help="skip timing grpo_logp_fwd / grpo_logp_bwd / grpo_ce_loss_fwd_bwd / grpo_advantages")
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="do not sample the shader clock and socket power (rocm-smi / amd-smi child processes); "
+                         "for runs under a profiler, whose preloaded library would follow those children")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for HBM counter scaling)")
     return ap.parse_args()
@@ -118,8 +121,9 @@ class ClockSampler:
     """Samples the shader clock (rocm-smi) and the socket power (amd-smi) from a helper
     thread, each read in a child process, while the timed steps run."""
 
-    def __init__(self):
+    def __init__(self, enabled=True):
         import threading
+        self.enabled = enabled
         self.sclk, self.power = [], []
         self._stop = threading.Event()
         self._thread = threading.Thread(target=self._run, daemon=True)
@@ -141,12 +145,14 @@ class ClockSampler:
                 return
 
     def __enter__(self):
-        self._thread.start()
+        if self.enabled:
+            self._thread.start()
         return self
 
     def __exit__(self, *exc):
         self._stop.set()
-        self._thread.join(timeout=30)
+        if self.enabled:
+            self._thread.join(timeout=30)
 
     def summary(self):
         avg = lambda v: sum(v) / len(v) if v else None
@@ -257,7 +263,7 @@ def main():
     peak_box = box_peak()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    with ClockSampler() as clocks:
+    with ClockSampler(enabled=not args.no_clocks) as clocks:
         t0 = time.perf_counter()
         for i in range(args.steps):
             evs[i].record()
