@@ -563,9 +563,9 @@ __device__ __forceinline__ void b_load(const char* Bw, int ks, int ks_count, bf1
 __device__ __forceinline__ void mma16(const bf16x8 (&a)[kFA], const bf16x8 (&b)[kFBW],
                                       floatx16 (&acc)[kFA][kFBW]) {
 #pragma unroll
-  for (int i = 0; i < kFA; ++i)
+  for (int j = 0; j < kFBW; ++j)
 #pragma unroll
-    for (int j = 0; j < kFBW; ++j)
+    for (int i = 0; i < kFA; ++i)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
 }
 
@@ -961,15 +961,17 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       } else {
+        // the stage's 8 loads and 8 fragment reads spread over all 16 MFMAs
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0(kTrans ? 28 : kVmAfterA));
       __builtin_amdgcn_s_barrier();
