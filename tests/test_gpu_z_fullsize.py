@@ -5,8 +5,9 @@ Every per-token output (logp, l_t, dH row) depends on its own row only, so the
 oracle computes the sampled rows exactly: the first and last 8 tokens of every
 chunk, 4 tokens on each side of every sequence boundary, and 128 uniform tokens.
 Sampled tokens get old/ref log-probabilities = oracle logp + the workload's noise;
-the others get -log V + noise, which only moves the loss, and the loss is checked
-through its fixed relation to the per-token terms (L = sum_t w_t l_t).
+the others get -log V + noise, which only moves the loss.  The loss is checked against
+the oracle's loss from the GPU's own log-probabilities at every token, and through its
+fixed relation to the per-token terms (L = sum_t w_t l_t).
 """
 import numpy as np
 import pytest
@@ -16,7 +17,7 @@ import oracle
 from rl_fine_tuning_amd import grpo_loss_fwd_bwd, grpo_workspace_bytes
 from synth import make_config
 
-from gpu_cases import DH_REL_L2, LOGP_ATOL, dev_matrix, f32, host_matrix, near_clip_boundary, rel_l2, say
+from gpu_cases import DH_REL_L2, LOGP_ATOL, LOSS_RTOL, dev_matrix, f32, host_matrix, near_clip_boundary, rel_l2, say
 
 pytestmark = pytest.mark.gpu
 
@@ -81,4 +82,12 @@ def test_full_size_sampled(cfg, keep):
     L_terms = float(np.sum(w * tl))
     scale = float(np.sum(np.abs(w * tl)))
     assert abs(L - L_terms) <= 1e-6 * scale, (L, L_terms)
+    # the loss over every token: the oracle's loss from the GPU's own log-probabilities (the
+    # GEMM side of logp is checked on the sampled rows above; this pins the per-token
+    # objective, the weights and the fp64 reduction at all T tokens)
+    L_or, ell_or, _ = oracle.grpo_loss_from_logp(logp, old.astype(np.float64), ref.astype(np.float64),
+                                                 adv.astype(np.float64), c.cu, c.mask)
+    scale_or = max(abs(L_or), float(np.sum(np.abs(w * ell_or))))
+    assert abs(L - L_or) <= LOSS_RTOL * scale_or, (L, L_or, scale_or)
+    assert np.all(np.abs(tl - ell_or) <= LOGP_ATOL * (1 + np.abs(adv[oracle.sequence_of_token(c.cu)])))
     say(f"  logp err {err:.2e}, dH rel L2 {e:.2e}, loss {L:.6e}, workspace {ws_bytes / 2**30:.2f} GiB")
