@@ -390,7 +390,7 @@ def main():
         ms_dw, dw_tf = None, None
         if case.dtype == "bf16":
             dW = torch.empty(V, D, dtype=torch.float32, device=dev)
-            tmw = Timer(4096)
+            tmw = Timer(32768)  # two launches per vocabulary band per chunk for the dW GEMM
             def step_dw():
                 grpo_advantages(rewards, G, out=adv)
                 grpo_loss_fwd_bwd(H, W, targets, cu, old, ref, adv, C, dH=dH, dW=dW, workspace=ws,
@@ -398,8 +398,9 @@ def main():
             step_dw()
             tmw.reset()
             ms_dw = timed(step_dw)
-            ms_k, _, _ = tmw.read("dw_gemm")
+            ms_k, _, dropped = tmw.read("dw_gemm")
             calls = tmw.read("loss_finalize")[1]  # one per call
+            assert dropped == 0, "timer capacity too small for the dW step"
             dw_tf = gemm_flops["dh_gemm"] * calls / (ms_k * 1e-3) / 1e12 if ms_k else None
             tmw.close()
             del dW

@@ -127,7 +127,8 @@ typedef enum {
   GRPO_K_HT_COPY = 13,     /* tokens' operand of the dW GEMM (bf16, when dW is requested) */
   GRPO_K_DW_GEMM = 14,     /* MFMA GEMM dW (+)= Gx^T H per chunk */
   GRPO_K_W_COPY = 15,      /* fragment-major W for the logits GEMMs (bf16, when it fits) */
-  GRPO_K_COUNT = 16
+  GRPO_K_QT_BAND = 16,     /* one vocabulary band of the dW GEMM's operand (P' - onehot)^T (bf16) */
+  GRPO_K_COUNT = 17
 } grpo_kernel_id;
 
 typedef struct grpo_timer grpo_timer; /* opaque, owned by the caller */
@@ -189,7 +190,8 @@ grpo_status grpo_advantages(const float* rewards, int64_t num_seqs, int64_t grou
  *   (ref_logp may be NULL only when beta == 0); adv fp32 [num_seqs].
  *   loss fp64 [1] (written); logp, token_loss fp32 [T] (written when not NULL;
  *   token_loss holds l_t, unweighted); dH [T, D] of shape->dtype (overwritten;
- *   masked tokens get +0 rows); dW fp32 [V, D] (NULL = not computed; bf16 only): the
+ *   masked tokens get +0 rows); dW fp32 [V, D], 16-byte aligned (NULL = not computed;
+ *   bf16 only; else GRPO_E_UNSUPPORTED): the
  *   gradient with respect to W, dW = sum_t (dL/dx_t)^T H_t with x_t = H_t W^T, overwritten
  *   (accumulated over the chunks in fixed order; for a full fine-tune, where the lm_head is
  *   trained: under LoRA it is frozen), one more 2 D V flop GEMM per token;

@@ -62,7 +62,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 // fragment-major copy of W^T with direct-to-LDS loads.
 // KIND_LSES (bf16): the LSE epilogue that also keeps the chunk's logits, as d = z - (tile
 // max) in fp16, in the probabilities buffer (the variant without the recompute GEMM).
-// KIND_DW (bf16): dW += Gx^T H_c, A = Q^T transposed from the chunk's fragment-major Q.
+// KIND_DW (bf16): dW += Gx^T H_c over one vocabulary band, A = the band of Q^T in fragment-major
+// order (qt_band_kernel), read by direct-to-LDS loads like the copy of W.
 enum Kind { KIND_LSE = 0, KIND_PROBS = 1, KIND_DH = 2, KIND_DHT = 3, KIND_LSES = 4, KIND_DW = 5 };
 
 // Byte offset of 16-byte chunk c of row r inside a [256 rows x 8 chunks] LDS tile.
@@ -493,45 +494,6 @@ struct TransTileA {
   }
 };
 
-// A operand of the dW GEMM: Q^T (rows = vocabulary, k = the chunk's tokens) from the
-// chunk's fragment-major Q (rows = tokens, 16-byte units of 8 vocabulary entries): thread i
-// takes tokens k0 + 4 (i % 8) .. + 3 of vocabulary rows 8 (i / 8) .. + 7 of the tile (four
-// 16-byte units, 64 contiguous bytes), transposes the 4 x 8 block in registers and writes
-// eight 8-byte half chunks, one per vocabulary row.  Columns past the padded vocabulary
-// read as 0; token rows past the chunk hold finite values that the zero rows of the
-// tokens' operand cancel.
-struct TransTileQ {
-  uint4 v[4];
-  const char* Q;
-  int ks_count, v0, vpad, tq, vg;
-  __device__ __forceinline__ void init(const void* Q_, int ks_count_, int row0, int tid) {
-    Q = reinterpret_cast<const char*>(Q_);
-    ks_count = ks_count_;
-    vpad = ks_count_ * 16;
-    tq = tid & 7;
-    vg = tid >> 3;
-    v0 = row0 + 8 * vg;
-  }
-  // Stages at or past kend (the ring's look-ahead past the last one) read nothing; the last
-  // stage's tokens stay below the copy's rows (rounded up to 256).
-  __device__ __forceinline__ void load(int k0, int kend) {
-    const bool in = v0 < vpad && k0 < kend;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      v[e] = in ? *reinterpret_cast<const uint4*>(Q + frag_off(k0 + 4 * tq + e, v0, ks_count))
-                : make_uint4(0u, 0u, 0u, 0u);
-  }
-  __device__ __forceinline__ void store(char* lds_stage) const {
-    const int c = tq >> 1, h = tq & 1;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const uint32_t w0 = halves(u4get(v[0], r >> 1), u4get(v[1], r >> 1), r & 1);
-      const uint32_t w1 = halves(u4get(v[2], r >> 1), u4get(v[3], r >> 1), r & 1);
-      *reinterpret_cast<uint2*>(lds_stage + lds_off2(8 * vg + r, c) + 8 * h) = make_uint2(w0, w1);
-    }
-  }
-};
-
 // A fragments of one 16-wide k step (kk = 0, 1) of a ring stage: rows 32 f + l % 32,
 // k = 16 kk + 8 (l / 32) + 0..7.
 __device__ __forceinline__ void a_frags(const char* As, int kk, int lane, bf16x8 (&a)[kFA]) {
@@ -877,7 +839,7 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  constexpr bool kTrans = KIND == KIND_DH || KIND == KIND_DW;  // A transposed in registers
+  constexpr bool kTrans = KIND == KIND_DH;  // A transposed in registers
   const int row_a0 = tile_a * kTA;
   const int row_b0 = tb * kTB;
   const int k_begin = ks * g.k_len;
@@ -897,13 +859,10 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
   const char* Bw =
       reinterpret_cast<const char*>(g.b) + (int64_t)tb * g.b_ks * kFB * 1024 + kFBW * w * 1024 + lane * 16;
   const int ks0 = k_begin >> 4;
-  using ATile = typename std::conditional<
-      KIND == KIND_DW, TransTileQ,
-      typename std::conditional<kTrans, TransTileA,
-                                typename std::conditional<kFragA, DmaFragA, DmaTileA>::type>::type>::type;
+  using ATile = typename std::conditional<kTrans, TransTileA,
+                                          typename std::conditional<kFragA, DmaFragA, DmaTileA>::type>::type;
   ATile at;
-  if constexpr (KIND == KIND_DW) at.init(g.a, g.p_ks, row_a0, tid);
-  else if constexpr (kTrans) at.init(A, g.lda, row_a0, tid);
+  if constexpr (kTrans) at.init(A, g.lda, row_a0, tid);
   else if constexpr (kFragA) at.init(g.a, g.b_ks, tile_a, tid);
   else at.init(A, g.lda, row_a0, g.a_rows, tid);
   auto afr = [&](const char* As, int kk, bf16x8 (&a)[kFA]) {
@@ -1117,20 +1076,31 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
       }
     }
   } else if constexpr (KIND == KIND_DW) {
-    // dW[v, d] = acc (first chunk) or dW[v, d] + acc, fp32; acc = sum_t Q[t, v] (-c_t H[t, d]).
+    // dW[v, d] = acc (first chunk) or dW[v, d] + acc, fp32, with the hidden units d as the A
+    // rows and the band's vocabulary entries v as the B rows: acc = sum_t (-c_t H[t, d]) Q[t, v].
+    // A lane's 4 consecutive accumulator rows are 4 consecutive floats of a dW row.
     float* dw = g.dw;
+    const int drem = g.D - row_a0;  // uniform; multiple of 8
 #pragma unroll
     for (int j = 0; j < kFBW; ++j) {
-      const int d = row_b0 + 64 * w + 32 * j + col;
-      if (d >= g.D) continue;
+      const int v = row_b0 + 64 * w + 32 * j + col;
+      if (v >= g.V) continue;
+      float* row = dw + (int64_t)v * g.D;
 #pragma unroll
       for (int i = 0; i < kFA; ++i) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int v = row_a0 + 32 * i + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (kEdge && v >= g.V) continue;
-          float* p = dw + (int64_t)v * g.D + d;
-          *p = g.accumulate ? *p + acc[i][j][r] : acc[i][j][r];
+        for (int q = 0; q < 4; ++q) {
+          if (kEdge && 32 * i + 8 * q >= drem) continue;
+          float4* p = reinterpret_cast<float4*>(row + row_a0 + 32 * i + 8 * q + 4 * hi);
+          float4 o = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          if (g.accumulate) {
+            const float4 x = *p;
+            o.x += x.x;
+            o.y += x.y;
+            o.z += x.z;
+            o.w += x.w;
+          }
+          *p = o;
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -1191,7 +1161,7 @@ void gemm16_kernel(const GemmArgs g) {
     ks = ta / g.tiles_a_base;
     tile_a = ta - ks * g.tiles_a_base;
   }
-  const bool edge = (tile_a + 1) * kTA > (kDH ? g.D : g.V);
+  const bool edge = (tile_a + 1) * kTA > ((kDH || KIND == KIND_DW) ? g.D : g.V);
   if constexpr (kDH) {
     constexpr bool kFrag = KIND == KIND_DHT;
     if (g.ksplit > 1) {
@@ -1202,8 +1172,8 @@ void gemm16_kernel(const GemmArgs g) {
       else gemm16_tile<KIND, false, false, false, kFrag>(g, smem, ks, tile_a, tb);
     }
   } else if constexpr (KIND == KIND_DW) {
-    if (edge) gemm16_tile<KIND, true, false, false, false>(g, smem, ks, tile_a, tb);
-    else gemm16_tile<KIND, false, false, false, false>(g, smem, ks, tile_a, tb);
+    if (edge) gemm16_tile<KIND, true, false, false, true>(g, smem, ks, tile_a, tb);
+    else gemm16_tile<KIND, false, false, false, true>(g, smem, ks, tile_a, tb);
   } else if (g.a_frag) {
     if (g.lm.cap_in > 0.0f) {
       if (edge) gemm16_tile<KIND, true, false, true, true>(g, smem, ks, tile_a, tb);
@@ -1386,6 +1356,52 @@ __global__ __launch_bounds__(256) void ht_copy_kernel(const __bf16* __restrict__
     e[k] = x;
   }
   out[u] = make_uint4(pack_bf16(e[0], e[1]), pack_bf16(e[2], e[3]), pack_bf16(e[4], e[5]), pack_bf16(e[6], e[7]));
+}
+
+// One band of the dW GEMM's vocabulary-row operand: Q^T for vocabulary entries band0 ..
+// band0 + rows_band - 1 (rows) and the slice's tokens (k), in the fragment-major layout
+// [vr / 256][t / 16][(vr % 256) / 32][lane][8 tokens] with lane = vr % 32 + 32 ((t % 16) / 8),
+// from the slice's fragment-major Q (rows = tokens, k = vocabulary, ks_v k steps).  Thread u
+// transposes one block of 8 tokens x 8 vocabulary entries in registers: 8 lanes (128
+// contiguous bytes) of one Q fragment in, 8 lanes (128 contiguous bytes) of one band fragment
+// out; the 8 threads of a group read one whole kilobyte fragment of Q.  Vocabulary entries
+// past Q's width (ks_v 16) read as 0.  Q's token rows past the slice hold finite values that
+// the zero rows of the dW GEMM's tokens' operand cancel.
+__global__ __launch_bounds__(256) void qt_band_kernel(const uint4* __restrict__ Q, int ks_v, int rows_pad,
+                                                      int band0, int rows_band, int ks_t,
+                                                      uint4* __restrict__ out) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int nv16 = rows_band / 16;      // 16-entry vocabulary steps in the band
+  const int64_t nfrag = (int64_t)(rows_pad / 32) * nv16;
+  if (u >= nfrag * 8) return;
+  const int j = (int)(u & 7);
+  const int64_t f = u >> 3;             // (token tile, vocabulary step, 32-token group), group fastest
+  const int tg = (int)(f & 7);
+  const int64_t rest = f >> 3;
+  const int vs = (int)(rest % nv16);
+  const int tb = (int)(rest / nv16);
+  const int t0 = tb * kTB + tg * 32 + (j & 3) * 8;
+  const int v0 = band0 + vs * 16 + (j >> 2) * 8;
+  uint4 in[8];
+  if (v0 < ks_v * 16) {
+    const uint4* src = Q + ((((int64_t)tb * ks_v + (v0 >> 4)) * kFB + tg) * 64 + (j & 3) * 8 + 32 * (j >> 2));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) in[k] = src[k];
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) in[k] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  // out[m]: vocabulary entry v0 + m for tokens t0 .. t0 + 7
+  const int vr0 = v0 - band0;
+  uint4* dst = out + ((((int64_t)(vr0 / kTA) * ks_t + (t0 >> 4)) * kFA + (vr0 % kTA) / 32) * 64 + (vr0 & 31) +
+                      32 * ((t0 >> 3) & 1));
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const int wi = m >> 1;
+    const bool hi = m & 1;
+    dst[m] = make_uint4(halves(u4get(in[0], wi), u4get(in[1], wi), hi), halves(u4get(in[2], wi), u4get(in[3], wi), hi),
+                        halves(u4get(in[4], wi), u4get(in[5], wi), hi), halves(u4get(in[6], wi), u4get(in[7], wi), hi));
+  }
 }
 
 // ---------------------------------------------------------------------------- small kernels
@@ -1831,7 +1847,8 @@ grpo_status logp_impl(const Plan& p, const grpo_shape* shape, const T* H, const 
 template <typename T>
 void backward_chunk(Launcher& L, const Plan& p, const T* W, const WCopies<T>& wc, const T* Hc, char* Hf, int rows,
                     int64_t k, const float* lse_c, const float* g_c, const int32_t* targets_c, T* dH_c, T* P,
-                    float* part, const LogitMap& lm, const float* zy_c, bool probs_ready, float* dW) {
+                    float* part, const LogitMap& lm, const float* zy_c, bool probs_ready, float* dW,
+                    char* Qt) {
   const bool bf16 = sizeof(T) == 2;
   const int srows = (int)(p.bwd_rows > 0 && p.bwd_rows < rows ? p.bwd_rows : rows);
   for (int r0 = 0; r0 < rows; r0 += srows) {
@@ -1909,9 +1926,10 @@ void backward_chunk(Launcher& L, const Plan& p, const T* W, const WCopies<T>& wc
     if constexpr (sizeof(T) == 2) {
       if (dW) {
         // dW (+)= Gx^T H: the tokens' operand (-c H)^T of the slice replaces the chunk's
-        // hidden-state copy (no longer needed once the slice's recompute GEMM has run), then
-        // the dW GEMM with the vocabulary as rows, the hidden units as columns and the
-        // slice's tokens as K.
+        // hidden-state copy (no longer needed once the slice's recompute GEMM has run), then,
+        // band by band of the plan's vocabulary tiles, Q^T of the band in fragment-major order
+        // and the dW GEMM with the band's vocabulary as rows, the hidden units as columns and
+        // the slice's tokens as K.
         const int ks_t = (int)(cdiv(sr, kTileB16) * kTileB16 / 16);
         const int64_t units = cdiv(p.D, kTileB16) * ks_t * kFB * 64;
         L.run(GRPO_K_HT_COPY, [&] {
@@ -1919,27 +1937,38 @@ void backward_chunk(Launcher& L, const Plan& p, const T* W, const WCopies<T>& wc
                              reinterpret_cast<const __bf16*>(Hs), sr, (int)p.D, ks_t, units, g_s, targets_s,
                              (int)p.V, lm.dscale, reinterpret_cast<uint4*>(Hf));
         });
-        GemmArgs gw = {};
-        gw.a = P;
-        gw.b = Hf;
-        gw.a_rows = (int)p.V;
-        gw.b_rows = (int)p.D;
-        gw.K = sr;
-        gw.k_len = sr;
-        gw.tiles_a_base = (int)p.ntiles_v;
-        gw.tiles_a = (int)p.ntiles_v;
-        gw.tiles_b = (int)cdiv(p.D, kTileB16);
-        gw.xcd_a = 8;
-        gw.group_b = 4;
-        gw.b_ks = ks_t;
-        gw.p_ks = (int)p.ks_v;
-        gw.V = (int)p.V;
-        gw.D = (int)p.D;
-        gw.ksplit = 1;
-        gw.lm = lm;
-        gw.dw = dW;
-        gw.accumulate = k > 0 || r0 > 0;
-        launch_gemm<T, KIND_DW>(L, GRPO_K_DW_GEMM, gw);
+        for (int64_t b0 = 0; b0 < p.ntiles_v; b0 += p.qt_tiles) {
+          const int nb = (int)(p.ntiles_v - b0 < p.qt_tiles ? p.ntiles_v - b0 : p.qt_tiles);
+          const int band0 = (int)(b0 * kTileA16);
+          const int64_t threads = (int64_t)(ks_t / 2) * (nb * kTileA16 / 16) * 8;  // 8 per Q fragment
+          L.run(GRPO_K_QT_BAND, [&] {
+            hipLaunchKernelGGL(qt_band_kernel, dim3(grid1(threads, 256)), dim3(256), 0, L.stream,
+                               reinterpret_cast<const uint4*>(P), (int)p.ks_v, ks_t * 16, band0, nb * kTileA16,
+                               ks_t, reinterpret_cast<uint4*>(Qt));
+          });
+          // A: (-c H)^T (rows = hidden units), B: the band of Q^T (rows = vocabulary entries)
+          GemmArgs gw = {};
+          gw.a = Hf;
+          gw.a_frag = 1;
+          gw.b = Qt;
+          gw.a_rows = (int)p.D;
+          gw.b_rows = nb * kTileB16;
+          gw.K = sr;
+          gw.k_len = sr;
+          gw.tiles_a_base = (int)cdiv(p.D, kTileA16);
+          gw.tiles_a = gw.tiles_a_base;
+          gw.tiles_b = nb;
+          gw.xcd_a = nb >= 8 ? 1 : nb >= 4 ? 2 : nb >= 2 ? 4 : 8;  // 8 / xcd_a XCD ranges of the band
+          gw.group_b = 4;
+          gw.b_ks = ks_t;
+          gw.V = (int)p.V - band0;  // the band's rows relative to its first vocabulary entry
+          gw.D = (int)p.D;
+          gw.ksplit = 1;
+          gw.lm = lm;
+          gw.dw = dW + (int64_t)band0 * p.D;
+          gw.accumulate = k > 0 || r0 > 0;
+          launch_gemm<T, KIND_DW>(L, GRPO_K_DW_GEMM, gw);
+        }
       }
     }
   }
@@ -2050,7 +2079,7 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, int mode, const gr
       });
     }
     backward_chunk<T>(L, p, W, wc, Hc, Hf, rows, k, lse + t0, gbuf + t0, targets + t0, dH + t0 * p.D, P,
-                      part, lm, zy + t0, keep, dW);
+                      part, lm, zy + t0, keep, dW, ws + p.off_Qt);
   }
   if (dW && p.nchunks == 0)  // no tokens: the gradient is 0
     hipLaunchKernelGGL(zero_fill_kernel, dim3(1024), dim3(256), 0, L.stream, dW, (int64_t)p.V * p.D);
@@ -2082,7 +2111,7 @@ grpo_status logp_bwd_impl(const Plan& p, const grpo_shape* shape, const T* H, co
     const T* Hc = H + t0 * p.D;
     if constexpr (sizeof(T) == 2) enqueue_frag_copy(L, p, Hc, rows, Hf);
     backward_chunk<T>(L, p, W, wc, Hc, Hf, rows, k, lse + t0, grad + t0, targets + t0, dH + t0 * p.D, P,
-                      part, lm, zy + t0, false, dW);
+                      part, lm, zy + t0, false, dW, ws + p.off_Qt);
   }
   return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_E_HIP;
 }
@@ -2147,7 +2176,7 @@ grpo_status grpo_loss_fwd_bwd(const grpo_shape* shape, const grpo_loss_params* p
   st = validate_cu(cu_seqlens, num_seqs, shape->T);
   if (st != GRPO_OK) return st;
   if (!aligned16(H) || !aligned16(W) || !aligned16(dH)) return GRPO_E_UNSUPPORTED;
-  if (dW && shape->dtype != GRPO_BF16) return GRPO_E_UNSUPPORTED;
+  if (dW && (shape->dtype != GRPO_BF16 || !aligned16(dW))) return GRPO_E_UNSUPPORTED;
   Plan p;
   st = make_plan(shape, num_seqs, true, &p, dW != nullptr);
   if (st != GRPO_OK) return st;
@@ -2172,7 +2201,7 @@ grpo_status grpo_logp_bwd(const grpo_shape* shape, const void* H, const void* W,
   if (!W) return GRPO_E_NULL;
   if (p.T > 0 && (!H || !targets || !lse || !grad_logp || !dH)) return GRPO_E_NULL;
   if (!aligned16(H) || !aligned16(W) || !aligned16(dH)) return GRPO_E_UNSUPPORTED;
-  if (dW && shape->dtype != GRPO_BF16) return GRPO_E_UNSUPPORTED;
+  if (dW && (shape->dtype != GRPO_BF16 || !aligned16(dW))) return GRPO_E_UNSUPPORTED;
   if (!ws_ok(p, workspace, workspace_bytes)) return GRPO_E_WORKSPACE;
   if (p.T == 0 && !dW) return GRPO_OK;  // nothing to do
   (void)hipGetLastError();
@@ -2199,7 +2228,7 @@ grpo_status grpo_ce_loss_fwd_bwd(const grpo_shape* shape, const void* H, const v
   if (!loss || !W) return GRPO_E_NULL;
   if (p.T > 0 && (!H || !targets || !dH)) return GRPO_E_NULL;
   if (!aligned16(H) || !aligned16(W) || !aligned16(dH)) return GRPO_E_UNSUPPORTED;
-  if (dW && shape->dtype != GRPO_BF16) return GRPO_E_UNSUPPORTED;
+  if (dW && (shape->dtype != GRPO_BF16 || !aligned16(dW))) return GRPO_E_UNSUPPORTED;
   if (!ws_ok(p, workspace, workspace_bytes)) return GRPO_E_WORKSPACE;
   (void)hipGetLastError();
   Launcher L{reinterpret_cast<hipStream_t>(stream), timer};

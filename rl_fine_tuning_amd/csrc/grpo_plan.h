@@ -39,10 +39,11 @@ struct Plan {
   bool use_wt = false;    // bf16: the dH GEMM reads a fragment-major W^T from the workspace
   bool use_wf = false;    // bf16: the logits GEMMs read a fragment-major W from the workspace
   int64_t bwd_rows = 0;   // tokens per backward slice (bf16: a multiple of 256; >= C when unsliced)
+  int64_t qt_tiles = 0;   // bf16 with dW: vocabulary tiles per band of the dW GEMM's transposed operand
   bool backward = false;
   size_t off_zy = 0, off_lse = 0, off_pm = 0, off_ps = 0;
   size_t off_g = 0, off_wl = 0, off_seq = 0, off_cu = 0, off_cnt = 0, off_wseq = 0;
-  size_t off_P = 0, off_part = 0, off_Hf = 0, off_WT = 0, off_Wf = 0;
+  size_t off_P = 0, off_part = 0, off_Hf = 0, off_WT = 0, off_Wf = 0, off_Qt = 0;
   size_t total = 0;
 };
 

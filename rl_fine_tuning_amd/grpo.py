@@ -19,7 +19,7 @@ GRPO_AGG = {"seq_mean": 0, "token_mean": 1}
 GRPO_STD = {"unbiased": 0, "population": 1}
 KERNELS = ["target_logit", "logits_lse", "merge", "probs", "dh_gemm", "dh_reduce", "token_index",
            "loss_finalize", "advantages", "frag_copy", "transpose_w", "probs_kept", "onehot_fix", "ht_copy",
-           "dw_gemm", "w_copy"]
+           "dw_gemm", "w_copy", "qt_band"]
 KERNEL_ID = {k: i for i, k in enumerate(KERNELS)}
 
 
