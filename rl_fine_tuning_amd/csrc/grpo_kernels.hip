@@ -1358,49 +1358,65 @@ __global__ __launch_bounds__(256) void ht_copy_kernel(const __bf16* __restrict__
   out[u] = make_uint4(pack_bf16(e[0], e[1]), pack_bf16(e[2], e[3]), pack_bf16(e[4], e[5]), pack_bf16(e[6], e[7]));
 }
 
-// One band of the dW GEMM's vocabulary-row operand: Q^T for vocabulary entries band0 ..
-// band0 + rows_band - 1 (rows) and the slice's tokens (k), in the fragment-major layout
+// One band of the dW GEMM's vocabulary-row operand: Q^T for the band's vocabulary entries
+// (rows, from band0) and the slice's tokens (k), in the fragment-major layout
 // [vr / 256][t / 16][(vr % 256) / 32][lane][8 tokens] with lane = vr % 32 + 32 ((t % 16) / 8),
-// from the slice's fragment-major Q (rows = tokens, k = vocabulary, ks_v k steps).  Thread u
-// transposes one block of 8 tokens x 8 vocabulary entries in registers: 8 lanes (128
-// contiguous bytes) of one Q fragment in, 8 lanes (128 contiguous bytes) of one band fragment
-// out; the 8 threads of a group read one whole kilobyte fragment of Q.  Vocabulary entries
-// past Q's width (ks_v 16) read as 0.  Q's token rows past the slice hold finite values that
-// the zero rows of the dW GEMM's tokens' operand cancel.
-__global__ __launch_bounds__(256) void qt_band_kernel(const uint4* __restrict__ Q, int ks_v, int rows_pad,
-                                                      int band0, int rows_band, int ks_t,
-                                                      uint4* __restrict__ out) {
-  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int nv16 = rows_band / 16;      // 16-entry vocabulary steps in the band
-  const int64_t nfrag = (int64_t)(rows_pad / 32) * nv16;
-  if (u >= nfrag * 8) return;
-  const int j = (int)(u & 7);
-  const int64_t f = u >> 3;             // (token tile, vocabulary step, 32-token group), group fastest
-  const int tg = (int)(f & 7);
-  const int64_t rest = f >> 3;
-  const int vs = (int)(rest % nv16);
-  const int tb = (int)(rest / nv16);
-  const int t0 = tb * kTB + tg * 32 + (j & 3) * 8;
-  const int v0 = band0 + vs * 16 + (j >> 2) * 8;
-  uint4 in[8];
-  if (v0 < ks_v * 16) {
-    const uint4* src = Q + ((((int64_t)tb * ks_v + (v0 >> 4)) * kFB + tg) * 64 + (j & 3) * 8 + 32 * (j >> 2));
+// from the slice's fragment-major Q (rows = tokens, k = vocabulary, ks_v k steps).  Block
+// (tb, g) moves one 256-token tile x 64 vocabulary entries (32 fragments of 1 KB each way)
+// through LDS: wave w loads the 8 fragments of vocabulary step 4 g + w (8 KB contiguous, one
+// kilobyte per instruction); thread (f, j) transposes the 8 x 8 block j of fragment f in
+// registers (its 8 tokens are lanes 8 j .. 8 j + 7); the output fragments go back to LDS and
+// out one kilobyte per instruction.  LDS slots rotate within each group of 8 units so that
+// every 8-lane group of an access touches 8 distinct 16-byte bank columns.  Vocabulary steps
+// past Q's width (ks_v) read as 0; Q's token rows past the slice hold finite values that the
+// zero rows of the dW GEMM's tokens' operand cancel.
+__device__ __forceinline__ int qt_in_slot(int f, int l) { return f * 64 + 8 * (l >> 3) + (((l & 7) + (l >> 3)) & 7); }
+__device__ __forceinline__ int qt_out_slot(int F, int L) {
+  return F * 64 + 8 * (L >> 3) + (((L & 7) + (L >> 3) + 2 * (F & 1)) & 7);
+}
+__global__ __launch_bounds__(256) void qt_band_kernel(const uint4* __restrict__ Q, int ks_v, int tiles_t,
+                                                      int band0, int ks_t, uint4* __restrict__ out) {
+  __shared__ uint4 lds[32 * 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int tb = blockIdx.x % tiles_t;  // token tile
+  const int g = blockIdx.x / tiles_t;   // 64-entry vocabulary group of the band
+  {
+    const int v16 = (band0 >> 4) + 4 * g + w;  // this wave's vocabulary step
+    const bool in = v16 < ks_v;
+    const uint4* src = Q + ((int64_t)tb * ks_v + v16) * (kFB * 64) + lane;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) in[k] = src[k];
-  } else {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) in[k] = make_uint4(0u, 0u, 0u, 0u);
+    for (int k = 0; k < 8; ++k)
+      lds[qt_in_slot(8 * w + k, lane)] = in ? src[k * 64] : make_uint4(0u, 0u, 0u, 0u);
   }
-  // out[m]: vocabulary entry v0 + m for tokens t0 .. t0 + 7
-  const int vr0 = v0 - band0;
-  uint4* dst = out + ((((int64_t)(vr0 / kTA) * ks_t + (t0 >> 4)) * kFA + (vr0 % kTA) / 32) * 64 + (vr0 & 31) +
-                      32 * ((t0 >> 3) & 1));
+  __syncthreads();
+  const int f = tid >> 3, j = tid & 7;
+  uint4 v[8];  // v[k]: token t0 + k, vocabulary entries v0 .. v0 + 7
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const int wi = m >> 1;
-    const bool hi = m & 1;
-    dst[m] = make_uint4(halves(u4get(in[0], wi), u4get(in[1], wi), hi), halves(u4get(in[2], wi), u4get(in[3], wi), hi),
-                        halves(u4get(in[4], wi), u4get(in[5], wi), hi), halves(u4get(in[6], wi), u4get(in[7], wi), hi));
+  for (int k = 0; k < 8; ++k) v[k] = lds[qt_in_slot(f, 8 * j + k)];
+  __syncthreads();
+  {
+    const int t0 = (f & 7) * 32 + (j & 3) * 8;   // within the token tile
+    const int v0 = (f >> 3) * 16 + (j >> 2) * 8;  // within the 64-entry group
+    const int F = (v0 >> 5) * 16 + (t0 >> 4);
+    const int L0 = (v0 & 31) + 32 * ((t0 >> 3) & 1);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {  // vocabulary entry v0 + m for tokens t0 .. t0 + 7
+      const int wi = m >> 1;
+      const bool hi = m & 1;
+      lds[qt_out_slot(F, L0 + m)] =
+          make_uint4(halves(u4get(v[0], wi), u4get(v[1], wi), hi), halves(u4get(v[2], wi), u4get(v[3], wi), hi),
+                     halves(u4get(v[4], wi), u4get(v[5], wi), hi), halves(u4get(v[6], wi), u4get(v[7], wi), hi));
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int F = 8 * w + k;  // vocabulary row group F / 16 of the 64-entry group, token step F % 16
+    const int vr = 64 * g + 32 * (F >> 4);
+    out[(((int64_t)(vr >> 8) * ks_t + 16 * tb + (F & 15)) * kFA + ((vr & 255) >> 5)) * 64 + lane] =
+        lds[qt_out_slot(F, lane)];
   }
 }
 
@@ -1940,11 +1956,11 @@ void backward_chunk(Launcher& L, const Plan& p, const T* W, const WCopies<T>& wc
         for (int64_t b0 = 0; b0 < p.ntiles_v; b0 += p.qt_tiles) {
           const int nb = (int)(p.ntiles_v - b0 < p.qt_tiles ? p.ntiles_v - b0 : p.qt_tiles);
           const int band0 = (int)(b0 * kTileA16);
-          const int64_t threads = (int64_t)(ks_t / 2) * (nb * kTileA16 / 16) * 8;  // 8 per Q fragment
+          const int tiles_t = ks_t / 16;  // 256-token tiles of the slice
           L.run(GRPO_K_QT_BAND, [&] {
-            hipLaunchKernelGGL(qt_band_kernel, dim3(grid1(threads, 256)), dim3(256), 0, L.stream,
-                               reinterpret_cast<const uint4*>(P), (int)p.ks_v, ks_t * 16, band0, nb * kTileA16,
-                               ks_t, reinterpret_cast<uint4*>(Qt));
+            hipLaunchKernelGGL(qt_band_kernel, dim3(tiles_t * nb * (kTileA16 / 64)), dim3(256), 0, L.stream,
+                               reinterpret_cast<const uint4*>(P), (int)p.ks_v, tiles_t, band0, ks_t,
+                               reinterpret_cast<uint4*>(Qt));
           });
           // A: (-c H)^T (rows = hidden units), B: the band of Q^T (rows = vocabulary entries)
           GemmArgs gw = {};
