@@ -201,6 +201,7 @@ def test_logp_bwd_validation():
     assert f(wsp=ctypes.c_void_p((1 << 20) + 16)) == 4
     assert f(shape(T=0), H=None, y=None, lse=None, g=None, dH=None) == 0  # nothing to do
     assert f(shape(dtype=1, D=64), dW=FAKE) == 5  # dW: bf16 only
+    assert f(dW=ctypes.c_void_p((1 << 20) + 8)) == 5  # dW: 16-byte aligned (its epilogue moves float4s)
 
 
 def test_ce_loss_validation():
