@@ -205,11 +205,11 @@ grpo_status make_plan(const grpo_shape* s, int64_t S, bool backward, Plan* out, 
       p.off_Wf = take(wf);
     }
     // dW: the GEMM's vocabulary-row operand (P' - onehot)^T, fragment-major, one band of
-    // vocabulary tiles at a time (16 tiles fill the GPU at D <= 4096); a narrower band where
-    // 16 would pass the bound, one tile at the least.
+    // vocabulary tiles at a time (32 tiles: two rounds of the GPU's workgroups at D = 4096); a
+    // narrower band where 32 would pass the bound, one tile at the least.
     if (bf16 && dW && p.nchunks > 0) {
       const size_t tile_bytes = (size_t)kTileA16 * (size_t)p.rows_pad * 2;
-      int64_t nb = 16;
+      int64_t nb = 32;
       while (nb > 1 && (nb > p.ntiles_v || off + align_up(nb * tile_bytes) > bound)) nb >>= 1;
       p.qt_tiles = nb;
       p.off_Qt = take(nb * tile_bytes);
