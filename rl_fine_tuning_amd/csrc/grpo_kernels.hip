@@ -98,22 +98,6 @@ __device__ __forceinline__ uint32_t u4get(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-// Zero the elements [n, 16 / sizeof(T)) of a 16-byte chunk.
-template <typename T>
-__device__ __forceinline__ uint4 keep_first(uint4 x, int n) {
-  uint32_t w[4] = {x.x, x.y, x.z, x.w};
-  if (sizeof(T) == 2) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (e >= n) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (e >= n) w[e] = 0;
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
 // LogitMap (grpo_plan.h): temperature tau, scale s = multiply / divide, softcap c.  Without
 // a cap zscale = dscale = s / tau; with it zscale = c / tau, dscale = s / tau, cap_in = s / c.
 
@@ -128,12 +112,13 @@ __device__ __forceinline__ float tanh_fast(float a) {
 
 struct GemmArgs {
   const void* a;      // LSE / PROBS: W [V, D] or its fragment-major copy.  DH: W [V, D], read
-                      // transposed.  DHT: the fragment-major copy of W^T
-  const void* b;      // LSE / PROBS: hidden-state chunk [rows, D].  DH: probabilities [rows, ldp]
+                      // transposed.  DHT: the fragment-major copy of W^T.  DW: (-c H)^T, fragment-major
+  const void* b;      // LSE / PROBS: hidden-state chunk [rows, D].  DH: probabilities [rows, ldp].
+                      // DW: the band of Q^T, fragment-major
   int64_t lda, ldb;   // row strides (elements)
-  int a_rows;         // rows of the MFMA A operand: V (LSE / PROBS) or D (DH)
-  int b_rows;         // tokens in the chunk
-  int K;              // reduction length: D (LSE / PROBS) or V (DH)
+  int a_rows;         // rows of the MFMA A operand: V (LSE / PROBS) or D (DH, DW)
+  int b_rows;         // tokens in the chunk (DW: rows of the band)
+  int K;              // reduction length: D (LSE / PROBS), V (DH) or the slice's tokens (DW)
   int k_len;          // DH: vocabulary entries per split; otherwise K
   int tiles_a_base;   // A tiles before the split factor
   int tiles_a, tiles_b;
@@ -151,10 +136,9 @@ struct GemmArgs {
   // DH
   const float* g;         // [b_rows]
   const float* zy;        // [b_rows]: target logits (the softcap's W[y] factor)
-  float* dw;              // DW: [V, D] fp32
+  float* dw;              // DW: [V, D] fp32, offset to the band's first vocabulary row
   int accumulate;         // DW: add to dw (later chunks) instead of overwriting it
   const int32_t* targets; // [b_rows]
-  const void* w;          // W, for the W[y] term
   void* dh;               // [b_rows, D] (ksplit == 1)
   float* part;            // [ksplit][b_rows][D] (ksplit > 1)
   int D;
@@ -339,8 +323,8 @@ struct TransTile<float> {
 // from global memory straight into registers, from a fragment-major copy of B in which
 // every 32-row x 16-k MFMA operand fragment is one contiguous 1 KB block.  The A tile
 // enters the ring by direct-to-LDS loads from the same layout when the workspace holds a
-// fragment-major copy of W (or W^T) (DmaFragA), else from row-major W (DmaTileA) or
-// transposed in registers on the way (TransTileA, TransTileQ).  Per 32 of K a workgroup
+// fragment-major copy of W, W^T or the dW operands (DmaFragA), else from row-major W
+// (DmaTileA) or transposed in registers on the way (TransTileA).  Per 32 of K a workgroup
 // moves 32 KB from L2 (16 KB of A, 4 x 4 KB of B) for 4.2 MFLOP.
 constexpr int kTA = kTileA16;           // A rows per workgroup
 constexpr int kTB = kTileB16;           // B rows per workgroup
@@ -1925,7 +1909,6 @@ void backward_chunk(Launcher& L, const Plan& p, const T* W, const WCopies<T>& wc
     gd.zy = zy_s;
     gd.g = g_s;
     gd.targets = targets_s;
-    gd.w = W;
     gd.dh = dH_s;
     gd.part = part;
     gd.V = (int)p.V;
