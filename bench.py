@@ -43,8 +43,11 @@ def parse():
     ap.add_argument("--no-entry-points", action="store_true",
                     help="skip timing grpo_logp_fwd / grpo_logp_bwd / grpo_ce_loss_fwd_bwd / grpo_advantages")
     ap.add_argument("--no-clocks", action="store_true",
-                    help="do not sample the shader clock and socket power (rocm-smi / amd-smi child processes); "
-                         "for runs under a profiler, whose preloaded library would follow those children")
+                    help="do not sample the shader clock and socket power (sysfs reads in a helper thread)")
+    ap.add_argument("--other-configs", default="1,2,4",
+                    help="short runs of these other workloads, reported under other_configs ('' = none)")
+    ap.add_argument("--other-steps", type=int, default=3)
+    ap.add_argument("--other-warmup", type=int, default=1)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for HBM counter scaling)")
     return ap.parse_args()
@@ -97,50 +100,93 @@ def measured_traffic(kernel, workload_is_profiled):
     return (float(m.group(1)) * ff + float(m.group(2)) * wf) * 1024.0
 
 
-def box_peak():
-    """CU count and max shader clock of the gfx950 agent from rocminfo, and the dense bf16
-    MFMA peak they imply (4096 flop per clock per CU); None where rocminfo is unavailable."""
-    import re
-    import subprocess
+def sysfs_dir(props):
+    """The PCI device directory of the GPU in sysfs (its clock and power files), or None."""
     try:
-        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+        d = f"/sys/bus/pci/devices/{props.pci_domain_id:04x}:{props.pci_bus_id:02x}:{props.pci_device_id:02x}.0"
+        return d if os.path.isdir(d) else None
     except Exception:
         return None
-    for agent in out.split("Agent ")[1:]:
-        if "gfx950" not in agent:
+
+
+def _read(path):
+    try:
+        with open(path) as f:
+            return f.read()
+    except Exception:
+        return None
+
+
+def sclk_levels(dev):
+    """(current MHz or None, max MHz or None) from the DPM table pp_dpm_sclk ('*' marks the
+    current level)."""
+    import re
+    txt = _read(os.path.join(dev, "pp_dpm_sclk")) if dev else None
+    if not txt:
+        return None, None
+    cur, top = None, None
+    for line in txt.splitlines():
+        m = re.search(r"(\d+)\s*Mhz", line, re.I)
+        if not m:
             continue
-        cu = re.search(r"Compute Unit:\s+(\d+)", agent)
-        clk = re.search(r"Max Clock Freq\. \(MHz\):\s+(\d+)", agent)
-        if cu and clk:
-            cus, mhz = int(cu.group(1)), int(clk.group(1))
-            return {"compute_units": cus, "max_sclk_mhz": mhz, "bf16_dense_tflops": cus * mhz * 1e6 * 4096 / 1e12}
-    return None
+        mhz = int(m.group(1))
+        top = mhz if top is None else max(top, mhz)
+        if "*" in line:
+            cur = mhz
+    return cur, top
+
+
+def box_peak(props, dev):
+    """CU count (device properties) and maximum shader clock (the DPM table) of the GPU, and
+    the dense bf16 MFMA peak they imply (4096 flop per clock per CU)."""
+    cus = int(props.multi_processor_count)
+    _, mhz = sclk_levels(dev)
+    if not mhz:
+        return {"compute_units": cus, "max_sclk_mhz": None, "bf16_dense_tflops": None}
+    return {"compute_units": cus, "max_sclk_mhz": mhz, "bf16_dense_tflops": cus * mhz * 1e6 * 4096 / 1e12,
+            "source": "device properties, pp_dpm_sclk"}
 
 
 class ClockSampler:
-    """Samples the shader clock (rocm-smi) and the socket power (amd-smi) from a helper
-    thread, each read in a child process, while the timed steps run."""
+    """Samples the shader clock and the socket power from sysfs files of the GPU (read in this
+    process by a helper thread: no child processes) while the timed steps run."""
 
-    def __init__(self, enabled=True):
+    def __init__(self, dev, enabled=True, period=0.1):
+        import glob
         import threading
-        self.enabled = enabled
+        self.dev = dev
+        self.enabled = enabled and dev is not None
+        self.period = period
         self.sclk, self.power = [], []
+        self.freq_file = self.power_file = None
+        if self.enabled:
+            for h in sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*"))):
+                if self.freq_file is None and _read(os.path.join(h, "freq1_input")):
+                    self.freq_file = os.path.join(h, "freq1_input")
+                for name in ("power1_average", "power1_input"):
+                    if self.power_file is None and _read(os.path.join(h, name)):
+                        self.power_file = os.path.join(h, name)
         self._stop = threading.Event()
         self._thread = threading.Thread(target=self._run, daemon=True)
 
+    def _sample(self):
+        if self.freq_file:
+            v = _read(self.freq_file)
+            if v and v.strip().isdigit():
+                self.sclk.append(int(v) / 1e6)  # Hz
+        else:
+            cur, _ = sclk_levels(self.dev)
+            if cur:
+                self.sclk.append(cur)
+        if self.power_file:
+            v = _read(self.power_file)
+            if v and v.strip().isdigit():
+                self.power.append(int(v) / 1e6)  # microwatts
+
     def _run(self):
-        import re
-        import subprocess
-        while not self._stop.is_set():
+        while not self._stop.wait(self.period):
             try:
-                out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=10).stdout
-                m = re.search(r"sclk clock level: \d+: \((\d+)Mhz\)", out)
-                if m and not self._stop.is_set():
-                    self.sclk.append(int(m.group(1)))
-                out = subprocess.run(["amd-smi", "metric", "-p"], capture_output=True, text=True, timeout=10).stdout
-                m = re.search(r"SOCKET_POWER:\s+(\d+)\s*W", out)
-                if m and not self._stop.is_set():
-                    self.power.append(int(m.group(1)))
+                self._sample()
             except Exception:
                 return
 
@@ -157,7 +203,9 @@ class ClockSampler:
     def summary(self):
         avg = lambda v: sum(v) / len(v) if v else None
         return {"sclk_mhz_avg": avg(self.sclk), "sclk_samples": len(self.sclk),
-                "socket_power_w_avg": avg(self.power), "power_samples": len(self.power)}
+                "socket_power_w_avg": avg(self.power), "power_samples": len(self.power),
+                "sources": {"sclk": self.freq_file or (os.path.join(self.dev, "pp_dpm_sclk") if self.dev else None),
+                            "power": self.power_file}}
 
 
 def cpu_baseline(case, n_tokens):
@@ -201,28 +249,18 @@ def cpu_baseline(case, n_tokens):
     return res
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py measures one GPU: this path runs on a single MI355X and has no multi-GPU mode "
-              "(run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
-    if args.copy_calibration:
-        copy_calibration()
-        return
-
+def prepare(cfg, chunk=0):
+    """Synthetic inputs of workload `cfg` resident on the GPU, a workspace, and the step: group
+    advantages, then grpo_loss_fwd_bwd (dH into a preallocated buffer)."""
     import numpy as np
     import torch
 
-    from rl_fine_tuning_amd import (Timer, grpo_advantages, grpo_ce_loss_fwd_bwd, grpo_logp_bwd, grpo_logp_fwd,
-                                    grpo_loss_fwd_bwd, grpo_workspace_bytes)
-    from synth import CONFIGS, make_config
+    from rl_fine_tuning_amd import grpo_advantages, grpo_logp_fwd, grpo_loss_fwd_bwd, grpo_workspace_bytes
+    from synth import make_config
 
-    cfg = args.config
-    spec = CONFIGS[cfg]
     t_gen = time.perf_counter()
     case = make_config(cfg)
-    C = args.chunk or case.chunk
+    C = chunk or case.chunk
     T, D, V, S, G = case.T, case.D, case.V, case.S, case.G
     log(f"config {cfg}: T={T} D={D} V={V} S={S} chunk={C}; inputs drawn in {time.perf_counter() - t_gen:.1f} s")
     dev = torch.device("cuda:0")
@@ -252,6 +290,118 @@ def main():
         return grpo_loss_fwd_bwd(H, W, targets, cu, old, ref, adv, C, dH=dH, workspace=ws, timer=timer,
                                  want_logp=False, want_token_loss=False, keep_chunk_logits=keep)
 
+    return dict(case=case, C=C, H=H, W=W, targets=targets, rewards=rewards, old=old, ref=ref, ws=ws,
+                ws_bytes=ws_bytes, dH=dH, adv=adv, step=step)
+
+
+def gemm_flops(T, D, V, C):
+    """Algorithmic flops of each GEMM kind over one step (2 rows D V per chunk each)."""
+    rows = [min(C, T - k * C) for k in range((T + C - 1) // C)]
+    f = sum(2.0 * r * D * V for r in rows)
+    return {"logits_lse": f, "probs": f, "dh_gemm": f}
+
+
+def short_run(cfg, steps, warmup):
+    """A short timing of the same step on another workload: tokens/s, MFMA fraction, per-GEMM
+    TFLOP/s (HIP events around each launch), workspace and peak extra memory."""
+    import torch
+
+    from rl_fine_tuning_amd import Timer
+    from synth import CONFIGS
+
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    w = prepare(cfg)
+    case, C, step = w["case"], w["C"], w["step"]
+    T, D, V = case.T, case.D, case.V
+    torch.cuda.synchronize()
+    base_mem = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    for _ in range(warmup):
+        step()
+    timer = Timer(16384)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(timer)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms = 1e3 * el / steps
+    gf = gemm_flops(T, D, V, C)
+    gemms = {}
+    for k, f in gf.items():
+        t_ms, n, _ = timer.read(k)
+        gemms[k] = {"tflops": f * steps / (t_ms * 1e-3) / 1e12 if t_ms else None, "launches_per_step": n / steps}
+    timer.close()
+    res = {"workload": CONFIGS[cfg]["workload"], "T": T, "D": D, "V": V, "chunk_tokens": C,
+           "tokens_per_s": T * steps / el, "ms_per_step": ms, "steps": steps, "warmup": warmup,
+           "mfma_frac_step": 6.0 * T * D * V / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), "gemms": gemms,
+           "workspace_bytes": w["ws_bytes"], "peak_extra_bytes": torch.cuda.max_memory_allocated() - base_mem}
+    del w, step
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    log(f"config {cfg}: {res['tokens_per_s']:.0f} tokens/s ({res['mfma_frac_step']:.3f} of peak)")
+    return res
+
+
+def provenance(torch):
+    """Where the numbers come from: hashes of the sources, the commit (when the tree is a git
+    checkout), the ROCm and torch versions, the workloads' seeds.  Files only, no child
+    processes."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES + ["include/grpo.h", "bench.py"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    head = None
+    try:
+        ref = open(os.path.join(ROOT, ".git", "HEAD")).read().strip()
+        if ref.startswith("ref: "):
+            name = ref[5:]
+            p = os.path.join(ROOT, ".git", name)
+            if os.path.exists(p):
+                head = open(p).read().strip()
+            else:
+                for line in open(os.path.join(ROOT, ".git", "packed-refs")):
+                    if line.strip().endswith(" " + name):
+                        head = line.split()[0]
+        else:
+            head = ref
+    except Exception:
+        head = None
+    rocm = _read("/opt/rocm/.info/version")
+    return {"sources_sha256": h.hexdigest(), "git_head": head, "rocm_version": rocm.strip() if rocm else None,
+            "torch": torch.__version__, "torch_hip": getattr(torch.version, "hip", None),
+            "seeds": {"rule": "synth.make_config(cfg) draws from PCG64(SeedSequence((1000 + cfg, stream, block)))",
+                      "headline": 1000 + 3}}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this path runs on a single MI355X and has no multi-GPU mode "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    from rl_fine_tuning_amd import (Timer, grpo_advantages, grpo_ce_loss_fwd_bwd, grpo_logp_bwd, grpo_logp_fwd,
+                                    grpo_loss_fwd_bwd, grpo_workspace_bytes)
+    from synth import CONFIGS, make_config
+
+    cfg = args.config
+    spec = CONFIGS[cfg]
+    w = prepare(cfg, args.chunk)
+    case, C, H, W, targets, rewards = w["case"], w["C"], w["H"], w["W"], w["targets"], w["rewards"]
+    old, ref, ws, ws_bytes, dH, adv, step = w["old"], w["ref"], w["ws"], w["ws_bytes"], w["dH"], w["adv"], w["step"]
+    T, D, V, S, G = case.T, case.D, case.V, case.S, case.G
+    dev = H.device
+    cu = case.cu
+
     torch.cuda.synchronize()
     base_mem = torch.cuda.memory_allocated()
     torch.cuda.reset_peak_memory_stats()
@@ -260,10 +410,12 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
     timer = Timer(16384)
-    peak_box = box_peak()
+    props = torch.cuda.get_device_properties(0)
+    dev_dir = sysfs_dir(props)
+    peak_box = box_peak(props, dev_dir)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    with ClockSampler(enabled=not args.no_clocks) as clocks:
+    with ClockSampler(dev_dir, enabled=not args.no_clocks) as clocks:
         t0 = time.perf_counter()
         for i in range(args.steps):
             evs[i].record()
@@ -281,9 +433,7 @@ def main():
     flops_step = 6.0 * T * D * V
     nchunks = (T + C - 1) // C
     rows = [min(C, T - k * C) for k in range(nchunks)]
-    gemm_flops = {"logits_lse": sum(2.0 * r * D * V for r in rows),
-                  "probs": sum(2.0 * r * D * V for r in rows),
-                  "dh_gemm": sum(2.0 * r * D * V for r in rows)}
+    gemm_flops = globals()["gemm_flops"](T, D, V, C)
     kernels = {}
     for k in ("target_logit", "logits_lse", "merge", "probs", "dh_gemm", "dh_reduce", "token_index",
               "loss_finalize", "frag_copy", "transpose_w", "w_copy", "onehot_fix"):
@@ -340,8 +490,8 @@ def main():
         "step_ms": {"median": step_ms[len(step_ms) // 2], "min": step_ms[0], "max": step_ms[-1],
                     "source": "HIP events around each timed step"},
         "clocks": dict(clocks.summary(), box=peak_box,
-                       note="sampled with rocm-smi / amd-smi during the timed steps; the roofline peak stays "
-                            "the published 2.5 PFLOP/s"),
+                       note="read from sysfs every 0.1 s during the timed steps; the roofline peak stays the "
+                            "published 2.5 PFLOP/s"),
         "workspace_bytes": ws_bytes,
         "peak_extra_bytes": peak_extra,
         "loss": loss,
@@ -413,6 +563,10 @@ def main():
                                   "grpo_advantages": {"us": 1e3 * ms_adv, "sequences": S}}
         log(f"entry points: logp_fwd {ms_f:.1f} ms, logp_bwd {ms_b:.1f} ms, ce {ms_ce:.1f} ms, "
             f"advantages {1e3 * ms_adv:.1f} us")
+    result["provenance"] = provenance(torch)
+    others = [int(x) for x in args.other_configs.split(",") if x.strip() and int(x) != cfg]
+    if others:
+        result["other_configs"] = {str(c): short_run(c, args.other_steps, args.other_warmup) for c in others}
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host")
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_sample_tokens)

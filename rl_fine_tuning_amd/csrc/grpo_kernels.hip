@@ -815,10 +815,193 @@ void gemm_kernel(const GemmArgs g) {
 // every wave's, and the A fragments of stage kt + 1, step 0 are read under the MFMAs of
 // step 1.  A ring slot is refilled only after the barrier that follows its last read.
 //
-// The tile body is instantiated per kind of tile, so that the common case (a tile inside
-// the matrix, unsplit K) has straight-line epilogues: kEdge marks the last tile along the
-// vocabulary (LSE / PROBS) or hidden (DH) axis, kSplit a dH tile of a split vocabulary.
-template <int KIND, bool kEdge, bool kSplit, bool kCap, bool kFragA>
+// Epilogue of a bf16 GEMM tile: straight-line code over the accumulators.  Rows of the last
+// vocabulary tile at or past V entered the main loop at -inf and stayed there (those rows of
+// W read as zero), so the logits epilogues need no masks: they add nothing to the max, their
+// exp is 0, and with a softcap they stay -inf.  Groups of 8 rows (32 i + 8 q + 0..7 of the
+// tile) past the stored width are skipped by uniform scalar tests.
+template <int KIND, bool kSplit, bool kCap>
+__device__ __forceinline__ void gemm16_epi(const GemmArgs& g, floatx16 (&acc)[kFA][kFBW], int ks, int tile_a,
+                                           int tb) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row_a0 = tile_a * kTA;
+  const int row_b0 = tb * kTB;
+  const int hi = lane >> 5;
+  const int col = lane & 31;
+  constexpr bool kLogits = KIND == KIND_LSE || KIND == KIND_PROBS || KIND == KIND_LSES;
+  // With a softcap the accumulators of token block j become v = tanh(cap_in x) (-inf stays
+  // -inf) at the start of that block's epilogue, one block at a time.
+  auto cap_block = [&](int j) {
+    if constexpr (kLogits && kCap) {
+#pragma unroll
+      for (int i = 0; i < kFA; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float x = acc[i][j][r];
+          const float t = tanh_fast(x * g.lm.cap_in);
+          acc[i][j][r] = x == -INFINITY ? x : t;
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  if constexpr (KIND == KIND_LSE || KIND == KIND_LSES) {
+    // Per token: max and sum of exp over this tile's vocabulary rows below V; KIND_LSES also
+    // keeps d = z - max (fp16, rounded to nearest) in the fragment-major layout of the
+    // probabilities (-inf past V).
+#pragma unroll
+    for (int j = 0; j < kFBW; ++j) {
+      cap_block(j);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < kFA; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));  // finite: row 0 of the tile is below V
+      const float zmax = mx * g.lm.zscale;  // zscale > 0, so this is the max of z
+      const int tok = row_b0 + 64 * w + 32 * j + col;
+      if constexpr (KIND == KIND_LSES) {
+        char* P = reinterpret_cast<char*>(g.p);
+        const int vpad = g.p_ks * 16 - row_a0;  // uniform; multiple of 16
+#pragma unroll
+        for (int i = 0; i < kFA; ++i) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int g0 = 32 * i + 8 * q;
+            if (__builtin_expect(g0 >= vpad, 0)) continue;
+            float d[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) d[u] = fmaf(acc[i][j][4 * q + u], g.lm.zscale, -zmax);
+            *reinterpret_cast<uint2*>(P + frag_off(tok, row_a0 + g0 + 4 * hi, g.p_ks)) =
+                make_uint2(pack_f16(d[0], d[1]), pack_f16(d[2], d[3]));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      const float c1 = g.lm.zscale * kLog2e, c0 = -zmax * kLog2e;
+      float sum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kFA; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], c1, c0));
+      sum += __shfl_xor(sum, 32);
+      if (hi == 0 && tok < g.b_rows) {
+        g.pm[(int64_t)tok * g.tiles_a + tile_a] = zmax;
+        g.ps[(int64_t)tok * g.tiles_a + tile_a] = sum;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else if constexpr (KIND == KIND_PROBS) {
+    // P'[token, v] = exp(z - lse[token]) (times 1 - v^2 with a softcap) into the
+    // fragment-major copy used as the B operand of the dH GEMM (the target entries are
+    // then rewritten by onehot_fix_kernel); the vocabulary padding up to the next 16 is
+    // written as zeros.  Rows of the copy past the chunk's tokens are written too (every
+    // consumer ignores them).
+    char* P = reinterpret_cast<char*>(g.p);
+    const int vpad = g.p_ks * 16 - row_a0;  // uniform; multiple of 16
+    const float c1 = g.lm.zscale * kLog2e;
+#pragma unroll
+    for (int j = 0; j < kFBW; ++j) {
+      cap_block(j);
+      const int tok = row_b0 + 64 * w + 32 * j + col;
+      const float c0 = -(tok < g.b_rows ? g.lse[tok] : 0.0f) * kLog2e;
+#pragma unroll
+      for (int i = 0; i < kFA; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int g0 = 32 * i + 8 * q;
+          if (__builtin_expect(g0 >= vpad, 0)) continue;
+          float e[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float x = acc[i][j][4 * q + u];
+            e[u] = __builtin_amdgcn_exp2f(fmaf(x, c1, c0));
+            if constexpr (kCap) e[u] = e[u] != 0.0f ? e[u] * (1.0f - x * x) : 0.0f;  // past V: x = -inf
+          }
+          store4(reinterpret_cast<__bf16*>(P + frag_off(tok, row_a0 + g0 + 4 * hi, g.p_ks)), e[0], e[1], e[2], e[3]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  } else if constexpr (KIND == KIND_DW) {
+    // dW[v, d] = acc (first chunk) or dW[v, d] + acc, fp32, with the hidden units d as the A
+    // rows and the band's vocabulary entries v as the B rows: acc = sum_t (-c_t H[t, d]) Q[t, v].
+    // A lane's 4 consecutive accumulator rows are 4 consecutive floats of a dW row.
+    float* dw = g.dw;
+    const int drem = g.D - row_a0;  // uniform; multiple of 8
+#pragma unroll
+    for (int j = 0; j < kFBW; ++j) {
+      const int v = row_b0 + 64 * w + 32 * j + col;
+      if (v >= g.V) continue;
+      float* row = dw + (int64_t)v * g.D;
+#pragma unroll
+      for (int i = 0; i < kFA; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (__builtin_expect(32 * i + 8 * q >= drem, 0)) continue;
+          float4* p = reinterpret_cast<float4*>(row + row_a0 + 32 * i + 8 * q + 4 * hi);
+          float4 o = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          if (g.accumulate) {
+            const float4 x = *p;
+            o.x += x.x;
+            o.y += x.y;
+            o.z += x.z;
+            o.w += x.w;
+          }
+          *p = o;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  } else {
+    // dH[token, d] = -c acc with acc = sum_v Q[token, v] W[v, d] (+0 rows for tokens without
+    // a gradient), or the raw fp32 partial when split.
+    const int drem = g.D - row_a0;  // uniform; multiple of 8
+#pragma unroll
+    for (int j = 0; j < kFBW; ++j) {
+      const int tok = row_b0 + 64 * w + 32 * j + col;
+      const bool ok = tok < g.b_rows;
+      if constexpr (kSplit) {
+        float* dst = g.part + ((int64_t)ks * g.b_rows + (ok ? tok : 0)) * g.D;
+#pragma unroll
+        for (int i = 0; i < kFA; ++i) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (__builtin_expect(32 * i + 8 * q >= drem, 0)) continue;
+            const int d0 = row_a0 + 32 * i + 8 * q + 4 * hi;
+            const float4 o =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            if (ok) *reinterpret_cast<float4*>(dst + d0) = o;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        continue;
+      }
+      const TokGrad tg = tok_grad(g.g, g.targets, g.zy, g.V, g.lm, tok, ok);
+      const float nc = -tg.c;
+      __bf16* dst = reinterpret_cast<__bf16*>(g.dh) + (int64_t)(ok ? tok : 0) * g.D;
+#pragma unroll
+      for (int i = 0; i < kFA; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (__builtin_expect(32 * i + 8 * q >= drem, 0)) continue;
+          const int d0 = row_a0 + 32 * i + 8 * q + 4 * hi;
+          float o[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) o[u] = tg.live ? nc * acc[i][j][4 * q + u] : 0.0f;
+          if (ok) store4(dst + d0, o[0], o[1], o[2], o[3]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+}
+
+// One kernel holds one tile body: the softcap (kCap), the A operand's layout (kFragA) and a
+// split vocabulary (kSplit, dH) are chosen on the host, so register allocation covers a
+// single main loop and epilogue.
+template <int KIND, bool kSplit, bool kCap, bool kFragA>
 __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int ks, int tile_a, int tb) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -837,6 +1020,19 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
     for (int j = 0; j < kFBW; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  if constexpr (KIND == KIND_LSE || KIND == KIND_PROBS || KIND == KIND_LSES) {
+    if (row_a0 + kTA > g.V) {  // uniform: the last vocabulary tile; its rows past V start at -inf
+      const int vlim_l = g.V - row_a0 - 4 * (lane >> 5);  // A-row 32 i + 8 (r / 4) + 4 (l / 32) + r % 4
+#pragma unroll
+      for (int i = 0; i < kFA; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float v0 = 32 * i + 8 * (r >> 2) + (r & 3) < vlim_l ? 0.0f : -INFINITY;
+#pragma unroll
+          for (int j = 0; j < kFBW; ++j) acc[i][j][r] = v0;
+        }
+    }
+  }
 
   const __bf16* A = reinterpret_cast<const __bf16*>(g.a);
   // this wave's 64 rows of the B tile in the fragment-major copy
@@ -948,231 +1144,21 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
     __builtin_amdgcn_s_barrier();
   }
 
-  const int hi = lane >> 5;
-  const int col = lane & 31;
-  // Epilogues without per-element bounds masks: in a tile that crosses the end of the
-  // vocabulary, a one-time pass sets the accumulators of rows >= V to -inf (exp gives 0,
-  // max ignores them); column bounds of 8-aligned groups are wave-uniform scalar tests
-  // (every limit is a multiple of 8 and the tile origin of 256); only stores depend on
-  // the lane's token.  With a softcap the accumulators first become v = tanh(cap_in x).
-  constexpr bool kLogits = KIND == KIND_LSE || KIND == KIND_PROBS || KIND == KIND_LSES;
-  if constexpr (kLogits && kCap) {
-#pragma unroll
-    for (int i = 0; i < kFA; ++i) {
-#pragma unroll
-      for (int j = 0; j < kFBW; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = tanh_fast(acc[i][j][r] * g.lm.cap_in);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  if constexpr (kLogits && kEdge) {
-    {
-#pragma unroll
-      for (int i = 0; i < kFA; ++i) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bool out = row_a0 + 4 * hi + 32 * i + 8 * (r >> 2) + (r & 3) >= g.V;
-#pragma unroll
-          for (int j = 0; j < kFBW; ++j) acc[i][j][r] = out ? -INFINITY : acc[i][j][r];
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  }
-  if constexpr (KIND == KIND_LSE || KIND == KIND_LSES) {
-    // Per token: max and sum of exp over this tile's 256 vocabulary rows (those < V);
-    // KIND_LSES also keeps d = z - max (fp16, rounded to nearest) in the fragment-major
-    // layout of the probabilities, -inf past V.
-#pragma unroll
-    for (int j = 0; j < kFBW; ++j) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < kFA; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float zmax = mx * g.lm.zscale;  // zscale > 0, so this is the max of z
-      if constexpr (KIND == KIND_LSES) {
-        char* P = reinterpret_cast<char*>(g.p);
-        const int vrem = g.p_ks * 16 - row_a0;  // uniform; multiple of 16
-        const int tok = row_b0 + 64 * w + 32 * j + col;
-#pragma unroll
-        for (int i = 0; i < kFA; ++i) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (kEdge && 32 * i + 8 * q >= vrem) continue;
-            const int v0 = row_a0 + 32 * i + 8 * q + 4 * hi;
-            float d[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) d[u] = fmaf(acc[i][j][4 * q + u], g.lm.zscale, -zmax);
-            *reinterpret_cast<uint2*>(P + frag_off(tok, v0, g.p_ks)) =
-                make_uint2(pack_f16(d[0], d[1]), pack_f16(d[2], d[3]));
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      float sum = 0.0f;
-      if (mx > -INFINITY) {
-        const float c1 = g.lm.zscale * kLog2e, c0 = -zmax * kLog2e;
-#pragma unroll
-        for (int i = 0; i < kFA; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], c1, c0));
-      }
-      sum += __shfl_xor(sum, 32);
-      const int tok = row_b0 + 64 * w + 32 * j + col;
-      if (hi == 0 && tok < g.b_rows) {
-        g.pm[(int64_t)tok * g.tiles_a + tile_a] = zmax;
-        g.ps[(int64_t)tok * g.tiles_a + tile_a] = sum;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  } else if constexpr (KIND == KIND_PROBS) {
-    // P'[token, v] = exp(z - lse[token]) (times 1 - v^2 with a softcap) into the
-    // fragment-major copy used as the B operand of the dH GEMM (the target entries are
-    // then rewritten by onehot_fix_kernel); the vocabulary padding up to the next 16 is
-    // written as zeros.  Rows of the copy past the chunk's tokens are written too (every
-    // consumer ignores them).
-    char* P = reinterpret_cast<char*>(g.p);
-    const int vrem = g.p_ks * 16 - row_a0;  // uniform; multiple of 16
-    const float c1 = g.lm.zscale * kLog2e;
-#pragma unroll
-    for (int j = 0; j < kFBW; ++j) {
-      const int tok = row_b0 + 64 * w + 32 * j + col;
-      const float c0 = -(tok < g.b_rows ? g.lse[tok] : 0.0f) * kLog2e;
-#pragma unroll
-      for (int i = 0; i < kFA; ++i) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (kEdge && 32 * i + 8 * q >= vrem) continue;
-          const int v0 = row_a0 + 32 * i + 8 * q + 4 * hi;
-          float e[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const float x = acc[i][j][4 * q + u];
-            e[u] = __builtin_amdgcn_exp2f(fmaf(x, c1, c0));
-            if constexpr (kCap) e[u] = e[u] != 0.0f ? e[u] * (1.0f - x * x) : 0.0f;  // masked: x = -inf
-          }
-          store4(reinterpret_cast<__bf16*>(P + frag_off(tok, v0, g.p_ks)), e[0], e[1], e[2], e[3]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  } else if constexpr (KIND == KIND_DW) {
-    // dW[v, d] = acc (first chunk) or dW[v, d] + acc, fp32, with the hidden units d as the A
-    // rows and the band's vocabulary entries v as the B rows: acc = sum_t (-c_t H[t, d]) Q[t, v].
-    // A lane's 4 consecutive accumulator rows are 4 consecutive floats of a dW row.
-    float* dw = g.dw;
-    const int drem = g.D - row_a0;  // uniform; multiple of 8
-#pragma unroll
-    for (int j = 0; j < kFBW; ++j) {
-      const int v = row_b0 + 64 * w + 32 * j + col;
-      if (v >= g.V) continue;
-      float* row = dw + (int64_t)v * g.D;
-#pragma unroll
-      for (int i = 0; i < kFA; ++i) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (kEdge && 32 * i + 8 * q >= drem) continue;
-          float4* p = reinterpret_cast<float4*>(row + row_a0 + 32 * i + 8 * q + 4 * hi);
-          float4 o = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-          if (g.accumulate) {
-            const float4 x = *p;
-            o.x += x.x;
-            o.y += x.y;
-            o.z += x.z;
-            o.w += x.w;
-          }
-          *p = o;
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  } else {
-    // dH[token, d] = -c acc with acc = sum_v Q[token, v] W[v, d] (+0 rows for tokens without
-    // a gradient), or the raw fp32 partial when split.
-    const int drem = g.D - row_a0;  // uniform; multiple of 8
-#pragma unroll
-    for (int j = 0; j < kFBW; ++j) {
-      const int tok = row_b0 + 64 * w + 32 * j + col;
-      const bool ok = tok < g.b_rows;
-      if constexpr (kSplit) {
-        float* dst = g.part + ((int64_t)ks * g.b_rows + (ok ? tok : 0)) * g.D;
-#pragma unroll
-        for (int i = 0; i < kFA; ++i) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (kEdge && 32 * i + 8 * q >= drem) continue;
-            const int d0 = row_a0 + 32 * i + 8 * q + 4 * hi;
-            const float4 o =
-                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-            if (ok) *reinterpret_cast<float4*>(dst + d0) = o;
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        continue;
-      }
-      const TokGrad tg = tok_grad(g.g, g.targets, g.zy, g.V, g.lm, tok, ok);
-      const float nc = -tg.c;
-      __bf16* dst = reinterpret_cast<__bf16*>(g.dh) + (int64_t)(ok ? tok : 0) * g.D;
-#pragma unroll
-      for (int i = 0; i < kFA; ++i) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (kEdge && 32 * i + 8 * q >= drem) continue;
-          const int d0 = row_a0 + 32 * i + 8 * q + 4 * hi;
-          float o[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) o[u] = tg.live ? nc * acc[i][j][4 * q + u] : 0.0f;
-          if (ok) store4(dst + d0, o[0], o[1], o[2], o[3]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  }
+  gemm16_epi<KIND, kSplit, kCap>(g, acc, ks, tile_a, tb);
 }
 
-template <int KIND>
+template <int KIND, bool kSplit, bool kCap, bool kFragA>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm16_kernel(const GemmArgs g) {
   __shared__ __attribute__((aligned(16))) char smem[kStagesA * kAStageBytes];
   int ta, tb;
   if (!map_tile(g, ta, tb)) return;
-  constexpr bool kDH = KIND == KIND_DH || KIND == KIND_DHT;
   int ks = 0, tile_a = ta;
-  if (kDH) {
+  if constexpr (KIND == KIND_DH || KIND == KIND_DHT) {
     ks = ta / g.tiles_a_base;
     tile_a = ta - ks * g.tiles_a_base;
   }
-  const bool edge = (tile_a + 1) * kTA > ((kDH || KIND == KIND_DW) ? g.D : g.V);
-  if constexpr (kDH) {
-    constexpr bool kFrag = KIND == KIND_DHT;
-    if (g.ksplit > 1) {
-      if (edge) gemm16_tile<KIND, true, true, false, kFrag>(g, smem, ks, tile_a, tb);
-      else gemm16_tile<KIND, false, true, false, kFrag>(g, smem, ks, tile_a, tb);
-    } else {
-      if (edge) gemm16_tile<KIND, true, false, false, kFrag>(g, smem, ks, tile_a, tb);
-      else gemm16_tile<KIND, false, false, false, kFrag>(g, smem, ks, tile_a, tb);
-    }
-  } else if constexpr (KIND == KIND_DW) {
-    if (edge) gemm16_tile<KIND, true, false, false, true>(g, smem, ks, tile_a, tb);
-    else gemm16_tile<KIND, false, false, false, true>(g, smem, ks, tile_a, tb);
-  } else if (g.a_frag) {
-    if (g.lm.cap_in > 0.0f) {
-      if (edge) gemm16_tile<KIND, true, false, true, true>(g, smem, ks, tile_a, tb);
-      else gemm16_tile<KIND, false, false, true, true>(g, smem, ks, tile_a, tb);
-    } else {
-      if (edge) gemm16_tile<KIND, true, false, false, true>(g, smem, ks, tile_a, tb);
-      else gemm16_tile<KIND, false, false, false, true>(g, smem, ks, tile_a, tb);
-    }
-  } else if (g.lm.cap_in > 0.0f) {
-    if (edge) gemm16_tile<KIND, true, false, true, false>(g, smem, ks, tile_a, tb);
-    else gemm16_tile<KIND, false, false, true, false>(g, smem, ks, tile_a, tb);
-  } else {
-    if (edge) gemm16_tile<KIND, true, false, false, false>(g, smem, ks, tile_a, tb);
-    else gemm16_tile<KIND, false, false, false, false>(g, smem, ks, tile_a, tb);
-  }
+  gemm16_tile<KIND, kSplit, kCap, kFragA>(g, smem, ks, tile_a, tb);
 }
 
 // Fragment-major copy of `rows` rows of a row-major bf16 matrix [rows, K] (ld = K), rows
@@ -1276,10 +1262,10 @@ __global__ __launch_bounds__(256) void probs_from_kept_kernel(uint4* __restrict_
   P[u] = out;
 }
 
-// Q[t, y_t] = P'[t, y_t] - wyf_t, computed in fp32 from the target logit and the log-sum-exp
-// and rounded once: for a confident token (P'_y near 1) the difference keeps its relative
-// precision.  One thread per token of the chunk; tokens with a target outside [0, V) are
-// left alone (their rows get no weight).
+// Q[t, y_t] = P'[t, y_t] - wyf_t = wyf_t (e^{logp_t} - 1) = wyf_t expm1(z_y - lse), computed in
+// fp32 and rounded once: for a confident token (P'_y near 1) the difference keeps its full
+// relative precision, where e^{logp} - 1 would cancel.  One thread per token of the chunk;
+// tokens with a target outside [0, V) are left alone (their rows get no weight).
 template <typename T>
 __global__ __launch_bounds__(256) void onehot_fix_kernel(T* __restrict__ P, int rows, int ks_count, int64_t ldp,
                                                          const int32_t* __restrict__ targets_c,
@@ -1290,14 +1276,12 @@ __global__ __launch_bounds__(256) void onehot_fix_kernel(T* __restrict__ P, int 
   const int y = targets_c[t];
   if (y < 0 || y >= V) return;
   const float zy = zy_c[t];
-  float p = __builtin_amdgcn_exp2f((zy - lse_c[t]) * kLog2e);
   float wyf = 1.0f;
   if (lm.cap_in > 0.0f) {
     const float v = zy / lm.zscale;
     wyf = 1.0f - v * v;
-    p *= wyf;
   }
-  const float q = p - wyf;
+  const float q = wyf * expm1f(zy - lse_c[t]);  // zy - lse is the token's logp, bit for bit
   if constexpr (sizeof(T) == 2) {
     char* dst = reinterpret_cast<char*>(P) + frag_off(t, y, ks_count);
     *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(pack_bf16(q, 0.0f) & 0xffffu);
@@ -1717,15 +1701,33 @@ struct Launcher {
 
 inline int grid1(int64_t n, int per) { return (int)((n + per - 1) / per); }
 
+// The bf16 kernel that holds this call's tile body (softcap, A layout and split are fixed
+// per launch).
+template <int KIND>
+void (*gemm16_pick(const GemmArgs& g))(const GemmArgs) {
+  if constexpr (KIND == KIND_DH || KIND == KIND_DHT) {
+    constexpr bool kFrag = KIND == KIND_DHT;
+    return g.ksplit > 1 ? gemm16_kernel<KIND, true, false, kFrag> : gemm16_kernel<KIND, false, false, kFrag>;
+  } else if constexpr (KIND == KIND_DW) {
+    return gemm16_kernel<KIND, false, false, true>;
+  } else {
+    const bool cap = g.lm.cap_in > 0.0f;
+    if (g.a_frag) return cap ? gemm16_kernel<KIND, false, true, true> : gemm16_kernel<KIND, false, false, true>;
+    return cap ? gemm16_kernel<KIND, false, true, false> : gemm16_kernel<KIND, false, false, false>;
+  }
+}
+
 template <typename T, int KIND>
 void launch_gemm(Launcher& L, int kid, const GemmArgs& g) {
   // the largest share of one XCD (the ranges of map_tile differ by at most one tile)
   const int per_xcd = (int)cdiv(g.tiles_a, g.xcd_a) * (int)cdiv(g.tiles_b, 8 / g.xcd_a);
   const int blocks = 8 * per_xcd;
-  if constexpr (sizeof(T) == 2)
-    L.run(kid, [&] { hipLaunchKernelGGL((gemm16_kernel<KIND>), dim3(blocks), dim3(kThreads), 0, L.stream, g); });
-  else
+  if constexpr (sizeof(T) == 2) {
+    void (*k)(const GemmArgs) = gemm16_pick<KIND>(g);
+    L.run(kid, [&] { hipLaunchKernelGGL(k, dim3(blocks), dim3(kThreads), 0, L.stream, g); });
+  } else {
     L.run(kid, [&] { hipLaunchKernelGGL((gemm_kernel<T, KIND>), dim3(blocks), dim3(kThreads), 0, L.stream, g); });
+  }
 }
 
 // Tokens' operand of the bf16 logits GEMMs: the fragment-major copy of the chunk's rows.

@@ -8,7 +8,7 @@ import torch
 import oracle
 from rl_fine_tuning_amd import Timer, grpo_ce_loss_fwd_bwd, grpo_logp_bwd, grpo_logp_fwd, grpo_loss_fwd_bwd
 
-from gpu_cases import DH_REL_L2, backward_passes, case, check_loss_outputs, rel_l2, say, to_device
+from gpu_cases import DH_REL_L2, backward_passes, case, check_loss_outputs, check_rows, say, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -44,9 +44,8 @@ def test_grpo_loss_dW(D, V, lengths, chunk, tau, cap, keep):
     assert tm.read("w_copy")[1] == int(info["w_copy"])
     tm.close()
     check_loss_outputs(k, got)  # dH and the forward outputs are unchanged by asking for dW
-    e = rel_l2(got["dW"].cpu().numpy(), ref["dW"])
-    say(f"  dW rel L2 {e:.2e}")
-    assert e <= DH_REL_L2
+    worst, e = check_rows(got["dW"].cpu().numpy(), ref["dW"], DH_REL_L2, "dW")
+    say(f"  dW worst row {worst:.2e}, whole {e:.2e}")
 
 
 def test_logp_bwd_and_ce_dW():
@@ -58,16 +57,14 @@ def test_logp_bwd_and_ce_dW():
     _, lse = grpo_logp_fwd(d["H"], d["W"], d["targets"], 512, return_lse=True)
     dH, dW = grpo_logp_bwd(d["H"], d["W"], d["targets"], lse, torch.from_numpy(grad).cuda(), 512, dW=True)
     rdH, rdW = oracle.logp_backward(k["H64"], k["W64"], k["targets"], grad.astype(np.float64), with_dW=True)
-    e = rel_l2(dW.cpu().numpy(), rdW)
-    say(f"dW logp_bwd rel L2 {e:.2e}")
-    assert e <= DH_REL_L2
+    worst, e = check_rows(dW.cpu().numpy(), rdW, DH_REL_L2, "dW")
+    say(f"dW logp_bwd worst row {worst:.2e}, whole {e:.2e}")
     mask = np.ones(T, np.uint8)
     mask[6] = 0
     out = oracle.cross_entropy_loss_and_grad(k["H64"], k["W64"], k["targets"], mask, with_dW=True)
     got = grpo_ce_loss_fwd_bwd(d["H"], d["W"], d["targets"], 512, mask=torch.from_numpy(mask).cuda(), dW=True)
-    e = rel_l2(got["dW"].cpu().numpy(), out["dW"])
-    say(f"dW ce rel L2 {e:.2e}")
-    assert e <= DH_REL_L2
+    worst, e = check_rows(got["dW"].cpu().numpy(), out["dW"], DH_REL_L2, "dW")
+    say(f"dW ce worst row {worst:.2e}, whole {e:.2e}")
 
 
 def test_dW_without_tokens_is_zero():

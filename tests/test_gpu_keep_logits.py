@@ -8,7 +8,7 @@ import torch
 import oracle
 from rl_fine_tuning_amd import Timer, grpo_ce_loss_fwd_bwd, grpo_loss_fwd_bwd
 
-from gpu_cases import DH_REL_L2, backward_passes, case, check_loss_outputs, host_matrix, rel_l2, say, to_device
+from gpu_cases import DH_REL_L2, backward_passes, case, check_loss_outputs, check_rows, host_matrix, say, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -43,9 +43,9 @@ def test_grpo_loss_keeping_chunk_logits(D, V, lengths, chunk, tau, cap):
     base = grpo_loss_fwd_bwd(d["H"], d["W"], d["targets"], k["c"].cu, d["old"], d["ref"], d["adv"], chunk, **kw)
     for key in ("loss", "logp", "token_loss"):
         assert torch.equal(torch.nan_to_num(kept[key], nan=7.0), torch.nan_to_num(base[key], nan=7.0)), key
-    rel = (kept["dH"].float() - base["dH"].float()).norm() / base["dH"].float().norm()
-    say(f"  dH kept vs recomputed rel L2 {rel.item():.2e}")
-    assert rel.item() <= 5e-3
+    worst, rel = check_rows(kept["dH"].float().cpu().numpy(), base["dH"].float().cpu().numpy(), DH_REL_L2)
+    say(f"  dH kept vs recomputed: worst row {worst:.2e}, whole {rel:.2e}")
+    assert rel <= 5e-3
 
 
 def test_ce_keeping_chunk_logits():
@@ -60,6 +60,5 @@ def test_ce_keeping_chunk_logits():
     torch.cuda.synchronize()
     assert torch.equal(kept["loss"], base["loss"])
     assert abs(float(kept["loss"].cpu()[0]) - out["loss"]) <= 1e-4 * abs(out["loss"])
-    e = rel_l2(oracle.widen(host_matrix(kept["dH"], "bf16"), "bf16"), out["dH"])
-    say(f"keep logits ce: dH rel L2 {e:.2e}")
-    assert e <= DH_REL_L2
+    worst, e = check_rows(oracle.widen(host_matrix(kept["dH"], "bf16"), "bf16"), out["dH"], DH_REL_L2)
+    say(f"keep logits ce: dH worst row {worst:.2e}, whole {e:.2e}")

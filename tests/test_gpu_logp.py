@@ -92,8 +92,8 @@ def test_peaked_softmax(w_std):
     lp, lse = run_logp(c, 128)
     ref, _ = oracle_logp(c)
     assert np.all(np.isfinite(lp)) and np.all(np.isfinite(lse))
-    # logits reach |z| ~ 3e2 here: fp32 rounding of z bounds the error
-    assert np.abs(lp - ref).max() <= LOGP_ATOL * max(1.0, w_std)
+    # logits reach |z| ~ 3e2 here; the per-token bar is still 1e-3
+    assert np.abs(lp - ref).max() <= LOGP_ATOL
 
 
 def test_out_of_range_targets_give_nan_only_there():

@@ -8,7 +8,7 @@ import oracle
 from rl_fine_tuning_amd import grpo_logp_fwd, grpo_loss_fwd_bwd
 from synth import make_config
 
-from gpu_cases import backward_passes, case, check_loss_outputs, dev_matrix, f32, say, to_device
+from gpu_cases import backward_passes, case, check_loss_outputs, check_rows, dev_matrix, f32, say, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -29,9 +29,8 @@ def test_config0_tiny_fp32():
              rewards=("bernoulli", 0.5))
     got = run_loss(k, c.chunk)
     torch.cuda.synchronize()
-    r = check_loss_outputs(k, got)
+    r = check_loss_outputs(k, got, dh_bar=1e-4)  # fp32 probabilities and dH: 1e-4 per row
     assert r["logp_err"] <= 1e-5
-    assert r["dH_rel"] <= 1e-4  # fp32 probabilities and dH
 
 
 @pytest.mark.parametrize("D,V,lengths,G,chunk,tau,beta,agg,mask_frac", [
@@ -59,6 +58,31 @@ def test_config_noise_levels_bf16():
     got = run_loss(k, 512)
     torch.cuda.synchronize()
     check_loss_outputs(k, got)
+
+
+def test_small_gradient_rows_at_their_own_scale():
+    # beta = 0.001 with the reference at the workloads' noise, groups whose rewards are all
+    # equal (A = 0) and tokens pushed past the clip range: those rows carry only the KL term
+    # beta (1 - e^delta) w_t, orders of magnitude below the others.  Each dH row is held to
+    # the bar relative to its own norm, so an error in g_t on them cannot hide.
+    k = case(61, D=384, V=3000, lengths=[300, 260, 340, 200, 280, 310, 150, 240], G=2, chunk=512,
+             rewards=("bernoulli", 0.5), old_std=0.3, ref_std=0.05, beta=0.001)
+    o = k["oracle"]
+    s = oracle.sequence_of_token(k["c"].cu)
+    A = k["adv"].astype(np.float64)[s]
+    rho = np.exp(o["logp"] - k["old"])
+    clipped = ((A > 0) & (rho > 1.2)) | ((A < 0) & (rho < 0.8))
+    kl_only = (A == 0) | clipped
+    assert np.sum(A == 0) > 0 and np.sum(clipped) > 0, "the case must hold zero-advantage and clipped tokens"
+    n_small = np.linalg.norm(o["dH"][kl_only], axis=1)
+    n_big = np.linalg.norm(o["dH"][~kl_only], axis=1)
+    assert np.median(n_small) < 1e-2 * np.median(n_big)
+    say(f"loss small rows: {int(kl_only.sum())} KL-only rows of {k['T']}, median norm ratio "
+        f"{np.median(n_small) / np.median(n_big):.1e}")
+    got = run_loss(k, 512)
+    torch.cuda.synchronize()
+    r = check_loss_outputs(k, got)
+    say(f"  dH worst row {r['dH_row_worst']:.2e}, whole {r['dH_rel']:.2e}")
 
 
 def test_well_conditioned_loss_relative_error():
@@ -95,8 +119,9 @@ def test_chunk_invariance_and_determinism():
         got = run_loss(k, chunk, d)
         for key in ("loss", "logp", "token_loss"):
             assert torch.equal(got[key], base[key]), (chunk, key)
-        rel = (got["dH"].float() - base["dH"].float()).norm() / base["dH"].float().norm()
-        assert rel.item() <= 1e-3, (chunk, rel.item())
+        # dH: the dH GEMM's vocabulary split follows the backward slice's token count, so the
+        # fp32 summation order (not the value) may change with the chunk size
+        check_rows(got["dH"].float().cpu().numpy(), base["dH"].float().cpu().numpy(), 1e-3)
 
 
 def test_logp_bitwise_equal_to_logp_fwd_and_on_policy_identity():
@@ -128,8 +153,7 @@ def test_fp32_ragged_with_mask():
     say("loss fp32 ragged masked")
     got = run_loss(k, 50)
     torch.cuda.synchronize()
-    r = check_loss_outputs(k, got)
-    assert r["dH_rel"] <= 1e-4
+    check_loss_outputs(k, got, dh_bar=1e-4)
 
 
 @pytest.mark.parametrize("V,chunk,expect_wt", [(10000, 512, 1), (1000, 256, 0)])
@@ -159,7 +183,7 @@ def test_dh_gemm_both_operand_paths(V, chunk, expect_wt):
 def test_confident_tokens_dH():
     # Softmax concentrated on the target (p_y near 1): dH = (g/tau)(W[y] - sum p W) is a
     # small difference of large terms; the target entry is formed in fp32 before rounding.
-    from gpu_cases import rel_l2, host_matrix
+    from gpu_cases import dh_rows_at, host_matrix, rel_l2
     k = case(101, D=128, V=700, lengths=[200, 150], G=2, chunk=128, w_std=2.0)
     H64, W64 = k["H64"], k["W64"]
     z = H64 @ W64.T
@@ -174,8 +198,17 @@ def test_confident_tokens_dH():
                             None, d["adv"], 128, beta=0.0)
     dH = oracle.widen(host_matrix(got["dH"], "bf16"), "bf16")
     e = rel_l2(dH, out["dH"])
-    say(f"confident tokens: median p_y {np.median(np.exp(lp)):.3f}, dH rel L2 {e:.2e}")
-    assert e <= 1e-2
+    assert e <= 1e-2, e
+    # row by row at the GPU's own logp: a saturated softmax (1 - p_y below fp32 resolution, a
+    # third of these tokens) has a row set by the fp32 logp; its target entry -expm1(logp)
+    # must still come out at full relative precision
+    lp_gpu = got["logp"].cpu().numpy().astype(np.float64)
+    s = oracle.sequence_of_token(k["c"].cu)
+    terms = oracle.grpo_token_terms(lp_gpu, old.astype(np.float64), None, k["adv"].astype(np.float64)[s], beta=0.0)
+    g = oracle.token_weights(k["c"].cu, k["mask"]) * terms["dell"]
+    ref_at = dh_rows_at(H64, W64, y, out["lse"], lp_gpu, g)
+    worst, _ = check_rows(dH, ref_at, 1e-2)
+    say(f"confident tokens: median p_y {np.median(np.exp(lp)):.3f}, dH worst row {worst:.2e}, whole {e:.2e}")
 
 
 def test_many_sequences_seq_mean():
@@ -216,8 +249,7 @@ def test_sliced_backward_uneven_slices_match_whole_chunks():
     for name in ("loss", "logp", "token_loss"):  # bit patterns: the invalid target's logp is NaN
         bits = torch.int64 if a[name].dtype == torch.float64 else torch.int32
         assert torch.equal(a[name].view(bits), b[name].view(bits)), name
-    rel = (a["dH"].float() - b["dH"].float()).norm() / b["dH"].float().norm()
-    assert rel.item() <= 1e-3, rel.item()
+    check_rows(a["dH"].float().cpu().numpy(), b["dH"].float().cpu().numpy(), 1e-3)
 
 
 @pytest.mark.parametrize("agg", ["seq_mean", "token_mean"])

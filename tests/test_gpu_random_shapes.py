@@ -10,7 +10,7 @@ import torch
 import oracle
 from rl_fine_tuning_amd import grpo_loss_fwd_bwd, grpo_plan_info
 
-from gpu_cases import DH_REL_L2, case, check_loss_outputs, rel_l2, say, to_device
+from gpu_cases import DH_REL_L2, case, check_loss_outputs, check_rows, say, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -51,13 +51,12 @@ def test_random_shape_matches_oracle(i):
                             temperature=p["tau"], logit_scale_multiply=p["scale"], logit_softcapping=p["cap"],
                             mask=d["mask"], keep_chunk_logits=p["keep"], dW=True if p["dW"] else None, **k["prm"])
     torch.cuda.synchronize()
-    r = check_loss_outputs(k, got)
-    say(f"  logp err {r['logp_err']:.2e} dH rel {r['dH_rel']:.2e}")
+    r = check_loss_outputs(k, got, dh_bar=1e-4 if p["dtype"] == "f32" else DH_REL_L2)
+    say(f"  logp err {r['logp_err']:.2e} dH worst row {r['dH_row_worst']:.2e}, whole {r['dH_rel']:.2e}")
     if p["dW"]:
         ref = oracle.grpo_loss_and_grad(k["H64"], k["W64"], k["targets"], k["c"].cu, k["mask"],
                                         k["old"].astype(np.float64), k["ref"].astype(np.float64),
                                         k["adv"].astype(np.float64), p["tau"], scale=p["scale"],
                                         softcap=p["cap"], with_dW=True, **k["prm"])
-        e = rel_l2(got["dW"].cpu().numpy(), ref["dW"])
-        say(f"  dW rel L2 {e:.2e}")
-        assert e <= DH_REL_L2
+        worst, e = check_rows(got["dW"].cpu().numpy(), ref["dW"], DH_REL_L2, "dW")
+        say(f"  dW worst row {worst:.2e}, whole {e:.2e}")

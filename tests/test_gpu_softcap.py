@@ -8,7 +8,7 @@ import oracle
 from rl_fine_tuning_amd import (Timer, grpo_ce_loss_fwd_bwd, grpo_logp_bwd, grpo_logp_fwd,
                                 grpo_loss_fwd_bwd)
 
-from gpu_cases import (DH_REL_L2, LOGP_ATOL, LOSS_RTOL, case, check_loss_outputs, host_matrix, rel_l2, say,
+from gpu_cases import (DH_REL_L2, LOGP_ATOL, LOSS_RTOL, case, check_loss_outputs, check_rows, host_matrix, say,
                        to_device)
 
 pytestmark = pytest.mark.gpu
@@ -38,10 +38,9 @@ def test_loss_with_logit_scale_and_softcap(dtype, D, V, lengths, chunk, tau, mul
     got = grpo_loss_fwd_bwd(d["H"], d["W"], d["targets"], k["c"].cu, d["old"], d["ref"], d["adv"], chunk,
                             temperature=tau, mask=d["mask"], **_logit_kw(mul, div, cap), **k["prm"])
     torch.cuda.synchronize()
-    r = check_loss_outputs(k, got)
-    say(f"  logp err {r['logp_err']:.2e} dH rel {r['dH_rel']:.2e} loss {r['loss']:.6e} vs {r['loss_ref']:.6e}")
-    if dtype == "f32":
-        assert r["dH_rel"] <= 1e-4
+    r = check_loss_outputs(k, got, dh_bar=1e-4 if dtype == "f32" else DH_REL_L2)
+    say(f"  logp err {r['logp_err']:.2e} dH worst row {r['dH_row_worst']:.2e} whole {r['dH_rel']:.2e} "
+        f"loss {r['loss']:.6e} vs {r['loss_ref']:.6e}")
 
 
 @pytest.mark.parametrize("dtype,cap", [("bf16", 3.0), ("f32", 3.0), ("bf16", 0.0)])
@@ -70,9 +69,8 @@ def test_logp_fwd_bwd_ce_with_softcap(dtype, cap):
     tm.close()
     ref = oracle.logp_backward(k["H64"], k["W64"], y, grad.astype(np.float64), tau, scale=_scale(mul, div),
                                softcap=cap)
-    e = rel_l2(oracle.widen(host_matrix(dH, dtype), dtype), ref)
-    say(f"  logp_bwd dH rel L2 {e:.2e}")
-    assert e <= (1e-4 if dtype == "f32" else DH_REL_L2)
+    worst, e = check_rows(oracle.widen(host_matrix(dH, dtype), dtype), ref, 1e-4 if dtype == "f32" else DH_REL_L2)
+    say(f"  logp_bwd dH worst row {worst:.2e}, whole {e:.2e}")
     mask = np.ones(T, np.uint8)
     mask[4] = 0
     out = oracle.cross_entropy_loss_and_grad(k["H64"], k["W64"], y, mask, tau, scale=_scale(mul, div), softcap=cap)
@@ -81,6 +79,6 @@ def test_logp_fwd_bwd_ce_with_softcap(dtype, cap):
     torch.cuda.synchronize()
     L = float(got["loss"].cpu()[0])
     assert abs(L - out["loss"]) <= LOSS_RTOL * abs(out["loss"])
-    e = rel_l2(oracle.widen(host_matrix(got["dH"], dtype), dtype), out["dH"])
-    say(f"  ce loss {L:.8f} vs {out['loss']:.8f}, dH rel L2 {e:.2e}")
-    assert e <= (1e-4 if dtype == "f32" else DH_REL_L2)
+    worst, e = check_rows(oracle.widen(host_matrix(got["dH"], dtype), dtype), out["dH"],
+                          1e-4 if dtype == "f32" else DH_REL_L2)
+    say(f"  ce loss {L:.8f} vs {out['loss']:.8f}, dH worst row {worst:.2e}, whole {e:.2e}")

@@ -8,7 +8,7 @@ import oracle
 from rl_fine_tuning_amd import Timer, grpo_ce_loss_fwd_bwd, grpo_logp_bwd, grpo_logp_fwd
 from synth import make_case
 
-from gpu_cases import DH_REL_L2, LOGP_ATOL, LOSS_RTOL, dev_matrix, host_matrix, rel_l2, say
+from gpu_cases import DH_REL_L2, LOGP_ATOL, LOSS_RTOL, check_rows, dev_matrix, host_matrix, say
 
 pytestmark = pytest.mark.gpu
 
@@ -44,11 +44,10 @@ def test_logp_bwd_matches_oracle(dtype, D, V, lengths, chunk, tau, expect_wt):
     tm.close()
     ref = oracle.logp_backward(H64, W64, y, grad.astype(np.float64), tau)
     got = oracle.widen(host_matrix(dH, dtype), dtype)
-    e = rel_l2(got, ref)
-    say(f"  dH rel L2 {e:.2e}")
-    assert e <= (1e-4 if dtype == "f32" else DH_REL_L2)
     zero = (grad == 0) | (y < 0) | (y >= V)
     assert np.all(got[zero] == 0)
+    worst, e = check_rows(got, ref, 1e-4 if dtype == "f32" else DH_REL_L2)
+    say(f"  dH worst row {worst:.2e}, whole {e:.2e}")
 
 
 def test_logp_bwd_chunk_invariance():
@@ -59,8 +58,7 @@ def test_logp_bwd_chunk_invariance():
     base = grpo_logp_bwd(d["H"], d["W"], d["targets"], lse, grad, T)
     for chunk in (1, 100, 256):
         got = grpo_logp_bwd(d["H"], d["W"], d["targets"], lse, grad, chunk)
-        rel = (got.float() - base.float()).norm() / base.float().norm()
-        assert rel.item() <= 1e-3, (chunk, rel.item())
+        check_rows(got.float().cpu().numpy(), base.float().cpu().numpy(), 1e-3)
 
 
 @pytest.mark.parametrize("dtype,D,V,lengths,chunk,tau,mask_frac", [
@@ -87,10 +85,9 @@ def test_ce_loss_matches_oracle(dtype, D, V, lengths, chunk, tau, mask_frac):
     assert np.abs(lp[ok] - out["logp"][ok]).max() <= LOGP_ATOL
     assert np.array_equal(got["token_loss"].cpu().numpy(), -got["logp"].cpu().numpy(), equal_nan=True)
     dH = oracle.widen(host_matrix(got["dH"], dtype), dtype)
-    e = rel_l2(dH, out["dH"])
-    say(f"  loss {L:.8f} vs {out['loss']:.8f}, dH rel L2 {e:.2e}")
-    assert e <= (1e-4 if dtype == "f32" else DH_REL_L2)
     assert np.all(dH[mask == 0] == 0)
+    worst, e = check_rows(dH, out["dH"], 1e-4 if dtype == "f32" else DH_REL_L2)
+    say(f"  loss {L:.8f} vs {out['loss']:.8f}, dH worst row {worst:.2e}, whole {e:.2e}")
 
 
 def test_ce_all_masked_and_counted_invalid_target():

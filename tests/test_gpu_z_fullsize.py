@@ -17,7 +17,8 @@ import oracle
 from rl_fine_tuning_amd import grpo_loss_fwd_bwd, grpo_workspace_bytes
 from synth import make_config
 
-from gpu_cases import DH_REL_L2, LOGP_ATOL, LOSS_RTOL, dev_matrix, f32, host_matrix, near_clip_boundary, rel_l2, say
+from gpu_cases import (DH_REL_L2, LOGP_ATOL, LOSS_RTOL, check_rows, dev_matrix, f32, host_matrix, near_clip_boundary,
+                       dh_rows_at, rel_l2, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -77,6 +78,12 @@ def test_full_size_sampled(cfg, keep):
     amb = near_clip_boundary(lp_rows, old[rows].astype(np.float64), 0.2, 0.2)
     e = rel_l2(dH[~amb], dH_ref[~amb])
     assert e <= DH_REL_L2, e
+    # every sampled row at its own scale, against the oracle's dH at the GPU's log-probabilities
+    # (a token whose g_t nearly cancels would otherwise measure the fp32-vs-fp64 logp difference)
+    terms_at = oracle.grpo_token_terms(logp[rows], old[rows].astype(np.float64), ref[rows].astype(np.float64),
+                                       adv.astype(np.float64)[s[rows]], 0.2, 0.2, 0.001)
+    dH_at = dh_rows_at(H_rows, W64, c.targets[rows], lse_rows, logp[rows], w[rows] * terms_at["dell"])
+    worst, _ = check_rows(dH[~amb], dH_at[~amb], DH_REL_L2)
 
     L = float(got["loss"].cpu().numpy()[0])
     L_terms = float(np.sum(w * tl))
@@ -90,4 +97,5 @@ def test_full_size_sampled(cfg, keep):
     scale_or = max(abs(L_or), float(np.sum(np.abs(w * ell_or))))
     assert abs(L - L_or) <= LOSS_RTOL * scale_or, (L, L_or, scale_or)
     assert np.all(np.abs(tl - ell_or) <= LOGP_ATOL * (1 + np.abs(adv[oracle.sequence_of_token(c.cu)])))
-    say(f"  logp err {err:.2e}, dH rel L2 {e:.2e}, loss {L:.6e}, workspace {ws_bytes / 2**30:.2f} GiB")
+    say(f"  logp err {err:.2e}, dH worst row {worst:.2e}, whole {e:.2e}, loss {L:.6e}, "
+        f"workspace {ws_bytes / 2**30:.2f} GiB")
