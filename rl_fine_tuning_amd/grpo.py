@@ -6,6 +6,7 @@ binding fails loudly when the library has not been built.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -104,19 +105,57 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on(stream):
+    """Allocations made under this context belong to the call's stream, so the caching
+    allocator never hands a buffer the call's kernels still use to work on another stream."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return GRPO_BF16
     if t.dtype == torch.float32:
         return GRPO_F32
-    raise TypeError(f"unsupported dtype {t.dtype}")
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
 
 
-def _dev(t: torch.Tensor, name: str):
-    if not t.is_cuda:
+def _is_device(t: torch.Tensor) -> bool:
+    return t.is_cuda
+
+
+def _dev(t, name: str, device=None, dtype=None, shape=None):
+    """Check a tensor argument before its pointer reaches the library: a device tensor on
+    `device`, contiguous, of one of the dtypes in `dtype` and of shape `shape` (when given)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if not _is_device(t):
         raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call's tensors on {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if dtype is not None:
+        allowed = dtype if isinstance(dtype, tuple) else (dtype,)
+        if t.dtype not in allowed:
+            raise TypeError(f"{name} must be {' or '.join(str(d) for d in allowed)}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+_MASK = (torch.uint8, torch.bool)
+
+
+def _hw(H, W, targets):
+    """Shapes of the common inputs: H [T, D] bf16 or fp32, W [V, D] of H's dtype, targets int32 [T]."""
+    _dev(H, "H", dtype=(torch.bfloat16, torch.float32))
+    if H.dim() != 2:
+        raise ValueError(f"H must be [T, D], got shape {tuple(H.shape)}")
+    T, D = H.shape
+    _dev(W, "W", H.device, H.dtype)
+    if W.dim() != 2 or W.shape[1] != D:
+        raise ValueError(f"W must be [V, {D}], got shape {tuple(W.shape)}")
+    _dev(targets, "targets", H.device, torch.int32, (T,))
+    return int(T), int(D), int(W.shape[0])
 
 
 def make_shape(T, D, V, chunk_tokens, dtype, temperature=1.0, logit_scale_multiply=0.0, logit_scale_divide=0.0,
@@ -153,13 +192,33 @@ def grpo_plan_info(T, D, V, chunk_tokens, dtype=GRPO_BF16, temperature=1.0, num_
 
 
 def _workspace(nbytes, workspace, device):
+    """The caller's workspace (a uint8 device tensor of at least nbytes) or a new one."""
     if nbytes == 0:
         return None, 0
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    _dev(workspace, "workspace", device, torch.uint8)
     if workspace.numel() < nbytes:
-        raise ValueError("workspace too small")
+        raise ValueError(f"workspace too small: {workspace.numel()} bytes, the call needs {nbytes}")
     return workspace, workspace.numel()
+
+
+def _out(t, name, device, dtype, shape):
+    """A caller-given output (checked) or a new one."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _dev(t, name, device, dtype, shape)
+    return t
+
+
+def _want_dW(dW, V, D, device):
+    """dW argument: None/False = not computed, True = allocate, or an fp32 [V, D] tensor."""
+    if dW is None or dW is False:
+        return None
+    if dW is True:
+        return torch.empty(V, D, dtype=torch.float32, device=device)
+    _dev(dW, "dW", device, torch.float32, (V, D))
+    return dW
 
 
 class Timer:
@@ -196,18 +255,17 @@ def grpo_logp_fwd(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, chunk
                   logit_softcapping=0.0, return_lse: bool = False, out=None, workspace=None,
                   stream=None, timer: Timer | None = None):
     """logp[t] = log softmax(H[t] W^T / temperature)[targets[t]] (fp32), chunked."""
-    for t, n in ((H, "H"), (W, "W"), (targets, "targets")):
-        _dev(t, n)
-    T, D = H.shape
-    V = W.shape[0]
+    T, D, V = _hw(H, W, targets)
+    dev = H.device
     shape = make_shape(T, D, V, chunk_tokens, _dtype_code(H), temperature, logit_scale_multiply,
                        logit_scale_divide, logit_softcapping)
     nbytes = int(lib().grpo_workspace_bytes(ctypes.byref(shape), 1, 0))
-    ws, wsn = _workspace(nbytes, workspace, H.device)
-    logp = out if out is not None else torch.empty(T, dtype=torch.float32, device=H.device)
-    lse = torch.empty(T, dtype=torch.float32, device=H.device) if return_lse else None
-    st = lib().grpo_logp_fwd(ctypes.byref(shape), _ptr(H), _ptr(W), _ptr(targets), _ptr(logp), _ptr(lse),
-                             _ptr(ws), wsn, _stream(stream), timer.handle if timer else None)
+    with _on(stream):
+        ws, wsn = _workspace(nbytes, workspace, dev)
+        logp = _out(out, "out", dev, torch.float32, (T,))
+        lse = torch.empty(T, dtype=torch.float32, device=dev) if return_lse else None
+        st = lib().grpo_logp_fwd(ctypes.byref(shape), _ptr(H), _ptr(W), _ptr(targets), _ptr(logp), _ptr(lse),
+                                 _ptr(ws), wsn, _stream(stream), timer.handle if timer else None)
     _check(st, "grpo_logp_fwd")
     return (logp, lse) if return_lse else logp
 
@@ -219,24 +277,21 @@ def grpo_logp_bwd(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: 
     """dH of sum_t grad_logp[t] * logp_t, recomputing each chunk's logits from the forward's lse.
     With dW (an fp32 [V, D] tensor, or True to allocate one) returns (dH, dW).  A caller's
     workspace must hold grpo_workspace_bytes(..., with_dW=bool(dW)) bytes."""
-    for t, n in ((H, "H"), (W, "W"), (targets, "targets"), (lse, "lse"), (grad_logp, "grad_logp")):
-        _dev(t, n)
-    T, D = H.shape
-    V = W.shape[0]
+    T, D, V = _hw(H, W, targets)
+    dev = H.device
+    _dev(lse, "lse", dev, torch.float32, (T,))
+    _dev(grad_logp, "grad_logp", dev, torch.float32, (T,))
     shape = make_shape(T, D, V, chunk_tokens, _dtype_code(H), temperature, logit_scale_multiply,
                        logit_scale_divide, logit_softcapping)
-    nbytes = int(lib().grpo_workspace_bytes(ctypes.byref(shape), 1, 2 if dW is not None and dW is not False else 1))
-    ws, wsn = _workspace(nbytes, workspace, H.device)
-    if dH is None:
-        dH = torch.empty_like(H)
-    want_dW = dW is not None and dW is not False
-    if dW is True:
-        dW = torch.empty(V, D, dtype=torch.float32, device=H.device)
-    st = lib().grpo_logp_bwd(ctypes.byref(shape), _ptr(H), _ptr(W), _ptr(targets), _ptr(lse), _ptr(grad_logp),
-                             _ptr(dH), _ptr(dW) if want_dW else None, _ptr(ws), wsn, _stream(stream),
-                             timer.handle if timer else None)
+    with _on(stream):
+        dW = _want_dW(dW, V, D, dev)
+        nbytes = int(lib().grpo_workspace_bytes(ctypes.byref(shape), 1, 2 if dW is not None else 1))
+        ws, wsn = _workspace(nbytes, workspace, dev)
+        dH = _out(dH, "dH", dev, H.dtype, (T, D))
+        st = lib().grpo_logp_bwd(ctypes.byref(shape), _ptr(H), _ptr(W), _ptr(targets), _ptr(lse), _ptr(grad_logp),
+                                 _ptr(dH), _ptr(dW), _ptr(ws), wsn, _stream(stream), timer.handle if timer else None)
     _check(st, "grpo_logp_bwd")
-    return (dH, dW) if want_dW else dH
+    return (dH, dW) if dW is not None else dH
 
 
 def grpo_ce_loss_fwd_bwd(H, W, targets, chunk_tokens, *, temperature=1.0, logit_scale_multiply=0.0,
@@ -246,87 +301,102 @@ def grpo_ce_loss_fwd_bwd(H, W, targets, chunk_tokens, *, temperature=1.0, logit_
     """Mean cross-entropy over the unmasked tokens, per-token logp, dL/dH and (with dW: an
     fp32 [V, D] tensor, or True to allocate one) dL/dW.  A caller's workspace must hold
     grpo_workspace_bytes(..., with_dW=bool(dW)) bytes."""
-    for t, n in ((H, "H"), (W, "W"), (targets, "targets")):
-        _dev(t, n)
+    T, D, V = _hw(H, W, targets)
+    dev = H.device
     if mask is not None:
-        _dev(mask, "mask")
-    T, D = H.shape
-    V = W.shape[0]
+        _dev(mask, "mask", dev, _MASK, (T,))
     shape = make_shape(T, D, V, chunk_tokens, _dtype_code(H), temperature, logit_scale_multiply,
                        logit_scale_divide, logit_softcapping, keep_chunk_logits)
-    nbytes = int(lib().grpo_workspace_bytes(ctypes.byref(shape), 1, 2 if dW is not None and dW is not False else 1))
-    ws, wsn = _workspace(nbytes, workspace, H.device)
-    dev = H.device
-    loss = torch.empty(1, dtype=torch.float64, device=dev)
-    logp = torch.empty(T, dtype=torch.float32, device=dev) if want_logp else None
-    tl = torch.empty(T, dtype=torch.float32, device=dev) if want_token_loss else None
-    if dH is None:
-        dH = torch.empty_like(H)
-    if dW is True:
-        dW = torch.empty(V, D, dtype=torch.float32, device=dev)
-    st = lib().grpo_ce_loss_fwd_bwd(ctypes.byref(shape), _ptr(H), _ptr(W), _ptr(targets), _ptr(mask), _ptr(loss),
-                                    _ptr(logp), _ptr(tl), _ptr(dH), _ptr(dW) if dW is not None and dW is not False else None, _ptr(ws),
-                                    wsn, _stream(stream), timer.handle if timer else None)
+    with _on(stream):
+        dW = _want_dW(dW, V, D, dev)
+        nbytes = int(lib().grpo_workspace_bytes(ctypes.byref(shape), 1, 2 if dW is not None else 1))
+        ws, wsn = _workspace(nbytes, workspace, dev)
+        loss = torch.empty(1, dtype=torch.float64, device=dev)
+        logp = torch.empty(T, dtype=torch.float32, device=dev) if want_logp else None
+        tl = torch.empty(T, dtype=torch.float32, device=dev) if want_token_loss else None
+        dH = _out(dH, "dH", dev, H.dtype, (T, D))
+        st = lib().grpo_ce_loss_fwd_bwd(ctypes.byref(shape), _ptr(H), _ptr(W), _ptr(targets), _ptr(mask),
+                                        _ptr(loss), _ptr(logp), _ptr(tl), _ptr(dH), _ptr(dW), _ptr(ws), wsn,
+                                        _stream(stream), timer.handle if timer else None)
     _check(st, "grpo_ce_loss_fwd_bwd")
     return dict(loss=loss, logp=logp, token_loss=tl, dH=dH, dW=dW)
 
 
 def grpo_advantages(rewards: torch.Tensor, group_size: int, std_mode: str = "unbiased", eps: float = 1e-4,
                     *, out=None, stream=None) -> torch.Tensor:
-    _dev(rewards, "rewards")
-    adv = out if out is not None else torch.empty_like(rewards)
-    st = lib().grpo_advantages(_ptr(rewards), rewards.numel(), int(group_size), GRPO_STD[std_mode], float(eps),
-                               _ptr(adv), _stream(stream))
+    _dev(rewards, "rewards", dtype=torch.float32)
+    if rewards.dim() != 1:
+        raise ValueError(f"rewards must be [S], got shape {tuple(rewards.shape)}")
+    with _on(stream):
+        adv = _out(out, "out", rewards.device, torch.float32, tuple(rewards.shape))
+        st = lib().grpo_advantages(_ptr(rewards), rewards.numel(), int(group_size), GRPO_STD[std_mode], float(eps),
+                                   _ptr(adv), _stream(stream))
     _check(st, "grpo_advantages")
     return adv
+
+
+def _loss_call(H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk_tokens, *, temperature,
+               logit_scale_multiply, logit_scale_divide, logit_softcapping, keep_chunk_logits, clip_eps_low,
+               clip_eps_high, beta, agg, mask, want_logp, want_token_loss, loss, logp, token_loss, dH, dW,
+               workspace, stream, timer):
+    T, D, V = _hw(H, W, targets)
+    dev = H.device
+    cu = torch.as_tensor(cu_seqlens).cpu()
+    if cu.dim() != 1 or cu.numel() < 2 or cu.dtype not in (torch.int32, torch.int64):
+        raise ValueError("cu_seqlens must be a 1-D integer array of S + 1 offsets")
+    cu = cu.to(torch.int32).contiguous()
+    S = cu.numel() - 1
+    _dev(old_logp, "old_logp", dev, torch.float32, (T,))
+    if ref_logp is not None:
+        _dev(ref_logp, "ref_logp", dev, torch.float32, (T,))
+    _dev(adv, "adv", dev, torch.float32, (S,))
+    if mask is not None:
+        _dev(mask, "mask", dev, _MASK, (T,))
+    shape = make_shape(T, D, V, chunk_tokens, _dtype_code(H), temperature, logit_scale_multiply,
+                       logit_scale_divide, logit_softcapping, keep_chunk_logits)
+    params = GrpoLossParams(float(clip_eps_low), float(clip_eps_high), float(beta), GRPO_AGG[agg])
+    with _on(stream):
+        dW = _want_dW(dW, V, D, dev)
+        loss = _out(loss, "loss", dev, torch.float64, (1,))
+        logp = _out(logp, "logp", dev, torch.float32, (T,)) if want_logp or logp is not None else None
+        tl = (_out(token_loss, "token_loss", dev, torch.float32, (T,))
+              if want_token_loss or token_loss is not None else None)
+        dH = _out(dH, "dH", dev, H.dtype, (T, D))
+        args = [ctypes.byref(shape), ctypes.byref(params), _ptr(H), _ptr(W), _ptr(targets),
+                ctypes.c_void_p(cu.data_ptr()), S, _ptr(mask), _ptr(old_logp), _ptr(ref_logp), _ptr(adv),
+                _ptr(loss), _ptr(logp), _ptr(tl), _ptr(dH), _ptr(dW)]
+        nbytes = int(lib().grpo_workspace_bytes(ctypes.byref(shape), S, 2 if dW is not None else 1))
+        ws, wsn = _workspace(nbytes, workspace, dev)
+        st = lib().grpo_loss_fwd_bwd(*args, _ptr(ws), wsn, _stream(stream), timer.handle if timer else None)
+    _check(st, "grpo_loss_fwd_bwd")
+    return dict(loss=loss, logp=logp, token_loss=tl, dH=dH, dW=dW)
 
 
 def grpo_loss_fwd_bwd(H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk_tokens, *,
                       temperature=1.0, logit_scale_multiply=0.0, logit_scale_divide=0.0, logit_softcapping=0.0,
                       keep_chunk_logits=False, clip_eps_low=0.2, clip_eps_high=0.2, beta=0.001, agg="seq_mean",
-                      mask=None, want_logp=True, want_token_loss=True, dH=None, dW=None, workspace=None,
-                      stream=None, timer: Timer | None = None):
+                      mask=None, want_logp=True, want_token_loss=True, loss=None, logp=None, token_loss=None,
+                      dH=None, dW=None, workspace=None, stream=None, timer: Timer | None = None):
     """GRPO loss, per-token logp and objective, and dL/dH (and dL/dW with dW: an fp32 [V, D]
     tensor, or True to allocate one).  cu_seqlens is a host int32 array/tensor.  A caller's
-    workspace must hold grpo_workspace_bytes(..., num_seqs=S, with_dW=bool(dW)) bytes."""
-    for t, n in ((H, "H"), (W, "W"), (targets, "targets"), (old_logp, "old_logp"), (adv, "adv")):
-        _dev(t, n)
-    if ref_logp is not None:
-        _dev(ref_logp, "ref_logp")
-    if mask is not None:
-        _dev(mask, "mask")
-    cu = torch.as_tensor(cu_seqlens, dtype=torch.int32).cpu().contiguous()
-    S = cu.numel() - 1
-    T, D = H.shape
-    V = W.shape[0]
-    shape = make_shape(T, D, V, chunk_tokens, _dtype_code(H), temperature, logit_scale_multiply,
-                       logit_scale_divide, logit_softcapping, keep_chunk_logits)
-    params = GrpoLossParams(float(clip_eps_low), float(clip_eps_high), float(beta), GRPO_AGG[agg])
-    nbytes = int(lib().grpo_workspace_bytes(ctypes.byref(shape), S, 2 if dW is not None and dW is not False else 1))
-    ws, wsn = _workspace(nbytes, workspace, H.device)
-    dev = H.device
-    loss = torch.empty(1, dtype=torch.float64, device=dev)
-    logp = torch.empty(T, dtype=torch.float32, device=dev) if want_logp else None
-    tl = torch.empty(T, dtype=torch.float32, device=dev) if want_token_loss else None
-    if dH is None:
-        dH = torch.empty_like(H)
-    if dW is True:
-        dW = torch.empty(V, D, dtype=torch.float32, device=dev)
-    st = lib().grpo_loss_fwd_bwd(ctypes.byref(shape), ctypes.byref(params), _ptr(H), _ptr(W), _ptr(targets),
-                                 ctypes.c_void_p(cu.data_ptr()), S, _ptr(mask), _ptr(old_logp), _ptr(ref_logp),
-                                 _ptr(adv), _ptr(loss), _ptr(logp), _ptr(tl), _ptr(dH),
-                                 _ptr(dW) if dW is not None and dW is not False else None, _ptr(ws), wsn, _stream(stream),
-                                 timer.handle if timer else None)
-    _check(st, "grpo_loss_fwd_bwd")
-    return dict(loss=loss, logp=logp, token_loss=tl, dH=dH, dW=dW)
+    workspace must hold grpo_workspace_bytes(..., num_seqs=S, with_dW=bool(dW)) bytes.
+    Outputs (loss fp64 [1], logp and token_loss fp32 [T], dH) may be passed in."""
+    return _loss_call(H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk_tokens,
+                      temperature=temperature, logit_scale_multiply=logit_scale_multiply,
+                      logit_scale_divide=logit_scale_divide, logit_softcapping=logit_softcapping,
+                      keep_chunk_logits=keep_chunk_logits, clip_eps_low=clip_eps_low, clip_eps_high=clip_eps_high,
+                      beta=beta, agg=agg, mask=mask, want_logp=want_logp, want_token_loss=want_token_loss,
+                      loss=loss, logp=logp, token_loss=token_loss, dH=dH, dW=dW, workspace=workspace,
+                      stream=stream, timer=timer)
 
 
 def grpo_debug_token_index(cu_seqlens, T: int, chunk_tokens: int, device="cuda", stream=None):
     cu = torch.as_tensor(cu_seqlens, dtype=torch.int32).cpu().contiguous()
     S = cu.numel() - 1
-    out = [torch.empty(T, dtype=torch.int32, device=device) for _ in range(3)]
-    ws = torch.empty(max(256, (S + 1) * 4 + 255) // 256 * 256, dtype=torch.uint8, device=device)
-    st = lib().grpo_debug_token_index(ctypes.c_void_p(cu.data_ptr()), S, int(T), int(chunk_tokens),
-                                      *[_ptr(o) for o in out], _ptr(ws), ws.numel(), _stream(stream))
+    with _on(stream):
+        out = [torch.empty(T, dtype=torch.int32, device=device) for _ in range(3)]
+        ws = torch.empty(max(256, (S + 1) * 4 + 255) // 256 * 256, dtype=torch.uint8, device=device)
+        st = lib().grpo_debug_token_index(ctypes.c_void_p(cu.data_ptr()), S, int(T), int(chunk_tokens),
+                                          *[_ptr(o) for o in out], _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "grpo_debug_token_index")
     return tuple(out)

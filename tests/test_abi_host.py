@@ -253,3 +253,77 @@ def test_keep_chunk_logits_validation():
     # keeping the logits needs no memory beyond the same bound: one chunk's fp32 logits
     for (T, D, V, C) in [(110000, 4096, 151936, 8192), (40960, 1536, 151936, 4096), (380000, 2880, 201088, 8192)]:
         assert 0 < B.grpo_workspace_bytes(T, D, V, C, 0, num_seqs=2, keep_chunk_logits=True) <= C * V * 4
+
+
+class _FakeLib:
+    """Stands in for the library in binding tests: counts compute calls, sizes nothing."""
+
+    def __init__(self):
+        self.calls = []
+
+    def grpo_workspace_bytes(self, *a):
+        return 1024
+
+    def __getattr__(self, name):
+        def call(*a):
+            self.calls.append(name)
+            return 0
+        return call
+
+
+def test_binding_rejects_bad_arguments_before_the_library(monkeypatch):
+    # Every wrapper checks device, contiguity, dtype and shape of each tensor before a
+    # pointer reaches the library.  CPU tensors stand in for device tensors here.
+    import types
+    import torch
+    fake = _FakeLib()
+    monkeypatch.setattr(B, "lib", lambda: fake)
+    monkeypatch.setattr(B, "_is_device", lambda t: True)
+    monkeypatch.setattr(B, "_on", lambda s: __import__("contextlib").nullcontext())
+    stream = types.SimpleNamespace(cuda_stream=0)
+    T, D, V, S = 12, 16, 40, 3
+    bf = torch.bfloat16
+    good = dict(H=torch.zeros(T, D, dtype=bf), W=torch.zeros(V, D, dtype=bf),
+                targets=torch.zeros(T, dtype=torch.int32), cu=np.array([0, 4, 8, 12], np.int32),
+                old=torch.zeros(T), ref=torch.zeros(T), adv=torch.zeros(S))
+
+    def loss(**over):
+        a = dict(good, **over)
+        return B.grpo_loss_fwd_bwd(a["H"], a["W"], a["targets"], a["cu"], a["old"], a["ref"], a["adv"], 4,
+                                   stream=stream, **{k: v for k, v in over.items() if k in ("mask", "dH", "dW", "workspace")})
+
+    loss()
+    assert fake.calls == ["grpo_loss_fwd_bwd"]
+    bad = [
+        (dict(targets=torch.zeros(T, dtype=torch.int64)), TypeError),      # torch's default integer type
+        (dict(targets=torch.zeros(T + 1, dtype=torch.int32)), ValueError),
+        (dict(W=torch.zeros(V, D)), TypeError),                            # W's dtype differs from H's
+        (dict(W=torch.zeros(V, D + 8, dtype=bf)), ValueError),
+        (dict(H=torch.zeros(T, D, dtype=torch.float16)), TypeError),
+        (dict(H=torch.zeros(D, T, dtype=bf).t()), ValueError),             # not contiguous
+        (dict(old=torch.zeros(T, dtype=torch.float64)), TypeError),
+        (dict(ref=torch.zeros(T - 1)), ValueError),
+        (dict(adv=torch.zeros(S + 1)), ValueError),
+        (dict(mask=torch.zeros(T, dtype=torch.int32)), TypeError),
+        (dict(dH=torch.zeros(T, D)), TypeError),                           # dH takes H's dtype
+        (dict(dW=torch.zeros(V, D, dtype=bf)), TypeError),                 # dW is fp32
+        (dict(dW=torch.zeros(V + 1, D)), ValueError),
+        (dict(workspace=torch.zeros(2048)), TypeError),                    # a uint8 buffer
+        (dict(workspace=torch.zeros(16, dtype=torch.uint8)), ValueError),  # too small
+        (dict(H=np.zeros((T, D))), TypeError),
+    ]
+    for over, exc in bad:
+        with pytest.raises(exc):
+            loss(**over)
+    assert fake.calls == ["grpo_loss_fwd_bwd"], "a bad argument reached the library"
+    with pytest.raises(TypeError):
+        B.grpo_logp_fwd(good["H"], good["W"], torch.zeros(T, dtype=torch.int64), 4, stream=stream)
+    with pytest.raises(TypeError):
+        B.grpo_logp_bwd(good["H"], good["W"], good["targets"], torch.zeros(T, dtype=torch.float64), good["old"], 4,
+                        stream=stream)
+    with pytest.raises(ValueError):
+        B.grpo_ce_loss_fwd_bwd(good["H"], good["W"], good["targets"], 4, mask=torch.zeros(T + 2, dtype=torch.uint8),
+                               stream=stream)
+    with pytest.raises(TypeError):
+        B.grpo_advantages(torch.zeros(S, dtype=torch.float64), 3, stream=stream)
+    assert fake.calls == ["grpo_loss_fwd_bwd"]
