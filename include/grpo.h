@@ -42,7 +42,8 @@
  *  - A target outside [0, V) yields NaN logp / token_loss for that token (and a
  *    NaN loss if its weight is non-zero), a zero dH row, and no out-of-bounds access.
  *  - Calls keep no global state and may run concurrently on different streams with
- *    different workspaces.
+ *    different workspaces; grpo_loss_fwd_bwd_static is the exception (its workspace is one
+ *    array per device, see there).
  */
 #ifndef GRPO_MI355X_H
 #define GRPO_MI355X_H
@@ -61,7 +62,8 @@ typedef enum {
   GRPO_E_VALUE = 3,       /* a scalar is out of range or not finite */
   GRPO_E_WORKSPACE = 4,   /* workspace missing, too small or misaligned */
   GRPO_E_UNSUPPORTED = 5, /* dtype, alignment or divisibility this build does not handle */
-  GRPO_E_HIP = 6          /* the HIP runtime reported an error */
+  GRPO_E_HIP = 6,         /* the HIP runtime reported an error */
+  GRPO_E_SCRATCH = 7      /* the call needs more than grpo_loss_fwd_bwd_static's static scratch */
 } grpo_status;
 
 typedef enum { GRPO_BF16 = 0, GRPO_F32 = 1 } grpo_dtype;            /* element type of H, W, dH */
@@ -205,6 +207,28 @@ grpo_status grpo_loss_fwd_bwd(const grpo_shape* shape, const grpo_loss_params* p
                               double* loss, float* logp, float* token_loss, void* dH, float* dW,
                               void* workspace, size_t workspace_bytes, void* stream,
                               grpo_timer* timer);
+
+/* grpo_loss_fwd_bwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same arguments and
+ * results, without the workspace.  The call uses a workspace array compiled into the library,
+ * one copy per device, GRPO_STATIC_SCRATCH_BYTES (256 MiB) each, held from the library's load
+ * until the process ends; it calls no hipMalloc, hipFree or allocating routine.
+ *   The call must fit: grpo_workspace_bytes(shape, num_seqs, 1) (2 with dW) <= 256 MiB, else
+ *   GRPO_E_SCRATCH before anything is enqueued (e.g. the Qwen3-8B shape, V = 151936, fits with
+ *   chunk_tokens = 256, not with 8192).
+ *   The current device must be the device of `stream` and of the buffers.
+ *   Every call on one device shares that device's array: calls that overlap in time on one
+ *   device (different streams, or host threads) race and give undefined results; calls
+ *   queued on one stream are ordered and safe.  Nothing in the array needs to start at zero.
+ *   The first call on a device looks the array's device address up (hipGetSymbolAddress) and
+ *   keeps it; that lookup is the only HIP call besides the launches and hipGetDevice. */
+#define GRPO_STATIC_SCRATCH_BYTES ((size_t)256 << 20)
+grpo_status grpo_loss_fwd_bwd_static(const grpo_shape* shape, const grpo_loss_params* params,
+                                     const void* H, const void* W, const int32_t* targets,
+                                     const int32_t* cu_seqlens, int64_t num_seqs, const uint8_t* mask,
+                                     const float* old_logp, const float* ref_logp, const float* adv,
+                                     double* loss, float* logp, float* token_loss, void* dH, float* dW,
+                                     void* stream, grpo_timer* timer);
 
 /* Backward of grpo_logp_fwd ([P4] "Auslagern von Aktivierungen fuer Log-Softmax": the
  * forward keeps only the per-token log-sum-exp; the backward recomputes each chunk's logits

@@ -14,6 +14,7 @@ from .grpo import (  # noqa: F401
     grpo_logp_bwd,
     grpo_logp_fwd,
     grpo_loss_fwd_bwd,
+    grpo_loss_fwd_bwd_static,
     grpo_plan_info,
     grpo_workspace_bytes,
     lib,

@@ -251,6 +251,7 @@ const char* grpo_status_string(grpo_status s) {
     case GRPO_E_WORKSPACE: return "workspace missing, too small or misaligned";
     case GRPO_E_UNSUPPORTED: return "unsupported dtype, alignment or divisibility";
     case GRPO_E_HIP: return "HIP runtime error";
+    case GRPO_E_SCRATCH: return "the call needs more workspace than the static scratch of grpo_loss_fwd_bwd_static";
   }
   return "unknown status";
 }

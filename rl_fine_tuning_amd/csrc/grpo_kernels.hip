@@ -33,11 +33,18 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 #include <vector>
 
 #include "grpo.h"
 #include "grpo_plan.h"
+
+// Workspace of grpo_loss_fwd_bwd_static (for callers that cannot allocate): one copy per
+// device, held from the library's load until the process ends.  Every call on a device
+// uses the same bytes; each call writes every byte it reads, so nothing needs clearing.
+constexpr size_t kStaticScratchBytes = size_t(256) << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
 
 struct grpo_timer {
   int32_t capacity = 0;
@@ -2122,6 +2129,59 @@ bool ws_ok(const Plan& p, const void* ws, size_t bytes) {
   return ws != nullptr && bytes >= p.total && (reinterpret_cast<uintptr_t>(ws) % kAlign) == 0;
 }
 
+// Host-side checks and workspace plan of a grpo_loss_fwd_bwd call (no HIP call).
+grpo_status loss_check(const grpo_shape* shape, const grpo_loss_params* params, const void* H, const void* W,
+                       const int32_t* targets, const int32_t* cu_seqlens, int64_t num_seqs, const float* old_logp,
+                       const float* ref_logp, const float* adv, const double* loss, const void* dH, const float* dW,
+                       Plan* p) {
+  grpo_status st = validate_shape(shape);
+  if (st != GRPO_OK) return st;
+  st = validate_loss_params(params);
+  if (st != GRPO_OK) return st;
+  if (!loss || !adv || !W) return GRPO_E_NULL;
+  if (shape->T > 0 && (!H || !targets || !old_logp || !dH)) return GRPO_E_NULL;
+  if (params->beta != 0.0f && shape->T > 0 && !ref_logp) return GRPO_E_NULL;
+  st = validate_cu(cu_seqlens, num_seqs, shape->T);
+  if (st != GRPO_OK) return st;
+  if (!aligned16(H) || !aligned16(W) || !aligned16(dH)) return GRPO_E_UNSUPPORTED;
+  if (dW && (shape->dtype != GRPO_BF16 || !aligned16(dW))) return GRPO_E_UNSUPPORTED;
+  return make_plan(shape, num_seqs, true, p, dW != nullptr);
+}
+
+grpo_status loss_run(const Plan& p, const grpo_shape* shape, const grpo_loss_params* params, const void* H,
+                     const void* W, const int32_t* targets, const int32_t* cu_seqlens, const uint8_t* mask,
+                     const float* old_logp, const float* ref_logp, const float* adv, double* loss, float* logp,
+                     float* token_loss, void* dH, float* dW, char* ws, void* stream, grpo_timer* timer) {
+  (void)hipGetLastError();
+  Launcher L{reinterpret_cast<hipStream_t>(stream), timer};
+  const float* ref = params->beta != 0.0f ? ref_logp : nullptr;
+  if (p.dtype == GRPO_BF16)
+    return loss_impl<__bf16>(p, shape, 1, params, (const __bf16*)H, (const __bf16*)W, targets, cu_seqlens, mask,
+                             old_logp, ref, adv, loss, logp, token_loss, (__bf16*)dH, dW, ws, L);
+  return loss_impl<float>(p, shape, 1, params, (const float*)H, (const float*)W, targets, cu_seqlens, mask,
+                          old_logp, ref, adv, loss, logp, token_loss, (float*)dH, nullptr, ws, L);
+}
+
+// Device address of this device's copy of `scratch`, looked up once per device (with that
+// device current) and kept: in host code the array's name is not a device address.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+grpo_status static_scratch(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return GRPO_E_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return GRPO_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return GRPO_E_HIP;
+    g_scratch_ptr[dev] = reinterpret_cast<char*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return GRPO_OK;
+}
+
 }  // namespace
 }  // namespace grpo
 
@@ -2167,30 +2227,30 @@ grpo_status grpo_loss_fwd_bwd(const grpo_shape* shape, const grpo_loss_params* p
                               const uint8_t* mask, const float* old_logp, const float* ref_logp, const float* adv,
                               double* loss, float* logp, float* token_loss, void* dH, float* dW,
                               void* workspace, size_t workspace_bytes, void* stream, grpo_timer* timer) {
-  grpo_status st = validate_shape(shape);
-  if (st != GRPO_OK) return st;
-  st = validate_loss_params(params);
-  if (st != GRPO_OK) return st;
-  if (!loss || !adv || !W) return GRPO_E_NULL;
-  if (shape->T > 0 && (!H || !targets || !old_logp || !dH)) return GRPO_E_NULL;
-  if (params->beta != 0.0f && shape->T > 0 && !ref_logp) return GRPO_E_NULL;
-  st = validate_cu(cu_seqlens, num_seqs, shape->T);
-  if (st != GRPO_OK) return st;
-  if (!aligned16(H) || !aligned16(W) || !aligned16(dH)) return GRPO_E_UNSUPPORTED;
-  if (dW && (shape->dtype != GRPO_BF16 || !aligned16(dW))) return GRPO_E_UNSUPPORTED;
   Plan p;
-  st = make_plan(shape, num_seqs, true, &p, dW != nullptr);
+  grpo_status st = loss_check(shape, params, H, W, targets, cu_seqlens, num_seqs, old_logp, ref_logp, adv, loss, dH,
+                              dW, &p);
   if (st != GRPO_OK) return st;
   if (!ws_ok(p, workspace, workspace_bytes)) return GRPO_E_WORKSPACE;
-  (void)hipGetLastError();
-  Launcher L{reinterpret_cast<hipStream_t>(stream), timer};
-  char* ws = reinterpret_cast<char*>(workspace);
-  const float* ref = params->beta != 0.0f ? ref_logp : nullptr;
-  if (p.dtype == GRPO_BF16)
-    return loss_impl<__bf16>(p, shape, 1, params, (const __bf16*)H, (const __bf16*)W, targets, cu_seqlens, mask,
-                             old_logp, ref, adv, loss, logp, token_loss, (__bf16*)dH, dW, ws, L);
-  return loss_impl<float>(p, shape, 1, params, (const float*)H, (const float*)W, targets, cu_seqlens, mask,
-                          old_logp, ref, adv, loss, logp, token_loss, (float*)dH, nullptr, ws, L);
+  return loss_run(p, shape, params, H, W, targets, cu_seqlens, mask, old_logp, ref_logp, adv, loss, logp, token_loss,
+                  dH, dW, reinterpret_cast<char*>(workspace), stream, timer);
+}
+
+grpo_status grpo_loss_fwd_bwd_static(const grpo_shape* shape, const grpo_loss_params* params, const void* H,
+                                     const void* W, const int32_t* targets, const int32_t* cu_seqlens,
+                                     int64_t num_seqs, const uint8_t* mask, const float* old_logp,
+                                     const float* ref_logp, const float* adv, double* loss, float* logp,
+                                     float* token_loss, void* dH, float* dW, void* stream, grpo_timer* timer) {
+  Plan p;
+  grpo_status st = loss_check(shape, params, H, W, targets, cu_seqlens, num_seqs, old_logp, ref_logp, adv, loss, dH,
+                              dW, &p);
+  if (st != GRPO_OK) return st;
+  if (p.total > kStaticScratchBytes) return GRPO_E_SCRATCH;  // before any HIP call
+  char* ws = nullptr;
+  st = static_scratch(&ws);
+  if (st != GRPO_OK) return st;
+  return loss_run(p, shape, params, H, W, targets, cu_seqlens, mask, old_logp, ref_logp, adv, loss, logp, token_loss,
+                  dH, dW, ws, stream, timer);
 }
 
 grpo_status grpo_logp_bwd(const grpo_shape* shape, const void* H, const void* W, const int32_t* targets,

@@ -67,6 +67,9 @@ def lib() -> ctypes.CDLL:
         L.grpo_loss_fwd_bwd.argtypes = [sp, ctypes.POINTER(GrpoLossParams), vp, vp, vp, vp, i64, vp, vp,
                                         vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
         L.grpo_loss_fwd_bwd.restype = ctypes.c_int
+        L.grpo_loss_fwd_bwd_static.argtypes = [sp, ctypes.POINTER(GrpoLossParams), vp, vp, vp, vp, i64, vp, vp,
+                                               vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.grpo_loss_fwd_bwd_static.restype = ctypes.c_int
         L.grpo_logp_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
         L.grpo_logp_bwd.restype = ctypes.c_int
         L.grpo_ce_loss_fwd_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
@@ -335,7 +338,7 @@ def grpo_advantages(rewards: torch.Tensor, group_size: int, std_mode: str = "unb
     return adv
 
 
-def _loss_call(H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk_tokens, *, temperature,
+def _loss_call(static, H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk_tokens, *, temperature,
                logit_scale_multiply, logit_scale_divide, logit_softcapping, keep_chunk_logits, clip_eps_low,
                clip_eps_high, beta, agg, mask, want_logp, want_token_loss, loss, logp, token_loss, dH, dW,
                workspace, stream, timer):
@@ -365,10 +368,13 @@ def _loss_call(H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk_tokens,
         args = [ctypes.byref(shape), ctypes.byref(params), _ptr(H), _ptr(W), _ptr(targets),
                 ctypes.c_void_p(cu.data_ptr()), S, _ptr(mask), _ptr(old_logp), _ptr(ref_logp), _ptr(adv),
                 _ptr(loss), _ptr(logp), _ptr(tl), _ptr(dH), _ptr(dW)]
-        nbytes = int(lib().grpo_workspace_bytes(ctypes.byref(shape), S, 2 if dW is not None else 1))
-        ws, wsn = _workspace(nbytes, workspace, dev)
-        st = lib().grpo_loss_fwd_bwd(*args, _ptr(ws), wsn, _stream(stream), timer.handle if timer else None)
-    _check(st, "grpo_loss_fwd_bwd")
+        if static:
+            st = lib().grpo_loss_fwd_bwd_static(*args, _stream(stream), timer.handle if timer else None)
+        else:
+            nbytes = int(lib().grpo_workspace_bytes(ctypes.byref(shape), S, 2 if dW is not None else 1))
+            ws, wsn = _workspace(nbytes, workspace, dev)
+            st = lib().grpo_loss_fwd_bwd(*args, _ptr(ws), wsn, _stream(stream), timer.handle if timer else None)
+    _check(st, "grpo_loss_fwd_bwd_static" if static else "grpo_loss_fwd_bwd")
     return dict(loss=loss, logp=logp, token_loss=tl, dH=dH, dW=dW)
 
 
@@ -381,13 +387,34 @@ def grpo_loss_fwd_bwd(H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk_
     tensor, or True to allocate one).  cu_seqlens is a host int32 array/tensor.  A caller's
     workspace must hold grpo_workspace_bytes(..., num_seqs=S, with_dW=bool(dW)) bytes.
     Outputs (loss fp64 [1], logp and token_loss fp32 [T], dH) may be passed in."""
-    return _loss_call(H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk_tokens,
+    return _loss_call(False, H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk_tokens,
                       temperature=temperature, logit_scale_multiply=logit_scale_multiply,
                       logit_scale_divide=logit_scale_divide, logit_softcapping=logit_softcapping,
                       keep_chunk_logits=keep_chunk_logits, clip_eps_low=clip_eps_low, clip_eps_high=clip_eps_high,
                       beta=beta, agg=agg, mask=mask, want_logp=want_logp, want_token_loss=want_token_loss,
                       loss=loss, logp=logp, token_loss=token_loss, dH=dH, dW=dW, workspace=workspace,
                       stream=stream, timer=timer)
+
+
+def grpo_loss_fwd_bwd_static(H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk_tokens, *,
+                             temperature=1.0, logit_scale_multiply=0.0, logit_scale_divide=0.0,
+                             logit_softcapping=0.0, keep_chunk_logits=False, clip_eps_low=0.2, clip_eps_high=0.2,
+                             beta=0.001, agg="seq_mean", mask=None, want_logp=True, want_token_loss=True,
+                             loss=None, logp=None, token_loss=None, dH=None, dW=None, stream=None,
+                             timer: Timer | None = None):
+    """grpo_loss_fwd_bwd through the library's allocation-free entry point: its static
+    per-device scratch (GRPO_STATIC_SCRATCH_BYTES) replaces the workspace, so with every
+    output passed in nothing is allocated.  Calls that overlap on one device race."""
+    return _loss_call(True, H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk_tokens,
+                      temperature=temperature, logit_scale_multiply=logit_scale_multiply,
+                      logit_scale_divide=logit_scale_divide, logit_softcapping=logit_softcapping,
+                      keep_chunk_logits=keep_chunk_logits, clip_eps_low=clip_eps_low, clip_eps_high=clip_eps_high,
+                      beta=beta, agg=agg, mask=mask, want_logp=want_logp, want_token_loss=want_token_loss,
+                      loss=loss, logp=logp, token_loss=token_loss, dH=dH, dW=dW, workspace=None,
+                      stream=stream, timer=timer)
+
+
+GRPO_STATIC_SCRATCH_BYTES = 256 << 20
 
 
 def grpo_debug_token_index(cu_seqlens, T: int, chunk_tokens: int, device="cuda", stream=None):

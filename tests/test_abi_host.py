@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
 
 def test_status_strings():
     lib = B.lib()
-    for s in range(7):
+    for s in range(8):
         assert lib.grpo_status_string(s)
     assert lib.grpo_status_string(99) == b"unknown status"
 
@@ -326,4 +326,27 @@ def test_binding_rejects_bad_arguments_before_the_library(monkeypatch):
                                stream=stream)
     with pytest.raises(TypeError):
         B.grpo_advantages(torch.zeros(S, dtype=torch.float64), 3, stream=stream)
+    with pytest.raises(ValueError):
+        B.grpo_loss_fwd_bwd_static(good["H"], good["W"], good["targets"], good["cu"], good["old"], good["ref"],
+                                   torch.zeros(S - 1), 4, stream=stream)
     assert fake.calls == ["grpo_loss_fwd_bwd"]
+
+
+def test_static_entry_rejects_calls_beyond_its_scratch():
+    # grpo_loss_fwd_bwd_static refuses, before any HIP call, a call whose workspace would pass
+    # the static scratch (256 MiB), and accepts the same shape with a chunk small enough.
+    lib = B.lib()
+    T = 110000
+    cu = np.array([0, 55000, 110000], dtype=np.int32)
+    cup = cu.ctypes.data_as(ctypes.c_void_p)
+    prm = B.GrpoLossParams(0.2, 0.2, 0.001, 0)
+    big = B.make_shape(T, 4096, 151936, 8192, 0)
+    assert B.grpo_workspace_bytes(T, 4096, 151936, 8192, num_seqs=2) > B.GRPO_STATIC_SCRATCH_BYTES
+    st = lib.grpo_loss_fwd_bwd_static(ctypes.byref(big), ctypes.byref(prm), FAKE, FAKE, FAKE, cup, 2, None, FAKE,
+                                      FAKE, FAKE, FAKE, None, None, FAKE, None, None, None)
+    assert st == 7 and b"static scratch" in lib.grpo_status_string(st)
+    assert B.grpo_workspace_bytes(T, 4096, 151936, 256, num_seqs=2) <= B.GRPO_STATIC_SCRATCH_BYTES
+    # host-checkable errors come first, as for grpo_loss_fwd_bwd
+    st = lib.grpo_loss_fwd_bwd_static(ctypes.byref(big), ctypes.byref(prm), None, FAKE, FAKE, cup, 2, None, FAKE,
+                                      FAKE, FAKE, FAKE, None, None, FAKE, None, None, None)
+    assert st == 1
