@@ -87,7 +87,13 @@ typedef enum { GRPO_STD_UNBIASED = 0, GRPO_STD_POPULATION = 1 } grpo_std;
  * vocabulary tile) in fp16, in the buffer the probabilities occupy anyway (no extra
  * memory), and turns them into probabilities in place: 4 D V instead of 6 D V flop per
  * token.  logp, token_loss and the loss are bitwise the same either way; dH differs by the
- * fp16 rounding of d (relative error at most 2^-11 |d| per probability). */
+ * fp16 rounding of d (relative error at most 2^-11 |d| per probability).
+ * dh_fp32 (0 or 1) selects dH's element type for bf16 inputs: 0 writes dH as bf16 (rounded to
+ * nearest even, a relative error of up to 2^-9 per element), from probabilities rounded to
+ * bf16; 1 writes it as fp32 and keeps each entry of the backward's P - onehot as a bf16 pair
+ * hi + lo (lo = the rounding residual of hi, about 16 significant bits together), read by a
+ * dH GEMM twice as long over the vocabulary: per-row relative error ~1e-5 instead of ~1e-3.
+ * fp32 inputs always give fp32 dH (dh_fp32 is ignored). */
 typedef struct {
   int64_t T;
   int64_t D;
@@ -99,6 +105,7 @@ typedef struct {
   float logit_scale_divide;
   float logit_softcapping;
   int32_t keep_chunk_logits;
+  int32_t dh_fp32;     /* 0 or 1: dH is written as fp32 [T, D] for bf16 inputs (see below) */
 } grpo_shape;
 
 /* GRPO objective parameters ([P2], [P3], [P1]).  The ratio is clipped to
@@ -143,7 +150,9 @@ typedef struct grpo_timer grpo_timer; /* opaque, owned by the caller */
  * may also hold fragment-major copies of W^T (for the dH GEMM) and of W (for the logits
  * GEMMs), about D * V * 2 bytes each, and the backward may run over slices of a chunk's
  * tokens (not with dW): the library takes the largest of these layouts that keeps the
- * total within chunk_tokens * V * 4 (grpo_plan_info reports the choice). */
+ * total within chunk_tokens * V * 4 (grpo_plan_info reports the choice).  With dh_fp32 the
+ * probabilities take two bf16 halves (twice the room), and the backward runs in token slices
+ * without the copies when nothing else fits. */
 size_t grpo_workspace_bytes(const grpo_shape* shape, int64_t num_seqs, int with_backward);
 
 /* The workspace layout behind grpo_workspace_bytes for the same arguments (host only, no
@@ -191,7 +200,7 @@ grpo_status grpo_advantages(const float* rewards, int64_t num_seqs, int64_t grou
  *   mask uint8 [T] (NULL = every token counts); old_logp, ref_logp fp32 [T]
  *   (ref_logp may be NULL only when beta == 0); adv fp32 [num_seqs].
  *   loss fp64 [1] (written); logp, token_loss fp32 [T] (written when not NULL;
- *   token_loss holds l_t, unweighted); dH [T, D] of shape->dtype (overwritten;
+ *   token_loss holds l_t, unweighted); dH [T, D] of shape->dtype (fp32 with dh_fp32) (overwritten;
  *   masked tokens get +0 rows); dW fp32 [V, D], 16-byte aligned (NULL = not computed;
  *   bf16 only; else GRPO_E_UNSUPPORTED): the
  *   gradient with respect to W, dW = sum_t (dL/dx_t)^T H_t with x_t = H_t W^T, overwritten
@@ -238,7 +247,7 @@ grpo_status grpo_loss_fwd_bwd_static(const grpo_shape* shape, const grpo_loss_pa
  * the log-probabilities (other GRPO variants, other aggregations) back-propagates through it.
  *   H, W, targets, shape as for grpo_logp_fwd; lse fp32 [T]: the log-sum-exp grpo_logp_fwd
  *   returned for the same H, W and temperature; grad_logp fp32 [T] (dL/dlogp; 0 for tokens
- *   that do not contribute); dH [T, D] of shape->dtype (overwritten; +0 rows where
+ *   that do not contribute); dH [T, D] of shape->dtype (fp32 with dh_fp32) (overwritten; +0 rows where
  *   grad_logp is 0 or the target is outside [0, V)); dW fp32 [V, D] as for
  *   grpo_loss_fwd_bwd (NULL = not computed); workspace of grpo_workspace_bytes(shape, 1, 1)
  *   bytes (1, 2 with dW). */
@@ -252,7 +261,7 @@ grpo_status grpo_logp_bwd(const grpo_shape* shape, const void* H, const void* W,
  *   dH   = the grpo_logp_bwd of g_t = -mask_t / N.
  *   mask uint8 [T] (NULL = every token counts); loss fp64 [1] (written, summed in fp64 in a
  *   fixed token order); logp, token_loss fp32 [T] (written when not NULL; token_loss holds
- *   -logp_t); dH [T, D] of shape->dtype (overwritten); dW fp32 [V, D] as for
+ *   -logp_t); dH [T, D] of shape->dtype (fp32 with dh_fp32) (overwritten); dW fp32 [V, D] as for
  *   grpo_loss_fwd_bwd (NULL = not computed); workspace of grpo_workspace_bytes(shape, 1, 1)
  *   bytes (1, 2 with dW).  A counted token whose target is outside [0, V)
  *   makes the loss NaN; its dH row is +0. */

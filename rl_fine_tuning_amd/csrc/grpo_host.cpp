@@ -31,6 +31,7 @@ grpo_status validate_shape(const grpo_shape* s) {
     if (!isfinite(a) || a < 0.0f) return GRPO_E_VALUE;
   if (s->keep_chunk_logits != 0 && s->keep_chunk_logits != 1) return GRPO_E_VALUE;
   if (s->keep_chunk_logits && s->dtype != GRPO_BF16) return GRPO_E_UNSUPPORTED;
+  if (s->dh_fp32 != 0 && s->dh_fp32 != 1) return GRPO_E_VALUE;
   const LogitMap m = make_logit_map(s);
   for (float a : {m.zscale, m.dscale, m.cap_in})
     if (!isfinite(a)) return GRPO_E_VALUE;
@@ -118,6 +119,12 @@ grpo_status make_plan(const grpo_shape* s, int64_t S, bool backward, Plan* out, 
   p.ks_d = cdiv(p.D, 16);
   p.ks_v = cdiv(p.V, 16);
   p.backward = backward;
+  // fp32 dH for bf16 inputs: each probability is kept as a bf16 pair hi + lo (lo the rounding
+  // residual of hi), in two halves of a row of the probability buffer, so the dH GEMM reads
+  // it at about 16 bits of precision; the halves start on a ring stage (32 entries).
+  p.dh32 = backward && bf16 && s->dh_fp32 != 0;
+  p.ks_lo = p.dh32 ? cdiv(p.ks_v, 2) * 2 : 0;
+  p.ks_q = p.dh32 ? 2 * p.ks_lo : p.ks_v;
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -157,6 +164,7 @@ grpo_status make_plan(const grpo_shape* s, int64_t S, bool backward, Plan* out, 
     p.off_cu = take((size_t)(S + 1) * 4);
     p.off_cnt = take((size_t)S * 4);
     p.off_wseq = take((size_t)S * 8);
+
     const int64_t tail = p.nchunks > 0 ? p.T - (p.nchunks - 1) * p.C : 0;
     // dH partials when the backward of a chunk runs over slices of `rows` tokens: the
     // largest over the slices of a full chunk and of the last chunk.
@@ -172,7 +180,7 @@ grpo_status make_plan(const grpo_shape* s, int64_t S, bool backward, Plan* out, 
       return part;
     };
     auto prob_bytes = [&](int64_t rows) {
-      return bf16 ? (size_t)rows * (size_t)p.ks_v * 16 * 2 : C * (size_t)p.ldp * p.esize;
+      return bf16 ? (size_t)rows * (size_t)p.ks_q * 16 * 2 : C * (size_t)p.ldp * p.esize;
     };
     // Largest layout that fits: both copies with the whole chunk per backward pass; both
     // copies with the backward in two token slices (not with kept logits, which fill the
@@ -181,11 +189,15 @@ grpo_status make_plan(const grpo_shape* s, int64_t S, bool backward, Plan* out, 
     const int64_t full = bf16 ? p.rows_pad : (p.C > 0 ? p.C : 1);
     const int64_t half = bf16 ? cdiv(p.rows_pad / kTileB16, 2) * kTileB16 : full;
     const bool keep = s->keep_chunk_logits != 0;
+    // With fp32 dH (hi + lo probabilities, twice the buffer) one more layout: the backward in
+    // token slices without copies.
     struct Layout { int64_t rows; bool wt, wf; };
-    const Layout options[4] = {{full, true, true}, {half, true, true}, {full, true, false}, {full, false, false}};
+    const Layout options[5] = {{full, true, true}, {half, true, true}, {full, true, false}, {full, false, false},
+                               {half, false, false}};
     Layout pick = options[3];
     for (const Layout& o : options) {
       if (!bf16 || p.nchunks == 0) break;
+      if (&o == &options[4] && !p.dh32) break;
       if (o.rows != full && (keep || dW || o.rows >= full)) continue;
       if (off + align_up(prob_bytes(o.rows)) + align_up(part_bytes(o.rows)) + (o.wt ? wt : 0) + (o.wf ? wf : 0) <=
           bound) {

@@ -150,9 +150,14 @@ struct GemmArgs {
   float* part;            // [ksplit][b_rows][D] (ksplit > 1)
   int D;
   int ksplit;
+  int dh_f32;         // DH / DHT unsplit: dH is written as fp32
+  int lo_ks;          // PROBS: also write the lo halves from this k step (0: none)
+  int a_ks;           // bf16 DHT: k steps of the A copy when they differ from b_ks (0: same)
+  int a_wrap;         // DH / DHT over hi + lo probabilities: A's k step wraps to 0 here (0: none)
   int b_ks;           // bf16: k steps (ceil(K / 16)) of the fragment-major B copy (and A copy)
   int a_frag;         // bf16 LSE / PROBS / LSES: A is the fragment-major copy of W
-  int p_ks;           // bf16 PROBS: k steps (ceil(V / 16)) of the fragment-major probabilities
+  int p_ks;           // bf16 PROBS / LSES: k steps per row of the fragment-major probabilities
+  int v_ks;           // bf16 PROBS / LSES: k steps written (the vocabulary's, even with hi + lo halves)
 };
 
 // The backward's logit gradient Gx[t, v] = dL/dx[t, v] = -c_t Q[t, v] with
@@ -408,15 +413,18 @@ struct DmaFragA {
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t lane_off;  // 16 l
   int w;              // wave index (uniform)
-  __device__ __forceinline__ void init(const void* Af, int ks_count, int tile, int tid) {
+  int wrap;           // k step at which the operand's k index starts again at 0 (0: never)
+  __device__ __forceinline__ void init(const void* Af, int ks_count, int tile, int tid, int wrap_ks = 0) {
     const int64_t bytes = (int64_t)ks_count * kFA * 1024;
     rsrc = make_rsrc(reinterpret_cast<const char*>(Af) + (int64_t)tile * bytes, bytes);
     w = __builtin_amdgcn_readfirstlane(tid >> 6);
     lane_off = (uint32_t)((tid & 63) * 16);
+    wrap = wrap_ks;
   }
   __device__ __forceinline__ void issue(char* lds_stage, int k0, int kend) const {
     const uint32_t v = k0 < kend ? lane_off : kOOB;
-    const uint32_t base = (uint32_t)(k0 >> 4) * (kFA * 1024);
+    const int ks = (wrap > 0 && (k0 >> 4) >= wrap) ? (k0 >> 4) - wrap : (k0 >> 4);
+    const uint32_t base = (uint32_t)ks * (kFA * 1024);
 #pragma unroll
     for (int j = 0; j < kDmaA; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(lds_stage + (kDmaA * w + j) * 1024), 16, v,
@@ -447,9 +455,12 @@ struct TransTileA {
     for (int p = 0; p < 2; ++p)
       voff[p] = d0 + 128 * p + 4 * q < D ? (uint32_t)(((8 * c + 4 * h) * D + 128 * p + 4 * q) * 2) : kOOB;
   }
-  __device__ __forceinline__ void load(int k0, int kend) {
-    const int64_t rows = min(kend - k0, kBK16);
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(W + (int64_t)k0 * D + d0, rows > 0 ? (rows * D - d0) * 2 : 0);
+  // k0 in the (possibly doubled) reduction; wrap: where the vocabulary index starts again at 0
+  // (0: never); rows at or past V, or at or past kend, read as zero.
+  __device__ __forceinline__ void load(int k0, int kend, int wrap, int V) {
+    const int kv = (wrap > 0 && k0 >= wrap) ? k0 - wrap : k0;
+    const int64_t rows = min(min(kend - k0, kBK16), V - kv);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(W + (int64_t)kv * D + d0, rows > 0 ? (rows * D - d0) * 2 : 0);
 #pragma unroll
     for (int p = 0; p < 2; ++p)
 #pragma unroll
@@ -827,7 +838,7 @@ void gemm_kernel(const GemmArgs g) {
 // W read as zero), so the logits epilogues need no masks: they add nothing to the max, their
 // exp is 0, and with a softcap they stay -inf.  Groups of 8 rows (32 i + 8 q + 0..7 of the
 // tile) past the stored width are skipped by uniform scalar tests.
-template <int KIND, bool kSplit, bool kCap>
+template <int KIND, bool kSplit, bool kCap, bool kOut32>
 __device__ __forceinline__ void gemm16_epi(const GemmArgs& g, floatx16 (&acc)[kFA][kFBW], int ks, int tile_a,
                                            int tb) {
   const int tid = threadIdx.x;
@@ -870,7 +881,7 @@ __device__ __forceinline__ void gemm16_epi(const GemmArgs& g, floatx16 (&acc)[kF
       const int tok = row_b0 + 64 * w + 32 * j + col;
       if constexpr (KIND == KIND_LSES) {
         char* P = reinterpret_cast<char*>(g.p);
-        const int vpad = g.p_ks * 16 - row_a0;  // uniform; multiple of 16
+        const int vpad = g.v_ks * 16 - row_a0;  // uniform; multiple of 16
 #pragma unroll
         for (int i = 0; i < kFA; ++i) {
 #pragma unroll
@@ -906,7 +917,7 @@ __device__ __forceinline__ void gemm16_epi(const GemmArgs& g, floatx16 (&acc)[kF
     // written as zeros.  Rows of the copy past the chunk's tokens are written too (every
     // consumer ignores them).
     char* P = reinterpret_cast<char*>(g.p);
-    const int vpad = g.p_ks * 16 - row_a0;  // uniform; multiple of 16
+    const int vpad = g.v_ks * 16 - row_a0;  // uniform; multiple of 16
     const float c1 = g.lm.zscale * kLog2e;
 #pragma unroll
     for (int j = 0; j < kFBW; ++j) {
@@ -926,7 +937,13 @@ __device__ __forceinline__ void gemm16_epi(const GemmArgs& g, floatx16 (&acc)[kF
             e[u] = __builtin_amdgcn_exp2f(fmaf(x, c1, c0));
             if constexpr (kCap) e[u] = e[u] != 0.0f ? e[u] * (1.0f - x * x) : 0.0f;  // past V: x = -inf
           }
-          store4(reinterpret_cast<__bf16*>(P + frag_off(tok, row_a0 + g0 + 4 * hi, g.p_ks)), e[0], e[1], e[2], e[3]);
+          const uint32_t h01 = pack_bf16(e[0], e[1]), h23 = pack_bf16(e[2], e[3]);
+          *reinterpret_cast<uint2*>(P + frag_off(tok, row_a0 + g0 + 4 * hi, g.p_ks)) = make_uint2(h01, h23);
+          if constexpr (kOut32) {  // lo = e - hi, the part the bf16 rounding dropped
+            *reinterpret_cast<uint2*>(P + frag_off(tok, g.lo_ks * 16 + row_a0 + g0 + 4 * hi, g.p_ks)) =
+                make_uint2(pack_bf16(e[0] - bf16_lo(h01), e[1] - bf16_hi(h01)),
+                           pack_bf16(e[2] - bf16_lo(h23), e[3] - bf16_hi(h23)));
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -987,19 +1004,36 @@ __device__ __forceinline__ void gemm16_epi(const GemmArgs& g, floatx16 (&acc)[kF
       }
       const TokGrad tg = tok_grad(g.g, g.targets, g.zy, g.V, g.lm, tok, ok);
       const float nc = -tg.c;
-      __bf16* dst = reinterpret_cast<__bf16*>(g.dh) + (int64_t)(ok ? tok : 0) * g.D;
+      if constexpr (kOut32) {  // fp32 dH (the probabilities were read as hi + lo pairs)
+        float* dst = reinterpret_cast<float*>(g.dh) + (int64_t)(ok ? tok : 0) * g.D;
 #pragma unroll
-      for (int i = 0; i < kFA; ++i) {
+        for (int i = 0; i < kFA; ++i) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (__builtin_expect(32 * i + 8 * q >= drem, 0)) continue;
-          const int d0 = row_a0 + 32 * i + 8 * q + 4 * hi;
-          float o[4];
+          for (int q = 0; q < 4; ++q) {
+            if (__builtin_expect(32 * i + 8 * q >= drem, 0)) continue;
+            const int d0 = row_a0 + 32 * i + 8 * q + 4 * hi;
+            float o[4];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) o[u] = tg.live ? nc * acc[i][j][4 * q + u] : 0.0f;
-          if (ok) store4(dst + d0, o[0], o[1], o[2], o[3]);
+            for (int u = 0; u < 4; ++u) o[u] = tg.live ? nc * acc[i][j][4 * q + u] : 0.0f;
+            if (ok) store4(dst + d0, o[0], o[1], o[2], o[3]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        __bf16* dst = reinterpret_cast<__bf16*>(g.dh) + (int64_t)(ok ? tok : 0) * g.D;
+#pragma unroll
+        for (int i = 0; i < kFA; ++i) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (__builtin_expect(32 * i + 8 * q >= drem, 0)) continue;
+            const int d0 = row_a0 + 32 * i + 8 * q + 4 * hi;
+            float o[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) o[u] = tg.live ? nc * acc[i][j][4 * q + u] : 0.0f;
+            if (ok) store4(dst + d0, o[0], o[1], o[2], o[3]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
   }
@@ -1008,7 +1042,7 @@ __device__ __forceinline__ void gemm16_epi(const GemmArgs& g, floatx16 (&acc)[kF
 // One kernel holds one tile body: the softcap (kCap), the A operand's layout (kFragA) and a
 // split vocabulary (kSplit, dH) are chosen on the host, so register allocation covers a
 // single main loop and epilogue.
-template <int KIND, bool kSplit, bool kCap, bool kFragA>
+template <int KIND, bool kSplit, bool kCap, bool kFragA, bool kOut32>
 __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int ks, int tile_a, int tb) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1050,7 +1084,7 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
                                           typename std::conditional<kFragA, DmaFragA, DmaTileA>::type>::type;
   ATile at;
   if constexpr (kTrans) at.init(A, g.lda, row_a0, tid);
-  else if constexpr (kFragA) at.init(g.a, g.b_ks, tile_a, tid);
+  else if constexpr (kFragA) at.init(g.a, g.a_ks > 0 ? g.a_ks : g.b_ks, tile_a, tid, g.a_wrap);
   else at.init(A, g.lda, row_a0, g.a_rows, tid);
   auto afr = [&](const char* As, int kk, bf16x8 (&a)[kFA]) {
     if constexpr (kFragA) a_frags_f(As, kk, lane, a);
@@ -1062,7 +1096,7 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
     for (int st = 0; st < kStagesA - 1; ++st) {
       const int k0 = k_begin + st * kBK16;
       if constexpr (kTrans) {
-        at.load(k0, k_end);
+        at.load(k0, k_end, g.a_wrap * 16, g.V);
         at.store(smem + st * kAStageBytes);
       } else {
         at.issue(smem + st * kAStageBytes, k0, k_end);
@@ -1088,7 +1122,7 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
       char* sf = smem + slot_f * kAStageBytes;
       slot = slot_n;
       const int kf = k_begin + (kt + kStagesA - 1) * kBK16;
-      if constexpr (kTrans) at.load(kf, k_end);
+      if constexpr (kTrans) at.load(kf, k_end, g.a_wrap * 16, g.V);
       else at.issue(sf, kf, k_end);
       b_load(Bw, ks0 + 2 * (kt + 3), g.b_ks, nxt);
       afr(sc, 1, a1);
@@ -1151,10 +1185,10 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
     __builtin_amdgcn_s_barrier();
   }
 
-  gemm16_epi<KIND, kSplit, kCap>(g, acc, ks, tile_a, tb);
+  gemm16_epi<KIND, kSplit, kCap, kOut32>(g, acc, ks, tile_a, tb);
 }
 
-template <int KIND, bool kSplit, bool kCap, bool kFragA>
+template <int KIND, bool kSplit, bool kCap, bool kFragA, bool kOut32 = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm16_kernel(const GemmArgs g) {
   __shared__ __attribute__((aligned(16))) char smem[kStagesA * kAStageBytes];
@@ -1165,7 +1199,7 @@ void gemm16_kernel(const GemmArgs g) {
     ks = ta / g.tiles_a_base;
     tile_a = ta - ks * g.tiles_a_base;
   }
-  gemm16_tile<KIND, kSplit, kCap, kFragA>(g, smem, ks, tile_a, tb);
+  gemm16_tile<KIND, kSplit, kCap, kFragA, kOut32>(g, smem, ks, tile_a, tb);
 }
 
 // Fragment-major copy of `rows` rows of a row-major bf16 matrix [rows, K] (ld = K), rows
@@ -1230,18 +1264,22 @@ __global__ __launch_bounds__(256) void transpose_w_kernel(const __bf16* __restri
 // probabilities in place: P' = exp(d + m_tile - lse) (times 1 - v^2, v = z / zscale, with a
 // softcap), bf16 rounded to nearest even; rows past the chunk's tokens become 0.  One
 // thread per 16-byte unit (8 consecutive vocabulary entries of one token, one tile).
+// ks_count: the k steps the logits GEMM wrote; ks_stride: k steps per row of P; lo_ks > 0: also write
+// the lo halves (what the bf16 rounding dropped) from that k step on.
 __global__ __launch_bounds__(256) void probs_from_kept_kernel(uint4* __restrict__ P, int64_t units, int rows,
-                                                              int ks_count, const float* __restrict__ pm,
+                                                              int ks_count, int ks_stride, int lo_ks,
+                                                              const float* __restrict__ pm,
                                                               int ntiles, const float* __restrict__ lse_c,
                                                               LogitMap lm) {
-  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (u >= units) return;
-  const int l = (int)(u & 63);
-  const int64_t fr = u >> 6;
+  const int64_t uu = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (uu >= units) return;
+  const int l = (int)(uu & 63);
+  const int64_t fr = uu >> 6;
   const int fb = (int)(fr % kFB);
   const int64_t rest = fr / kFB;
   const int kstep = (int)(rest % ks_count);
   const int tb = (int)(rest / ks_count);
+  const int64_t u = (((int64_t)tb * ks_stride + kstep) * kFB + fb) * 64 + l;
   const int tok = tb * kTB + fb * 32 + (l & 31);
   const int v0 = kstep * 16 + 8 * (l >> 5);
   uint4 out = make_uint4(0u, 0u, 0u, 0u);
@@ -1265,19 +1303,34 @@ __global__ __launch_bounds__(256) void probs_from_kept_kernel(uint4* __restrict_
       }
     }
     out = make_uint4(pack_bf16(e[0], e[1]), pack_bf16(e[2], e[3]), pack_bf16(e[4], e[5]), pack_bf16(e[6], e[7]));
+    if (lo_ks > 0) {
+      float r[8];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const uint32_t w = u4get(out, h);
+        r[2 * h] = e[2 * h] - bf16_lo(w);
+        r[2 * h + 1] = e[2 * h + 1] - bf16_hi(w);
+      }
+      P[u + (int64_t)lo_ks * kFB * 64] =
+          make_uint4(pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3]), pack_bf16(r[4], r[5]), pack_bf16(r[6], r[7]));
+    }
+  } else if (lo_ks > 0) {
+    P[u + (int64_t)lo_ks * kFB * 64] = out;
   }
   P[u] = out;
 }
 
 // Q[t, y_t] = P'[t, y_t] - wyf_t = wyf_t (e^{logp_t} - 1) = wyf_t expm1(z_y - lse), computed in
 // fp32 and rounded once: for a confident token (P'_y near 1) the difference keeps its full
-// relative precision, where e^{logp} - 1 would cancel.  One thread per token of the chunk;
-// tokens with a target outside [0, V) are left alone (their rows get no weight).
+// relative precision, where e^{logp} - 1 would cancel.  With hi + lo pairs (lo_ks > 0: fp32
+// dH) the lo half gets what the rounding dropped.  One thread per token of the chunk; tokens
+// with a target outside [0, V) are left alone (their rows get no weight).
 template <typename T>
 __global__ __launch_bounds__(256) void onehot_fix_kernel(T* __restrict__ P, int rows, int ks_count, int64_t ldp,
                                                          const int32_t* __restrict__ targets_c,
                                                          const float* __restrict__ zy_c,
-                                                         const float* __restrict__ lse_c, int V, LogitMap lm) {
+                                                         const float* __restrict__ lse_c, int V, LogitMap lm,
+                                                         int lo_ks) {
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= rows) return;
   const int y = targets_c[t];
@@ -1291,7 +1344,12 @@ __global__ __launch_bounds__(256) void onehot_fix_kernel(T* __restrict__ P, int 
   const float q = wyf * expm1f(zy - lse_c[t]);  // zy - lse is the token's logp, bit for bit
   if constexpr (sizeof(T) == 2) {
     char* dst = reinterpret_cast<char*>(P) + frag_off(t, y, ks_count);
-    *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(pack_bf16(q, 0.0f) & 0xffffu);
+    const uint32_t b = pack_bf16(q, 0.0f) & 0xffffu;
+    *reinterpret_cast<uint16_t*>(dst) = (uint16_t)b;
+    if (lo_ks > 0) {  // hi + lo pairs: the lo half gets what the rounding dropped
+      char* dlo = reinterpret_cast<char*>(P) + frag_off(t, lo_ks * 16 + y, ks_count);
+      *reinterpret_cast<uint16_t*>(dlo) = (uint16_t)(pack_bf16(q - bf16_lo(b), 0.0f) & 0xffffu);
+    }
   } else {
     P[(int64_t)t * ldp + y] = q;
   }
@@ -1336,7 +1394,8 @@ __global__ __launch_bounds__(256) void ht_copy_kernel(const __bf16* __restrict__
 // One band of the dW GEMM's vocabulary-row operand: Q^T for the band's vocabulary entries
 // (rows, from band0) and the slice's tokens (k), in the fragment-major layout
 // [vr / 256][t / 16][(vr % 256) / 32][lane][8 tokens] with lane = vr % 32 + 32 ((t % 16) / 8),
-// from the slice's fragment-major Q (rows = tokens, k = vocabulary, ks_v k steps).  Block
+// from the slice's fragment-major Q (rows = tokens, k = vocabulary: ks_v k steps of ks_stride;
+// with hi + lo probabilities only the hi half is read).  Block
 // (tb, g) moves one 256-token tile x 64 vocabulary entries (32 fragments of 1 KB each way)
 // through LDS: wave w loads the 8 fragments of vocabulary step 4 g + w (8 KB contiguous, one
 // kilobyte per instruction); thread (f, j) transposes the 8 x 8 block j of fragment f in
@@ -1349,8 +1408,8 @@ __device__ __forceinline__ int qt_in_slot(int f, int l) { return f * 64 + 8 * (l
 __device__ __forceinline__ int qt_out_slot(int F, int L) {
   return F * 64 + 8 * (L >> 3) + (((L & 7) + (L >> 3) + 2 * (F & 1)) & 7);
 }
-__global__ __launch_bounds__(256) void qt_band_kernel(const uint4* __restrict__ Q, int ks_v, int tiles_t,
-                                                      int band0, int ks_t, uint4* __restrict__ out) {
+__global__ __launch_bounds__(256) void qt_band_kernel(const uint4* __restrict__ Q, int ks_v, int ks_stride,
+                                                      int tiles_t, int band0, int ks_t, uint4* __restrict__ out) {
   __shared__ uint4 lds[32 * 64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1360,7 +1419,7 @@ __global__ __launch_bounds__(256) void qt_band_kernel(const uint4* __restrict__ 
   {
     const int v16 = (band0 >> 4) + 4 * g + w;  // this wave's vocabulary step
     const bool in = v16 < ks_v;
-    const uint4* src = Q + ((int64_t)tb * ks_v + v16) * (kFB * 64) + lane;
+    const uint4* src = Q + ((int64_t)tb * ks_stride + v16) * (kFB * 64) + lane;
 #pragma unroll
     for (int k = 0; k < 8; ++k)
       lds[qt_in_slot(8 * w + k, lane)] = in ? src[k * 64] : make_uint4(0u, 0u, 0u, 0u);
@@ -1632,13 +1691,12 @@ __global__ __launch_bounds__(1024) void loss_finalize_kernel(const double* __res
   if (threadIdx.x == 0) loss[0] = sm[0];
 }
 
-// Fixed-order sum of the split-vocabulary dH partials, then (g / tau) (W[y] - sum).
+// Fixed-order sum of the split-vocabulary dH partials, then -c_t sum (T: dH's element type).
 template <typename T>
 __global__ __launch_bounds__(256) void dh_reduce_kernel(const float* __restrict__ part, int ksplit, int rows,
                                                         int D, int V, float dscale,
                                                         const float* __restrict__ g,
-                                                        const int32_t* __restrict__ targets,
-                                                        T* __restrict__ dh) {
+                                                        const int32_t* __restrict__ targets, T* __restrict__ dh) {
   const int quads = D / 4;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)rows * quads) return;
@@ -1714,11 +1772,19 @@ template <int KIND>
 void (*gemm16_pick(const GemmArgs& g))(const GemmArgs) {
   if constexpr (KIND == KIND_DH || KIND == KIND_DHT) {
     constexpr bool kFrag = KIND == KIND_DHT;
-    return g.ksplit > 1 ? gemm16_kernel<KIND, true, false, kFrag> : gemm16_kernel<KIND, false, false, kFrag>;
+    if (g.ksplit > 1) return gemm16_kernel<KIND, true, false, kFrag>;
+    return g.dh_f32 ? gemm16_kernel<KIND, false, false, kFrag, true> : gemm16_kernel<KIND, false, false, kFrag>;
   } else if constexpr (KIND == KIND_DW) {
     return gemm16_kernel<KIND, false, false, true>;
   } else {
     const bool cap = g.lm.cap_in > 0.0f;
+    if constexpr (KIND == KIND_PROBS) {
+      if (g.lo_ks > 0) {  // probabilities as hi + lo pairs (fp32 dH)
+        if (g.a_frag)
+          return cap ? gemm16_kernel<KIND, false, true, true, true> : gemm16_kernel<KIND, false, false, true, true>;
+        return cap ? gemm16_kernel<KIND, false, true, false, true> : gemm16_kernel<KIND, false, false, false, true>;
+      }
+    }
     if (g.a_frag) return cap ? gemm16_kernel<KIND, false, true, true> : gemm16_kernel<KIND, false, false, true>;
     return cap ? gemm16_kernel<KIND, false, true, false> : gemm16_kernel<KIND, false, false, false>;
   }
@@ -1805,7 +1871,8 @@ GemmArgs logits_args(const Plan& p, const T* W, const char* Wf, const T* Hc, con
   g.D = (int)p.D;
   g.ksplit = 1;
   g.b_ks = (int)p.ks_d;
-  g.p_ks = (int)p.ks_v;
+  g.p_ks = (int)p.ks_q;
+  g.v_ks = (int)(p.dh32 ? p.ks_lo : p.ks_v);  // hi + lo: the hi half's padding k step is written too
   return g;
 }
 
@@ -1853,12 +1920,16 @@ grpo_status logp_impl(const Plan& p, const grpo_shape* shape, const T* H, const 
 // dH = g (z'_y W[y] - P' W) (dH GEMM, split over the vocabulary when the slice is too small
 // to fill the GPU) and, if requested, dW (+)= Gx^T H.  Hf holds the chunk's fragment-major
 // hidden states (bf16).
+// dH_c: [rows, D] of T, or fp32 when the plan writes fp32 dH for bf16 inputs (the
+// probabilities then as hi + lo pairs, the dH GEMM's reduction over both halves).
 template <typename T>
 void backward_chunk(Launcher& L, const Plan& p, const T* W, const WCopies<T>& wc, const T* Hc, char* Hf, int rows,
-                    int64_t k, const float* lse_c, const float* g_c, const int32_t* targets_c, T* dH_c, T* P,
+                    int64_t k, const float* lse_c, const float* g_c, const int32_t* targets_c, void* dH_c, T* P,
                     float* part, const LogitMap& lm, const float* zy_c, bool probs_ready, float* dW,
                     char* Qt) {
   const bool bf16 = sizeof(T) == 2;
+  const bool out32 = bf16 && p.dh32;
+  const int64_t dh_esize = out32 ? 4 : (int64_t)sizeof(T);
   const int srows = (int)(p.bwd_rows > 0 && p.bwd_rows < rows ? p.bwd_rows : rows);
   for (int r0 = 0; r0 < rows; r0 += srows) {
     const int sr = rows - r0 < srows ? rows - r0 : srows;
@@ -1867,7 +1938,7 @@ void backward_chunk(Launcher& L, const Plan& p, const T* W, const WCopies<T>& wc
     const int32_t* targets_s = targets_c + r0;
     const float* zy_s = zy_c + r0;
     const T* Hs = Hc + (int64_t)r0 * p.D;
-    T* dH_s = dH_c + (int64_t)r0 * p.D;
+    void* dH_s = reinterpret_cast<char*>(dH_c) + (int64_t)r0 * p.D * dh_esize;
     if (!probs_ready) {
       const char* Hf_s = Hf;
       if constexpr (sizeof(T) == 2) {
@@ -1876,6 +1947,7 @@ void backward_chunk(Launcher& L, const Plan& p, const T* W, const WCopies<T>& wc
         Hf_s = Hf + (int64_t)(r0 / kTileB16) * p.ks_d * kFB * 1024;
       }
       GemmArgs gp = logits_args<T>(p, W, wc.Wf, Hs, Hf_s, sr, lm);
+      gp.lo_ks = out32 ? (int)p.ks_lo : 0;
       gp.lse = lse_s;
       gp.p = P;
       gp.ldp = p.ldp;
@@ -1886,14 +1958,17 @@ void backward_chunk(Launcher& L, const Plan& p, const T* W, const WCopies<T>& wc
     }
 
     L.run(GRPO_K_ONEHOT_FIX, [&] {
-      hipLaunchKernelGGL((onehot_fix_kernel<T>), dim3(grid1(sr, 256)), dim3(256), 0, L.stream, P, sr, (int)p.ks_v,
-                         p.ldp, targets_s, zy_s, lse_s, (int)p.V, lm);
+      hipLaunchKernelGGL((onehot_fix_kernel<T>), dim3(grid1(sr, 256)), dim3(256), 0, L.stream, P, sr, (int)p.ks_q,
+                         p.ldp, targets_s, zy_s, lse_s, (int)p.V, lm, out32 ? (int)p.ks_lo : 0);
     });
 
-    // dH^T tiles: hidden x tokens, K = vocabulary, split over the vocabulary if needed.
+    // dH^T tiles: hidden x tokens, K = vocabulary, split over the vocabulary if needed.  With
+    // hi + lo probabilities (fp32 dH) the reduction runs over the hi half (ks_lo k steps, the
+    // part past V zero) and then the lo half, W's vocabulary index starting again at 0.
+    const int64_t Kd = out32 ? p.ks_lo * 16 + p.V : p.V;
     const int ks_plan = dh_ksplit(sr, p.D, p.V, p.dtype);
-    const int k_len = (int)(cdiv(cdiv(p.V, ks_plan), p.bk) * p.bk);
-    const int ksplit = (int)cdiv(p.V, k_len);
+    const int k_len = (int)(cdiv(cdiv(Kd, ks_plan), p.bk) * p.bk);
+    const int ksplit = (int)cdiv(Kd, k_len);
     GemmArgs gd = {};
     gd.a = wc.WT ? static_cast<const void*>(wc.WT) : static_cast<const void*>(W);
     gd.b = P;
@@ -1901,7 +1976,7 @@ void backward_chunk(Launcher& L, const Plan& p, const T* W, const WCopies<T>& wc
     gd.ldb = p.ldp;
     gd.a_rows = (int)p.D;
     gd.b_rows = sr;
-    gd.K = (int)p.V;
+    gd.K = (int)Kd;
     gd.k_len = k_len;
     gd.tiles_a_base = (int)cdiv(p.D, bf16 ? kTileA16 : kTile);
     gd.tiles_a = gd.tiles_a_base * ksplit;
@@ -1913,12 +1988,15 @@ void backward_chunk(Launcher& L, const Plan& p, const T* W, const WCopies<T>& wc
     int xb = 8;
     while (xb > 1 && gd.tiles_b / xb < gd.group_b) xb >>= 1;
     gd.xcd_a = 8 / xb;
-    gd.b_ks = (int)p.ks_v;
+    gd.b_ks = (int)p.ks_q;
+    gd.a_ks = (int)p.ks_v;
+    gd.a_wrap = out32 ? (int)p.ks_lo : 0;
     gd.lm = lm;
     gd.zy = zy_s;
     gd.g = g_s;
     gd.targets = targets_s;
     gd.dh = dH_s;
+    gd.dh_f32 = out32;
     gd.part = part;
     gd.V = (int)p.V;
     gd.D = (int)p.D;
@@ -1927,8 +2005,13 @@ void backward_chunk(Launcher& L, const Plan& p, const T* W, const WCopies<T>& wc
     else launch_gemm<T, KIND_DH>(L, GRPO_K_DH_GEMM, gd);
     if (ksplit > 1) {
       L.run(GRPO_K_DH_REDUCE, [&] {
-        hipLaunchKernelGGL((dh_reduce_kernel<T>), dim3(grid1((int64_t)sr * (p.D / 4), 256)), dim3(256), 0,
-                           L.stream, part, ksplit, sr, (int)p.D, (int)p.V, lm.dscale, g_s, targets_s, dH_s);
+        const dim3 grid(grid1((int64_t)sr * (p.D / 4), 256));
+        if (out32)
+          hipLaunchKernelGGL((dh_reduce_kernel<float>), grid, dim3(256), 0, L.stream, part, ksplit, sr, (int)p.D,
+                             (int)p.V, lm.dscale, g_s, targets_s, reinterpret_cast<float*>(dH_s));
+        else
+          hipLaunchKernelGGL((dh_reduce_kernel<T>), grid, dim3(256), 0, L.stream, part, ksplit, sr, (int)p.D,
+                             (int)p.V, lm.dscale, g_s, targets_s, reinterpret_cast<T*>(dH_s));
       });
     }
     if constexpr (sizeof(T) == 2) {
@@ -1951,7 +2034,7 @@ void backward_chunk(Launcher& L, const Plan& p, const T* W, const WCopies<T>& wc
           const int tiles_t = ks_t / 16;  // 256-token tiles of the slice
           L.run(GRPO_K_QT_BAND, [&] {
             hipLaunchKernelGGL(qt_band_kernel, dim3(tiles_t * nb * (kTileA16 / 64)), dim3(256), 0, L.stream,
-                               reinterpret_cast<const uint4*>(P), (int)p.ks_v, tiles_t, band0, ks_t,
+                               reinterpret_cast<const uint4*>(P), (int)p.ks_v, (int)p.ks_q, tiles_t, band0, ks_t,
                                reinterpret_cast<uint4*>(Qt));
           });
           // A: (-c H)^T (rows = hidden units), B: the band of Q^T (rows = vocabulary entries)
@@ -1988,7 +2071,7 @@ template <typename T>
 grpo_status loss_impl(const Plan& p, const grpo_shape* shape, int mode, const grpo_loss_params* prm, const T* H,
                       const T* W, const int32_t* targets, const int32_t* cu_host, const uint8_t* mask,
                       const float* old_logp, const float* ref_logp, const float* adv, double* loss,
-                      float* logp, float* token_loss, T* dH, float* dW, char* ws, Launcher& L) {
+                      float* logp, float* token_loss, void* dH, float* dW, char* ws, Launcher& L) {
   const LogitMap lm = make_logit_map(shape);
   float* zy = reinterpret_cast<float*>(ws + p.off_zy);
   float* lse = reinterpret_cast<float*>(ws + p.off_lse);
@@ -2003,6 +2086,7 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, int mode, const gr
   T* P = reinterpret_cast<T*>(ws + p.off_P);
   char* Hf = ws + p.off_Hf;
   float* part = reinterpret_cast<float*>(ws + p.off_part);
+  const int64_t dh_esize = p.dh32 ? 4 : (int64_t)sizeof(T);
   const int S = (int)p.S;
   const int agg = mode == 2 ? (int)GRPO_AGG_TOKEN_MEAN : (int)prm->agg;
 
@@ -2079,15 +2163,17 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, int mode, const gr
       hipLaunchKernelGGL(merge_kernel, dim3(grid1(rows, 4)), dim3(256), 0, L.stream, m);
     });
     if (keep) {
-      const int64_t units = p.rows_pad * p.ks_v * 2;
+      const int64_t ks_w = p.dh32 ? p.ks_lo : p.ks_v;  // the k steps the logits GEMM wrote
+      const int64_t units = p.rows_pad * ks_w * 2;
       L.run(GRPO_K_PROBS_KEPT, [&] {
         hipLaunchKernelGGL(probs_from_kept_kernel, dim3(grid1(units, 256)), dim3(256), 0, L.stream,
-                           reinterpret_cast<uint4*>(P), units, rows, (int)p.ks_v, pm, (int)p.ntiles_v, lse + t0,
-                           lm);
+                           reinterpret_cast<uint4*>(P), units, rows, (int)ks_w, (int)p.ks_q,
+                           p.dh32 ? (int)p.ks_lo : 0, pm, (int)p.ntiles_v, lse + t0, lm);
       });
     }
-    backward_chunk<T>(L, p, W, wc, Hc, Hf, rows, k, lse + t0, gbuf + t0, targets + t0, dH + t0 * p.D, P,
-                      part, lm, zy + t0, keep, dW, ws + p.off_Qt);
+    backward_chunk<T>(L, p, W, wc, Hc, Hf, rows, k, lse + t0, gbuf + t0, targets + t0,
+                      reinterpret_cast<char*>(dH) + t0 * p.D * dh_esize, P, part, lm, zy + t0, keep, dW,
+                      ws + p.off_Qt);
   }
   if (dW && p.nchunks == 0)  // no tokens: the gradient is 0
     hipLaunchKernelGGL(zero_fill_kernel, dim3(1024), dim3(256), 0, L.stream, dW, (int64_t)p.V * p.D);
@@ -2100,12 +2186,13 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, int mode, const gr
 // Backward of grpo_logp_fwd: dH = (grad / tau) (W[y] - P W) per chunk, from the forward's lse.
 template <typename T>
 grpo_status logp_bwd_impl(const Plan& p, const grpo_shape* shape, const T* H, const T* W, const int32_t* targets,
-                          const float* lse, const float* grad, T* dH, float* dW, char* ws, Launcher& L) {
+                          const float* lse, const float* grad, void* dH, float* dW, char* ws, Launcher& L) {
   const LogitMap lm = make_logit_map(shape);
   T* P = reinterpret_cast<T*>(ws + p.off_P);
   char* Hf = ws + p.off_Hf;
   float* part = reinterpret_cast<float*>(ws + p.off_part);
   float* zy = reinterpret_cast<float*>(ws + p.off_zy);
+  const int64_t dh_esize = p.dh32 ? 4 : (int64_t)sizeof(T);
   {  // the target logits: the exact target entry of Q (and the softcap factor there)
     L.run(GRPO_K_TARGET_LOGIT, [&] {
       hipLaunchKernelGGL((target_logit_kernel<T>), dim3(grid1(p.T, 4)), dim3(256), 0, L.stream, H, W, targets,
@@ -2118,8 +2205,9 @@ grpo_status logp_bwd_impl(const Plan& p, const grpo_shape* shape, const T* H, co
     const int rows = (int)(p.T - t0 < p.C ? p.T - t0 : p.C);
     const T* Hc = H + t0 * p.D;
     if constexpr (sizeof(T) == 2) enqueue_frag_copy(L, p, Hc, rows, Hf);
-    backward_chunk<T>(L, p, W, wc, Hc, Hf, rows, k, lse + t0, grad + t0, targets + t0, dH + t0 * p.D, P,
-                      part, lm, zy + t0, false, dW, ws + p.off_Qt);
+    backward_chunk<T>(L, p, W, wc, Hc, Hf, rows, k, lse + t0, grad + t0, targets + t0,
+                      reinterpret_cast<char*>(dH) + t0 * p.D * dh_esize, P, part, lm, zy + t0, false, dW,
+                      ws + p.off_Qt);
   }
   return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_E_HIP;
 }
@@ -2157,9 +2245,9 @@ grpo_status loss_run(const Plan& p, const grpo_shape* shape, const grpo_loss_par
   const float* ref = params->beta != 0.0f ? ref_logp : nullptr;
   if (p.dtype == GRPO_BF16)
     return loss_impl<__bf16>(p, shape, 1, params, (const __bf16*)H, (const __bf16*)W, targets, cu_seqlens, mask,
-                             old_logp, ref, adv, loss, logp, token_loss, (__bf16*)dH, dW, ws, L);
+                             old_logp, ref, adv, loss, logp, token_loss, dH, dW, ws, L);
   return loss_impl<float>(p, shape, 1, params, (const float*)H, (const float*)W, targets, cu_seqlens, mask,
-                          old_logp, ref, adv, loss, logp, token_loss, (float*)dH, nullptr, ws, L);
+                          old_logp, ref, adv, loss, logp, token_loss, dH, nullptr, ws, L);
 }
 
 // Device address of this device's copy of `scratch`, looked up once per device (with that
@@ -2274,8 +2362,8 @@ grpo_status grpo_logp_bwd(const grpo_shape* shape, const void* H, const void* W,
   char* ws = reinterpret_cast<char*>(workspace);
   if (p.dtype == GRPO_BF16)
     return logp_bwd_impl<__bf16>(p, shape, (const __bf16*)H, (const __bf16*)W, targets, lse, grad_logp,
-                                 (__bf16*)dH, dW, ws, L);
-  return logp_bwd_impl<float>(p, shape, (const float*)H, (const float*)W, targets, lse, grad_logp, (float*)dH,
+                                 dH, dW, ws, L);
+  return logp_bwd_impl<float>(p, shape, (const float*)H, (const float*)W, targets, lse, grad_logp, dH,
                               nullptr, ws, L);
 }
 
@@ -2297,9 +2385,9 @@ grpo_status grpo_ce_loss_fwd_bwd(const grpo_shape* shape, const void* H, const v
   // one sequence spanning the stream (its bounds are written on the device): token-mean weights
   if (p.dtype == GRPO_BF16)
     return loss_impl<__bf16>(p, shape, 2, nullptr, (const __bf16*)H, (const __bf16*)W, targets, nullptr, mask,
-                             nullptr, nullptr, nullptr, loss, logp, token_loss, (__bf16*)dH, dW, ws, L);
+                             nullptr, nullptr, nullptr, loss, logp, token_loss, dH, dW, ws, L);
   return loss_impl<float>(p, shape, 2, nullptr, (const float*)H, (const float*)W, targets, nullptr, mask, nullptr,
-                          nullptr, nullptr, loss, logp, token_loss, (float*)dH, nullptr, ws, L);
+                          nullptr, nullptr, loss, logp, token_loss, dH, nullptr, ws, L);
 }
 
 grpo_status grpo_debug_token_index(const int32_t* cu_seqlens, int64_t num_seqs, int64_t T, int64_t chunk_tokens,

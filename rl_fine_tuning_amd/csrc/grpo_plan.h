@@ -40,6 +40,9 @@ struct Plan {
   bool use_wf = false;    // bf16: the logits GEMMs read a fragment-major W from the workspace
   int64_t bwd_rows = 0;   // tokens per backward slice (bf16: a multiple of 256; >= C when unsliced)
   int64_t qt_tiles = 0;   // bf16 with dW: vocabulary tiles per band of the dW GEMM's transposed operand
+  bool dh32 = false;      // bf16 backward writing fp32 dH: the probabilities as bf16 hi + lo pairs
+  int64_t ks_q = 0;       // bf16: k steps per row of the probability buffer (ks_v, or 2 ks_lo with dh32)
+  int64_t ks_lo = 0;      // bf16 with dh32: first k step of the lo half (ks_v rounded up to even)
   bool backward = false;
   size_t off_zy = 0, off_lse = 0, off_pm = 0, off_ps = 0;
   size_t off_g = 0, off_wl = 0, off_seq = 0, off_cu = 0, off_cnt = 0, off_wseq = 0;

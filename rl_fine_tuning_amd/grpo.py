@@ -29,7 +29,7 @@ class GrpoShape(ctypes.Structure):
                 ("chunk_tokens", ctypes.c_int64), ("dtype", ctypes.c_int32),
                 ("temperature", ctypes.c_float), ("logit_scale_multiply", ctypes.c_float),
                 ("logit_scale_divide", ctypes.c_float), ("logit_softcapping", ctypes.c_float),
-                ("keep_chunk_logits", ctypes.c_int32)]
+                ("keep_chunk_logits", ctypes.c_int32), ("dh_fp32", ctypes.c_int32)]
 
 
 class GrpoLossParams(ctypes.Structure):
@@ -162,11 +162,15 @@ def _hw(H, W, targets):
 
 
 def make_shape(T, D, V, chunk_tokens, dtype, temperature=1.0, logit_scale_multiply=0.0, logit_scale_divide=0.0,
-               logit_softcapping=0.0, keep_chunk_logits=False) -> GrpoShape:
+               logit_softcapping=0.0, keep_chunk_logits=False, dh_fp32=False) -> GrpoShape:
     """0 for a logit argument means 'not used' (see grpo_shape in include/grpo.h)."""
     return GrpoShape(int(T), int(D), int(V), int(chunk_tokens), int(dtype), float(temperature),
                      float(logit_scale_multiply), float(logit_scale_divide), float(logit_softcapping),
-                     int(bool(keep_chunk_logits)))
+                     int(bool(keep_chunk_logits)), int(bool(dh_fp32)))
+
+
+def _dh_dtype(H, dh_fp32):
+    return torch.float32 if dh_fp32 else H.dtype
 
 
 def _bwd_mode(with_backward, with_dW):
@@ -175,18 +179,18 @@ def _bwd_mode(with_backward, with_dW):
 
 def grpo_workspace_bytes(T, D, V, chunk_tokens, dtype=GRPO_BF16, temperature=1.0, num_seqs=1,
                          with_backward=True, logit_softcapping=0.0, keep_chunk_logits=False,
-                         with_dW=False) -> int:
+                         with_dW=False, dh_fp32=False) -> int:
     shape = make_shape(T, D, V, chunk_tokens, dtype, temperature, logit_softcapping=logit_softcapping,
-                       keep_chunk_logits=keep_chunk_logits)
+                       keep_chunk_logits=keep_chunk_logits, dh_fp32=dh_fp32)
     return int(lib().grpo_workspace_bytes(ctypes.byref(shape), int(num_seqs), _bwd_mode(with_backward, with_dW)))
 
 
 def grpo_plan_info(T, D, V, chunk_tokens, dtype=GRPO_BF16, temperature=1.0, num_seqs=1, with_backward=True,
-                   logit_softcapping=0.0, keep_chunk_logits=False, with_dW=False) -> dict:
+                   logit_softcapping=0.0, keep_chunk_logits=False, with_dW=False, dh_fp32=False) -> dict:
     """The library's workspace layout for a call: which fragment-major copies of W it keeps,
     the tokens per backward slice and the workspace bytes."""
     shape = make_shape(T, D, V, chunk_tokens, dtype, temperature, logit_softcapping=logit_softcapping,
-                       keep_chunk_logits=keep_chunk_logits)
+                       keep_chunk_logits=keep_chunk_logits, dh_fp32=dh_fp32)
     info = (ctypes.c_int64 * 4)()
     st = lib().grpo_plan_info(ctypes.byref(shape), int(num_seqs), _bwd_mode(with_backward, with_dW), info)
     _check(st, "grpo_plan_info")
@@ -255,9 +259,10 @@ class Timer:
 
 def grpo_logp_fwd(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, chunk_tokens: int,
                   temperature: float = 1.0, *, logit_scale_multiply=0.0, logit_scale_divide=0.0,
-                  logit_softcapping=0.0, return_lse: bool = False, out=None, workspace=None,
+                  logit_softcapping=0.0, return_lse: bool = False, out=None, lse=None, workspace=None,
                   stream=None, timer: Timer | None = None):
-    """logp[t] = log softmax(H[t] W^T / temperature)[targets[t]] (fp32), chunked."""
+    """logp[t] = log softmax(H[t] W^T / temperature)[targets[t]] (fp32), chunked.  With
+    return_lse (or an fp32 [T] `lse` given) also the per-token log-sum-exp."""
     T, D, V = _hw(H, W, targets)
     dev = H.device
     shape = make_shape(T, D, V, chunk_tokens, _dtype_code(H), temperature, logit_scale_multiply,
@@ -266,7 +271,8 @@ def grpo_logp_fwd(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, chunk
     with _on(stream):
         ws, wsn = _workspace(nbytes, workspace, dev)
         logp = _out(out, "out", dev, torch.float32, (T,))
-        lse = torch.empty(T, dtype=torch.float32, device=dev) if return_lse else None
+        return_lse = return_lse or lse is not None
+        lse = _out(lse, "lse", dev, torch.float32, (T,)) if return_lse else None
         st = lib().grpo_logp_fwd(ctypes.byref(shape), _ptr(H), _ptr(W), _ptr(targets), _ptr(logp), _ptr(lse),
                                  _ptr(ws), wsn, _stream(stream), timer.handle if timer else None)
     _check(st, "grpo_logp_fwd")
@@ -275,7 +281,7 @@ def grpo_logp_fwd(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, chunk
 
 def grpo_logp_bwd(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: torch.Tensor,
                   grad_logp: torch.Tensor, chunk_tokens: int, temperature: float = 1.0, *,
-                  logit_scale_multiply=0.0, logit_scale_divide=0.0, logit_softcapping=0.0, dH=None,
+                  logit_scale_multiply=0.0, logit_scale_divide=0.0, logit_softcapping=0.0, dh_fp32=False, dH=None,
                   dW=None, workspace=None, stream=None, timer: Timer | None = None):
     """dH of sum_t grad_logp[t] * logp_t, recomputing each chunk's logits from the forward's lse.
     With dW (an fp32 [V, D] tensor, or True to allocate one) returns (dH, dW).  A caller's
@@ -285,12 +291,12 @@ def grpo_logp_bwd(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: 
     _dev(lse, "lse", dev, torch.float32, (T,))
     _dev(grad_logp, "grad_logp", dev, torch.float32, (T,))
     shape = make_shape(T, D, V, chunk_tokens, _dtype_code(H), temperature, logit_scale_multiply,
-                       logit_scale_divide, logit_softcapping)
+                       logit_scale_divide, logit_softcapping, dh_fp32=dh_fp32)
     with _on(stream):
         dW = _want_dW(dW, V, D, dev)
         nbytes = int(lib().grpo_workspace_bytes(ctypes.byref(shape), 1, 2 if dW is not None else 1))
         ws, wsn = _workspace(nbytes, workspace, dev)
-        dH = _out(dH, "dH", dev, H.dtype, (T, D))
+        dH = _out(dH, "dH", dev, _dh_dtype(H, dh_fp32), (T, D))
         st = lib().grpo_logp_bwd(ctypes.byref(shape), _ptr(H), _ptr(W), _ptr(targets), _ptr(lse), _ptr(grad_logp),
                                  _ptr(dH), _ptr(dW), _ptr(ws), wsn, _stream(stream), timer.handle if timer else None)
     _check(st, "grpo_logp_bwd")
@@ -298,9 +304,9 @@ def grpo_logp_bwd(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: 
 
 
 def grpo_ce_loss_fwd_bwd(H, W, targets, chunk_tokens, *, temperature=1.0, logit_scale_multiply=0.0,
-                         logit_scale_divide=0.0, logit_softcapping=0.0, keep_chunk_logits=False, mask=None,
-                         want_logp=True, want_token_loss=False, dH=None, dW=None, workspace=None, stream=None,
-                         timer: Timer | None = None):
+                         logit_scale_divide=0.0, logit_softcapping=0.0, keep_chunk_logits=False, dh_fp32=False,
+                         mask=None, want_logp=True, want_token_loss=False, loss=None, logp=None, token_loss=None,
+                         dH=None, dW=None, workspace=None, stream=None, timer: Timer | None = None):
     """Mean cross-entropy over the unmasked tokens, per-token logp, dL/dH and (with dW: an
     fp32 [V, D] tensor, or True to allocate one) dL/dW.  A caller's workspace must hold
     grpo_workspace_bytes(..., with_dW=bool(dW)) bytes."""
@@ -309,15 +315,16 @@ def grpo_ce_loss_fwd_bwd(H, W, targets, chunk_tokens, *, temperature=1.0, logit_
     if mask is not None:
         _dev(mask, "mask", dev, _MASK, (T,))
     shape = make_shape(T, D, V, chunk_tokens, _dtype_code(H), temperature, logit_scale_multiply,
-                       logit_scale_divide, logit_softcapping, keep_chunk_logits)
+                       logit_scale_divide, logit_softcapping, keep_chunk_logits, dh_fp32)
     with _on(stream):
         dW = _want_dW(dW, V, D, dev)
         nbytes = int(lib().grpo_workspace_bytes(ctypes.byref(shape), 1, 2 if dW is not None else 1))
         ws, wsn = _workspace(nbytes, workspace, dev)
-        loss = torch.empty(1, dtype=torch.float64, device=dev)
-        logp = torch.empty(T, dtype=torch.float32, device=dev) if want_logp else None
-        tl = torch.empty(T, dtype=torch.float32, device=dev) if want_token_loss else None
-        dH = _out(dH, "dH", dev, H.dtype, (T, D))
+        loss = _out(loss, "loss", dev, torch.float64, (1,))
+        logp = _out(logp, "logp", dev, torch.float32, (T,)) if want_logp or logp is not None else None
+        tl = (_out(token_loss, "token_loss", dev, torch.float32, (T,))
+              if want_token_loss or token_loss is not None else None)
+        dH = _out(dH, "dH", dev, _dh_dtype(H, dh_fp32), (T, D))
         st = lib().grpo_ce_loss_fwd_bwd(ctypes.byref(shape), _ptr(H), _ptr(W), _ptr(targets), _ptr(mask),
                                         _ptr(loss), _ptr(logp), _ptr(tl), _ptr(dH), _ptr(dW), _ptr(ws), wsn,
                                         _stream(stream), timer.handle if timer else None)
@@ -339,7 +346,7 @@ def grpo_advantages(rewards: torch.Tensor, group_size: int, std_mode: str = "unb
 
 
 def _loss_call(static, H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk_tokens, *, temperature,
-               logit_scale_multiply, logit_scale_divide, logit_softcapping, keep_chunk_logits, clip_eps_low,
+               logit_scale_multiply, logit_scale_divide, logit_softcapping, keep_chunk_logits, dh_fp32, clip_eps_low,
                clip_eps_high, beta, agg, mask, want_logp, want_token_loss, loss, logp, token_loss, dH, dW,
                workspace, stream, timer):
     T, D, V = _hw(H, W, targets)
@@ -356,7 +363,7 @@ def _loss_call(static, H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk
     if mask is not None:
         _dev(mask, "mask", dev, _MASK, (T,))
     shape = make_shape(T, D, V, chunk_tokens, _dtype_code(H), temperature, logit_scale_multiply,
-                       logit_scale_divide, logit_softcapping, keep_chunk_logits)
+                       logit_scale_divide, logit_softcapping, keep_chunk_logits, dh_fp32)
     params = GrpoLossParams(float(clip_eps_low), float(clip_eps_high), float(beta), GRPO_AGG[agg])
     with _on(stream):
         dW = _want_dW(dW, V, D, dev)
@@ -364,7 +371,7 @@ def _loss_call(static, H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk
         logp = _out(logp, "logp", dev, torch.float32, (T,)) if want_logp or logp is not None else None
         tl = (_out(token_loss, "token_loss", dev, torch.float32, (T,))
               if want_token_loss or token_loss is not None else None)
-        dH = _out(dH, "dH", dev, H.dtype, (T, D))
+        dH = _out(dH, "dH", dev, _dh_dtype(H, dh_fp32), (T, D))
         args = [ctypes.byref(shape), ctypes.byref(params), _ptr(H), _ptr(W), _ptr(targets),
                 ctypes.c_void_p(cu.data_ptr()), S, _ptr(mask), _ptr(old_logp), _ptr(ref_logp), _ptr(adv),
                 _ptr(loss), _ptr(logp), _ptr(tl), _ptr(dH), _ptr(dW)]
@@ -380,7 +387,8 @@ def _loss_call(static, H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk
 
 def grpo_loss_fwd_bwd(H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk_tokens, *,
                       temperature=1.0, logit_scale_multiply=0.0, logit_scale_divide=0.0, logit_softcapping=0.0,
-                      keep_chunk_logits=False, clip_eps_low=0.2, clip_eps_high=0.2, beta=0.001, agg="seq_mean",
+                      keep_chunk_logits=False, dh_fp32=False, clip_eps_low=0.2, clip_eps_high=0.2, beta=0.001,
+                      agg="seq_mean",
                       mask=None, want_logp=True, want_token_loss=True, loss=None, logp=None, token_loss=None,
                       dH=None, dW=None, workspace=None, stream=None, timer: Timer | None = None):
     """GRPO loss, per-token logp and objective, and dL/dH (and dL/dW with dW: an fp32 [V, D]
@@ -390,7 +398,8 @@ def grpo_loss_fwd_bwd(H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk_
     return _loss_call(False, H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk_tokens,
                       temperature=temperature, logit_scale_multiply=logit_scale_multiply,
                       logit_scale_divide=logit_scale_divide, logit_softcapping=logit_softcapping,
-                      keep_chunk_logits=keep_chunk_logits, clip_eps_low=clip_eps_low, clip_eps_high=clip_eps_high,
+                      keep_chunk_logits=keep_chunk_logits, dh_fp32=dh_fp32, clip_eps_low=clip_eps_low,
+                      clip_eps_high=clip_eps_high,
                       beta=beta, agg=agg, mask=mask, want_logp=want_logp, want_token_loss=want_token_loss,
                       loss=loss, logp=logp, token_loss=token_loss, dH=dH, dW=dW, workspace=workspace,
                       stream=stream, timer=timer)
@@ -398,7 +407,8 @@ def grpo_loss_fwd_bwd(H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk_
 
 def grpo_loss_fwd_bwd_static(H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk_tokens, *,
                              temperature=1.0, logit_scale_multiply=0.0, logit_scale_divide=0.0,
-                             logit_softcapping=0.0, keep_chunk_logits=False, clip_eps_low=0.2, clip_eps_high=0.2,
+                             logit_softcapping=0.0, keep_chunk_logits=False, dh_fp32=False, clip_eps_low=0.2,
+                             clip_eps_high=0.2,
                              beta=0.001, agg="seq_mean", mask=None, want_logp=True, want_token_loss=True,
                              loss=None, logp=None, token_loss=None, dH=None, dW=None, stream=None,
                              timer: Timer | None = None):
@@ -408,7 +418,8 @@ def grpo_loss_fwd_bwd_static(H, W, targets, cu_seqlens, old_logp, ref_logp, adv,
     return _loss_call(True, H, W, targets, cu_seqlens, old_logp, ref_logp, adv, chunk_tokens,
                       temperature=temperature, logit_scale_multiply=logit_scale_multiply,
                       logit_scale_divide=logit_scale_divide, logit_softcapping=logit_softcapping,
-                      keep_chunk_logits=keep_chunk_logits, clip_eps_low=clip_eps_low, clip_eps_high=clip_eps_high,
+                      keep_chunk_logits=keep_chunk_logits, dh_fp32=dh_fp32, clip_eps_low=clip_eps_low,
+                      clip_eps_high=clip_eps_high,
                       beta=beta, agg=agg, mask=mask, want_logp=want_logp, want_token_loss=want_token_loss,
                       loss=loss, logp=logp, token_loss=token_loss, dH=dH, dW=dW, workspace=None,
                       stream=stream, timer=timer)

@@ -198,8 +198,9 @@ def check_loss_outputs(k, got, *, rows=None, dh_bar=DH_REL_L2):
         assert np.isnan(L)
     else:
         assert abs(L - o["loss"]) <= LOSS_RTOL * scale, f"loss {L} vs {o['loss']} (scale {scale})"
-    dH = host_matrix(got["dH"], k["dtype"])
-    dH = oracle.widen(dH[rows], k["dtype"])
+    dh_dt = "f32" if got["dH"].dtype == torch.float32 else k["dtype"]  # fp32 dH for bf16 inputs too
+    dH = host_matrix(got["dH"], dh_dt)
+    dH = oracle.widen(dH[rows], dh_dt)
     ref = o["dH"][rows]
     amb = near_clip_boundary(o["logp"][rows], k["old"][rows].astype(np.float64),
                              k["prm"]["clip_eps_low"], k["prm"]["clip_eps_high"])

@@ -350,3 +350,22 @@ def test_static_entry_rejects_calls_beyond_its_scratch():
     st = lib.grpo_loss_fwd_bwd_static(ctypes.byref(big), ctypes.byref(prm), None, FAKE, FAKE, cup, 2, None, FAKE,
                                       FAKE, FAKE, FAKE, None, None, FAKE, None, None, None)
     assert st == 1
+
+
+def test_dh_fp32_validation_and_plan():
+    lib = B.lib()
+    sh = B.make_shape(100, 64, 512, 32, 0)
+    sh.dh_fp32 = 2
+    assert lib.grpo_workspace_bytes(ctypes.byref(sh), 1, 1) == 0  # 0 or 1 only
+    # fp32 dH keeps the probabilities as bf16 hi + lo pairs: the buffer doubles (both halves
+    # padded to an even number of 16-entry k steps)
+    a = B.grpo_workspace_bytes(1000, 64, 512, 256)
+    b = B.grpo_workspace_bytes(1000, 64, 512, 256, dh_fp32=True)
+    assert b - a == 256 * 2 * 32 * 16 * 2 - 256 * 32 * 16 * 2
+    assert B.grpo_workspace_bytes(1000, 64, 512, 256, dtype=1, dh_fp32=True) == \
+        B.grpo_workspace_bytes(1000, 64, 512, 256, dtype=1)  # fp32 inputs: dH is fp32 anyway
+    # at the Qwen3-8B shape the doubled buffer fits the one-chunk bound by slicing the backward
+    i = B.grpo_plan_info(110000, 4096, 151936, 8192, num_seqs=2, dh_fp32=True)
+    assert i["backward_slice_tokens"] == 4096 and i["workspace_bytes"] <= 8192 * 151936 * 4
+    assert B.grpo_plan_info(110000, 4096, 151936, 8192, num_seqs=2) == \
+        B.grpo_plan_info(110000, 4096, 151936, 8192, num_seqs=2, dh_fp32=False)

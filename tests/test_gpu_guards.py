@@ -1,0 +1,125 @@
+"""Guard canaries: each output and the workspace of every entry point sits inside a larger
+buffer whose bytes before and after it hold a known pattern, and after the call the pattern
+must be intact.  The library may write only its outputs and a workspace whose size
+grpo_workspace_bytes states (bounded by one chunk's fp32 logits: "Reinforcement Learning GRPO
+mit 7x laengerem Kontext", section "Chunking der abgeflachten Sequenzlaenge", Eq. 3)."""
+import numpy as np
+import pytest
+import torch
+
+from rl_fine_tuning_amd import (grpo_ce_loss_fwd_bwd, grpo_logp_bwd, grpo_logp_fwd, grpo_loss_fwd_bwd,
+                                grpo_loss_fwd_bwd_static, grpo_workspace_bytes)
+from rl_fine_tuning_amd.grpo import GRPO_STATIC_SCRATCH_BYTES
+from synth import make_case, make_config
+
+from gpu_cases import dev_matrix, say
+from test_gpu_random_shapes import params
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 1 << 20       # bytes on each side
+PATTERN = 0xA5
+
+
+class Guarded:
+    """A tensor of `shape` and `dtype` with GUARD patterned bytes before and after it."""
+
+    def __init__(self, shape, dtype):
+        n = int(np.prod(shape)) * torch.empty(0, dtype=dtype).element_size()
+        self.n = n
+        self.buf = torch.full((GUARD + n + GUARD,), PATTERN, dtype=torch.uint8, device="cuda")
+        self.t = self.buf[GUARD:GUARD + n].view(dtype).view(shape)
+
+    def intact(self):
+        return bool((self.buf[:GUARD] == PATTERN).all()) and bool((self.buf[GUARD + self.n:] == PATTERN).all())
+
+
+def _inputs(c, dtype):
+    T, V = c.T, c.V
+    d = dict(H=dev_matrix(c.H, dtype), W=dev_matrix(c.W, dtype), targets=torch.from_numpy(c.targets).cuda(),
+             mask=torch.from_numpy(c.mask).cuda(), adv=torch.from_numpy(np.linspace(-1, 1, c.S, dtype=np.float32)).cuda())
+    base = -np.log(V)
+    d["old"] = torch.from_numpy((base + c.noise_old * 30).astype(np.float32)).cuda()
+    d["ref"] = torch.from_numpy((base + c.noise_ref).astype(np.float32)).cuda()
+    return d
+
+
+def _run_all(c, dtype, chunk, *, cap=0.0, keep=False, dW=False, static=True):
+    """Every entry point on one case with guarded outputs and workspace; returns the names of
+    the buffers whose guards changed."""
+    T, D, V, S = c.T, c.D, c.V, c.S
+    d = _inputs(c, dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    code = 0 if dtype == "bf16" else 1
+    bad = []
+
+    def check(name, *gs):
+        for i, g in enumerate(gs):
+            if not g.intact():
+                bad.append(f"{name}[{i}]")
+
+    kw = dict(logit_softcapping=cap)
+    # grpo_logp_fwd
+    ws = Guarded((grpo_workspace_bytes(T, D, V, chunk, code, with_backward=False, logit_softcapping=cap),), torch.uint8)
+    lp, lse = Guarded((T,), torch.float32), Guarded((T,), torch.float32)
+    grpo_logp_fwd(d["H"], d["W"], d["targets"], chunk, out=lp.t, lse=lse.t, workspace=ws.t, **kw)
+    torch.cuda.synchronize()
+    check("logp_fwd", ws, lp, lse)
+    # grpo_logp_bwd
+    ws = Guarded((grpo_workspace_bytes(T, D, V, chunk, code, logit_softcapping=cap, with_dW=dW),), torch.uint8)
+    dH = Guarded((T, D), tdt)
+    dWg = Guarded((V, D), torch.float32) if dW else None
+    grad = (d["old"] - d["ref"]).contiguous()
+    grpo_logp_bwd(d["H"], d["W"], d["targets"], lse.t, grad, chunk, dH=dH.t, dW=dWg.t if dW else None,
+                  workspace=ws.t, **kw)
+    torch.cuda.synchronize()
+    check("logp_bwd", ws, dH, *([dWg] if dW else []))
+    # grpo_loss_fwd_bwd and grpo_ce_loss_fwd_bwd
+    for name in ("loss", "ce"):
+        ws = Guarded((grpo_workspace_bytes(T, D, V, chunk, code, num_seqs=S if name == "loss" else 1,
+                                           logit_softcapping=cap, keep_chunk_logits=keep, with_dW=dW),), torch.uint8)
+        outs = dict(loss=Guarded((1,), torch.float64), logp=Guarded((T,), torch.float32),
+                    token_loss=Guarded((T,), torch.float32), dH=Guarded((T, D), tdt))
+        if dW:
+            outs["dW"] = Guarded((V, D), torch.float32)
+        o = {k: g.t for k, g in outs.items()}
+        if name == "loss":
+            grpo_loss_fwd_bwd(d["H"], d["W"], d["targets"], c.cu, d["old"], d["ref"], d["adv"], chunk, mask=d["mask"],
+                              keep_chunk_logits=keep, workspace=ws.t, **o, **kw)
+        else:
+            grpo_ce_loss_fwd_bwd(d["H"], d["W"], d["targets"], chunk, mask=d["mask"], keep_chunk_logits=keep,
+                                 workspace=ws.t, **o, **kw)
+        torch.cuda.synchronize()
+        check(name, ws, *outs.values())
+    # grpo_loss_fwd_bwd_static (its scratch is the library's own)
+    need = grpo_workspace_bytes(T, D, V, chunk, code, num_seqs=S, logit_softcapping=cap, keep_chunk_logits=keep,
+                                with_dW=dW)
+    if static and need <= GRPO_STATIC_SCRATCH_BYTES:
+        outs = dict(loss=Guarded((1,), torch.float64), logp=Guarded((T,), torch.float32),
+                    token_loss=Guarded((T,), torch.float32), dH=Guarded((T, D), tdt))
+        if dW:
+            outs["dW"] = Guarded((V, D), torch.float32)
+        grpo_loss_fwd_bwd_static(d["H"], d["W"], d["targets"], c.cu, d["old"], d["ref"], d["adv"], chunk,
+                                 mask=d["mask"], keep_chunk_logits=keep, **{k: g.t for k, g in outs.items()}, **kw)
+        torch.cuda.synchronize()
+        check("static", *outs.values())
+    return bad
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_guards_random_shapes(i):
+    p = params(i)
+    c = make_case(9100 + i, D=p["D"], V=p["V"], G=p["G"], lengths=p["lengths"], dtype=p["dtype"], chunk=p["chunk"],
+                  w_std=0.2 if p["cap"] else 0.02)
+    say(f"guards random case {i}: {p} T={c.T}")
+    bad = _run_all(c, p["dtype"], p["chunk"], cap=p["cap"], keep=p["keep"], dW=p["dW"])
+    assert not bad, bad
+
+
+@pytest.mark.parametrize("cfg,keep,dW", [(3, False, False), (3, True, False), (3, False, True), (4, False, False),
+                                         (4, False, True)])
+def test_guards_full_size(cfg, keep, dW):
+    c = make_config(cfg)
+    say(f"guards full size config {cfg}: T={c.T} D={c.D} V={c.V} chunk={c.chunk} keep={keep} dW={dW}")
+    bad = _run_all(c, "bf16", c.chunk, keep=keep, dW=dW, static=False)
+    assert not bad, bad
