@@ -99,3 +99,53 @@ def test_full_size_sampled(cfg, keep):
     assert np.all(np.abs(tl - ell_or) <= LOGP_ATOL * (1 + np.abs(adv[oracle.sequence_of_token(c.cu)])))
     say(f"  logp err {err:.2e}, dH worst row {worst:.2e}, whole {e:.2e}, loss {L:.6e}, "
         f"workspace {ws_bytes / 2**30:.2f} GiB")
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_full_size_dW_sampled_rows(cfg):
+    # dW at full size in the benchmark's chunking (every chunk's bands accumulated in order),
+    # checked on selected vocabulary rows: the first and last row of every 32-tile band, rows of
+    # the last (partial) tile and the tail of V.  Each row of dW is
+    #   dW[v] = sum_t g_t (onehot(y_t)_v - p_t,v) H_t,   p_t,v = exp(z_t,v - lse_t),
+    # computed in fp64 over all T tokens from the GPU's own lse and logp (as the per-row dH
+    # reference does), so it measures the dW path itself.
+    from rl_fine_tuning_amd import grpo_logp_fwd
+    c = make_config(cfg)
+    T, D, V, C = c.T, c.D, c.V, c.chunk
+    say(f"full size dW config {cfg}: T={T} D={D} V={V} chunk={C}")
+    H = dev_matrix(c.H, "bf16")
+    W = dev_matrix(c.W, "bf16")
+    y = torch.from_numpy(c.targets).cuda()
+    logp0, lse = grpo_logp_fwd(H, W, y, C, return_lse=True)
+    old = (logp0.double() + torch.from_numpy(c.noise_old).cuda()).float()
+    ref = (logp0.double() + torch.from_numpy(c.noise_ref).cuda()).float()
+    adv = torch.from_numpy(f32(oracle.group_advantages(c.rewards, c.G))).cuda()
+    got = grpo_loss_fwd_bwd(H, W, y, c.cu, old, ref, adv, C, dW=True)
+    torch.cuda.synchronize()
+    logp = got["logp"].cpu().numpy().astype(np.float64)
+    assert torch.equal(got["logp"], logp0)  # the loss call's logp is the forward's, bit for bit
+    band = 32 * 256
+    vs = set()
+    for b0 in range(0, V, band):
+        vs.update([b0, min(V, b0 + band) - 1])
+    last_tile = (V - 1) // 256 * 256
+    vs.update([last_tile, last_tile + 1, V - 2, V - 1, V // 2])
+    vs = np.array(sorted(vs))
+    s = oracle.sequence_of_token(c.cu)
+    w = oracle.token_weights(c.cu, c.mask)
+    terms = oracle.grpo_token_terms(logp, old.cpu().numpy().astype(np.float64), ref.cpu().numpy().astype(np.float64),
+                                    adv.cpu().numpy().astype(np.float64)[s], 0.2, 0.2, 0.001)
+    g = w * terms["dell"]
+    lse64 = lse.cpu().numpy().astype(np.float64)
+    Wv = oracle.widen(c.W[vs], "bf16")
+    ref_rows = np.zeros((len(vs), D))
+    for t0 in range(0, T, 8192):  # fp64 over row blocks of H
+        Hb = oracle.widen(c.H[t0:t0 + 8192], "bf16")
+        coef = -np.exp(Hb @ Wv.T - lse64[t0:t0 + 8192, None])  # -p_t,v
+        yb = c.targets[t0:t0 + 8192]
+        hit = yb[:, None] == vs[None, :]
+        coef[hit] += 1.0
+        ref_rows += (g[t0:t0 + 8192, None] * coef).T @ Hb
+    dW_rows = got["dW"][torch.from_numpy(vs).cuda()].cpu().numpy().astype(np.float64)
+    worst, whole = check_rows(dW_rows, ref_rows, DH_REL_L2, "dW")
+    say(f"  dW rows {len(vs)}: worst row {worst:.2e}, whole {whole:.2e}")
