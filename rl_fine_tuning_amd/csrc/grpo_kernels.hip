@@ -143,6 +143,7 @@ struct GemmArgs {
   // DH
   const float* g;         // [b_rows]
   const float* zy;        // [b_rows]: target logits (the softcap's W[y] factor)
+  float* zy_out;          // LSE / LSES (bf16): [b_rows] target logits captured from the tile
   float* dw;              // DW: [V, D] fp32, offset to the band's first vocabulary row
   int accumulate;         // DW: add to dw (later chunks) instead of overwriting it
   const int32_t* targets; // [b_rows]
@@ -879,6 +880,20 @@ __device__ __forceinline__ void gemm16_epi(const GemmArgs& g, floatx16 (&acc)[kF
       mx = fmaxf(mx, __shfl_xor(mx, 32));  // finite: row 0 of the tile is below V
       const float zmax = mx * g.lm.zscale;  // zscale > 0, so this is the max of z
       const int tok = row_b0 + 64 * w + 32 * j + col;
+      if (g.zy_out) {
+        // The target logit z[t, y_t] from the same accumulator the max and the sum use: the lane
+        // holding tile row y_t - row_a0 (rows 32 i + 8 q + 4 hi + u) picks it out.  A tile holds a
+        // given token's target with probability 256 / V, so this branch is rare and divergent.
+        const int tloc = tok < g.b_rows ? g.targets[tok] - row_a0 : -1;
+        if (tloc >= 0 && tloc < kTA && ((tloc >> 2) & 1) == hi) {
+          float z = 0.0f;
+#pragma unroll
+          for (int i = 0; i < kFA; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) z = 32 * i + 8 * (r >> 2) + 4 * hi + (r & 3) == tloc ? acc[i][j][r] : z;
+          g.zy_out[tok] = z * g.lm.zscale;
+        }
+      }
       if constexpr (KIND == KIND_LSES) {
         char* P = reinterpret_cast<char*>(g.p);
         const int vpad = g.v_ks * 16 - row_a0;  // uniform; multiple of 16
@@ -1503,7 +1518,9 @@ struct MergeArgs {
   int ntiles;
   int rows;
   int64_t t0;
-  const float* zy;      // [T]
+  const float* zy;      // [T]: target logits (written only for targets in [0, V))
+  const int32_t* targets;  // [T]
+  int V;
   float* lse;           // [T]
   float* logp;          // [T] or NULL
   int mode;               // 0: log-probs only, 1: GRPO terms, 2: cross-entropy terms
@@ -1549,7 +1566,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   if (!valid || lane != 0) return;
   const int64_t t = a.t0 + j;
   const float lse = M + logf(S);
-  const float lp = a.zy[t] - lse;
+  const int y = a.targets[t];
+  const float lp = (y >= 0 && y < a.V ? a.zy[t] : __builtin_nanf("")) - lse;
   a.lse[t] = lse;
   if (a.logp) a.logp[t] = lp;
   if (a.mode == 0) return;
@@ -1845,6 +1863,18 @@ WCopies<T> prepare_w(Launcher& L, const Plan& p, const T* W, char* ws) {
   return c;
 }
 
+// z[t, y_t] for every token by a row dot product (the fp32 path, and the split backward, which
+// runs no logits GEMM).
+template <typename T>
+void launch_target_logits(Launcher& L, const Plan& p, const T* H, const T* W, const int32_t* targets,
+                          const LogitMap& lm, float* zy) {
+  if (p.T == 0) return;
+  L.run(GRPO_K_TARGET_LOGIT, [&] {
+    hipLaunchKernelGGL((target_logit_kernel<T>), dim3(grid1(p.T, 4)), dim3(256), 0, L.stream, H, W, targets,
+                       (int)p.T, (int)p.D, (int)p.V, lm, zy);
+  });
+}
+
 // Arguments shared by the two logits GEMMs of a chunk (W rows x tokens, K = D); Wf is the
 // fragment-major copy of W or nullptr.
 template <typename T>
@@ -1885,10 +1915,8 @@ grpo_status logp_impl(const Plan& p, const grpo_shape* shape, const T* H, const 
   float* pm = reinterpret_cast<float*>(ws + p.off_pm);
   float* ps = reinterpret_cast<float*>(ws + p.off_ps);
   char* Hf = ws + p.off_Hf;
-  L.run(GRPO_K_TARGET_LOGIT, [&] {
-    hipLaunchKernelGGL((target_logit_kernel<T>), dim3(grid1(p.T, 4)), dim3(256), 0, L.stream, H, W, targets,
-                       (int)p.T, (int)p.D, (int)p.V, lm, zy);
-  });
+  // bf16: the logits GEMM captures the target logits in its epilogue; fp32: a row dot product
+  if constexpr (sizeof(T) != 2) launch_target_logits<T>(L, p, H, W, targets, lm, zy);
   const WCopies<T> wc = prepare_w<T>(L, p, W, ws);
   for (int64_t k = 0; k < p.nchunks; ++k) {
     const int64_t t0 = k * p.C;
@@ -1897,6 +1925,10 @@ grpo_status logp_impl(const Plan& p, const grpo_shape* shape, const T* H, const 
     GemmArgs g = logits_args<T>(p, W, wc.Wf, H + t0 * p.D, Hf, rows, lm);
     g.pm = pm;
     g.ps = ps;
+    if constexpr (sizeof(T) == 2) {
+      g.targets = targets + t0;
+      g.zy_out = zy + t0;
+    }
     launch_gemm<T, KIND_LSE>(L, GRPO_K_LOGITS_LSE, g);
     MergeArgs m = {};
     m.pm = pm;
@@ -1905,6 +1937,8 @@ grpo_status logp_impl(const Plan& p, const grpo_shape* shape, const T* H, const 
     m.rows = rows;
     m.t0 = t0;
     m.zy = zy;
+    m.targets = targets;
+    m.V = (int)p.V;
     m.lse = lse;
     m.logp = logp;
     L.run(GRPO_K_MERGE, [&] {
@@ -2108,12 +2142,8 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, int mode, const gr
     hipLaunchKernelGGL(seq_count_kernel, dim3(S), dim3(256), 0, L.stream, cu, mask, cnt);
     hipLaunchKernelGGL(seq_weight_kernel, dim3(1), dim3(256), 0, L.stream, cnt, S, agg, wseq);
   });
-  if (p.T > 0) {
-    L.run(GRPO_K_TARGET_LOGIT, [&] {
-      hipLaunchKernelGGL((target_logit_kernel<T>), dim3(grid1(p.T, 4)), dim3(256), 0, L.stream, H, W, targets,
-                         (int)p.T, (int)p.D, (int)p.V, lm, zy);
-    });
-  }
+  // bf16: the logits GEMM captures the target logits in its epilogue; fp32: a row dot product
+  if constexpr (sizeof(T) != 2) launch_target_logits<T>(L, p, H, W, targets, lm, zy);
   const WCopies<T> wc = prepare_w<T>(L, p, W, ws);
   for (int64_t k = 0; k < p.nchunks; ++k) {
     const int64_t t0 = k * p.C;
@@ -2124,6 +2154,10 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, int mode, const gr
     GemmArgs gl = logits_args<T>(p, W, wc.Wf, Hc, Hf, rows, lm);
     gl.pm = pm;
     gl.ps = ps;
+    if constexpr (sizeof(T) == 2) {
+      gl.targets = targets + t0;
+      gl.zy_out = zy + t0;
+    }
     if constexpr (sizeof(T) == 2) {
       if (keep) {
         gl.p = P;
@@ -2142,6 +2176,8 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, int mode, const gr
     m.rows = rows;
     m.t0 = t0;
     m.zy = zy;
+    m.targets = targets;
+    m.V = (int)p.V;
     m.lse = lse;
     m.logp = logp;
     m.mode = mode;
@@ -2193,12 +2229,8 @@ grpo_status logp_bwd_impl(const Plan& p, const grpo_shape* shape, const T* H, co
   float* part = reinterpret_cast<float*>(ws + p.off_part);
   float* zy = reinterpret_cast<float*>(ws + p.off_zy);
   const int64_t dh_esize = p.dh32 ? 4 : (int64_t)sizeof(T);
-  {  // the target logits: the exact target entry of Q (and the softcap factor there)
-    L.run(GRPO_K_TARGET_LOGIT, [&] {
-      hipLaunchKernelGGL((target_logit_kernel<T>), dim3(grid1(p.T, 4)), dim3(256), 0, L.stream, H, W, targets,
-                         (int)p.T, (int)p.D, (int)p.V, lm, zy);
-    });
-  }
+  // the target logits: the exact target entry of Q (and the softcap factor there)
+  launch_target_logits<T>(L, p, H, W, targets, lm, zy);
   const WCopies<T> wc = prepare_w<T>(L, p, W, ws);
   for (int64_t k = 0; k < p.nchunks; ++k) {
     const int64_t t0 = k * p.C;

@@ -54,5 +54,10 @@ def test_timer_counts_launches():
     torch.cuda.synchronize()
     ms, n, dropped = tm.read("logits_lse")
     assert n == 3 and ms > 0 and dropped == 0
-    assert tm.read("merge")[1] == 3 and tm.read("target_logit")[1] == 1
+    # bf16: the logits GEMM captures the target logits itself; fp32 takes a row dot product
+    assert tm.read("merge")[1] == 3 and tm.read("target_logit")[1] == 0
+    tm.reset()
+    grpo_logp_fwd(dev_matrix(c.H, "bf16").float(), dev_matrix(c.W, "bf16").float(), y, 256, timer=tm)
+    torch.cuda.synchronize()
+    assert tm.read("logits_lse")[1] == 3 and tm.read("target_logit")[1] == 1
     tm.close()
