@@ -114,7 +114,11 @@ __device__ __forceinline__ uint32_t u4get(const uint4& v, int i) {
 __device__ __forceinline__ float tanh_fast(float a) {
   const float e = __builtin_amdgcn_exp2f(2.0f * kLog2e * a);
   const float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
-  return fabsf(a) < 0.015625f ? a * fmaf(-a * a, 1.0f / 3.0f, 1.0f) : t;
+  const float s = a * fmaf(-a * a, 1.0f / 3.0f, 1.0f);  // |a| < 2^-6: keeps tanh's relative precision
+  // Both forms are computed and one is picked by a byte permute (selector bytes 4..7 take the
+  // first operand, 0..3 the second), so the choice stays a per-lane select, never a branch.
+  const uint32_t sel = fabsf(a) < 0.015625f ? 0x07060504u : 0x03020100u;
+  return __uint_as_float(__builtin_amdgcn_perm(__float_as_uint(s), __float_as_uint(t), sel));
 }
 
 struct GemmArgs {
@@ -855,14 +859,15 @@ __device__ __forceinline__ void gemm16_epi(const GemmArgs& g, floatx16 (&acc)[kF
   auto cap_block = [&](int j) {
     if constexpr (kLogits && kCap) {
 #pragma unroll
-      for (int i = 0; i < kFA; ++i)
+      for (int i = 0; i < kFA; ++i) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float x = acc[i][j][r];
           const float t = tanh_fast(x * g.lm.cap_in);
           acc[i][j][r] = x == -INFINITY ? x : t;
         }
-      __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);  // 16 values in flight at a time
+      }
     }
   };
   if constexpr (KIND == KIND_LSE || KIND == KIND_LSES) {
