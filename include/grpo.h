@@ -152,11 +152,17 @@ typedef struct grpo_timer grpo_timer; /* opaque, owned by the caller */
  * tokens (not with dW): the library takes the largest of these layouts that keeps the
  * total within chunk_tokens * V * 4 (grpo_plan_info reports the choice).  With dh_fp32 the
  * probabilities take two bf16 halves (twice the room), and the backward runs in token slices
- * without the copies when nothing else fits. */
+ * without the copies when nothing else fits.  Without room for the whole W^T copy (bf16, no
+ * dh_fp32, no dW, chunks of at least 2048 tokens) the rest of the bound holds one band of it:
+ * each backward pass transposes W band by band of the vocabulary into that room, and the dH
+ * GEMM accumulates over the bands. */
 size_t grpo_workspace_bytes(const grpo_shape* shape, int64_t num_seqs, int with_backward);
 
 /* The workspace layout behind grpo_workspace_bytes for the same arguments (host only, no
- * HIP call): info[0] = 1 if the dH GEMM reads a fragment-major copy of W^T, info[1] = 1 if
+ * HIP call): info[0] = how the dH GEMM reads W^T: 0 transposing W tiles in registers, 1 from a
+ * fragment-major copy made once per call, n >= 2 from n vocabulary bands of that copy made in
+ * each backward pass (consecutive passes walk the bands in opposite orders and reuse the band
+ * that is already in place); info[1] = 1 if
  * the logits GEMMs read a fragment-major copy of W, info[2] = tokens per backward slice
  * (>= the chunk's tokens when the backward of a chunk runs in one pass; 0 without the
  * backward), info[3] = workspace bytes.  GRPO_E_NULL if info is NULL; the shape errors of

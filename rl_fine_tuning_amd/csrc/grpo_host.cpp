@@ -168,13 +168,14 @@ grpo_status make_plan(const grpo_shape* s, int64_t S, bool backward, Plan* out, 
     const int64_t tail = p.nchunks > 0 ? p.T - (p.nchunks - 1) * p.C : 0;
     // dH partials when the backward of a chunk runs over slices of `rows` tokens: the
     // largest over the slices of a full chunk and of the last chunk.
-    auto part_bytes = [&](int64_t rows) {
+    // (always: the banded W^T form accumulates partials even without a split)
+    auto part_bytes = [&](int64_t rows, bool always = false) {
       size_t part = 0;
       for (int64_t n : {p.C, tail}) {
         for (int64_t r0 = 0; r0 < n; r0 += rows) {
           const int64_t sr = n - r0 < rows ? n - r0 : rows;
           const int ks = dh_ksplit(sr, p.D, p.V, p.dtype);
-          if (ks > 1 && (size_t)ks * sr * p.D * 4 > part) part = (size_t)ks * sr * p.D * 4;
+          if ((ks > 1 || always) && (size_t)ks * sr * p.D * 4 > part) part = (size_t)ks * sr * p.D * 4;
         }
       }
       return part;
@@ -205,9 +206,30 @@ grpo_status make_plan(const grpo_shape* s, int64_t S, bool backward, Plan* out, 
         break;
       }
     }
+    // Without room for the whole W^T copy (and neither fp32 dH nor dW), the dH GEMM can still
+    // read W^T fragment-major: band by band of the vocabulary, each band transposed into the
+    // workspace before the GEMM launch that reduces over it, whose fp32 partials accumulate
+    // over the bands.  It pays for its transposes (W read and written in each backward pass)
+    // from chunks of kBandMinRows tokens on.
+    bool bands = false;
+    if (bf16 && !pick.wt && !p.dh32 && !dW && p.nchunks > 0 && p.C >= kBandMinRows) {
+      const size_t used = off + align_up(prob_bytes(pick.rows)) + align_up(part_bytes(pick.rows, true));
+      const size_t ks_bytes = (size_t)cdiv(p.D, kTileA16) * kTileA16 * 16 * 2;  // one k step of the copy
+      if (used < bound) {
+        const int64_t ks_max = (int64_t)((bound - used) / ks_bytes) / 2 * 2;
+        if (ks_max >= kBandMinKs && ks_max < p.ks_v) {
+          const int64_t nb = cdiv(p.ks_v, ks_max);
+          p.wt_band_ks = cdiv(cdiv(p.ks_v, nb), 2) * 2;
+          p.wt_bands = cdiv(p.ks_v, p.wt_band_ks);
+          bands = p.wt_bands >= 2;
+          if (!bands) p.wt_band_ks = p.wt_bands = 0;
+        }
+      }
+    }
     p.bwd_rows = pick.rows;
     p.off_P = take(prob_bytes(pick.rows));
-    p.off_part = take(p.nchunks > 0 ? part_bytes(pick.rows) : 0);
+    p.off_part = take(p.nchunks > 0 ? part_bytes(pick.rows, bands) : 0);
+    if (bands) p.off_WTb = take((size_t)cdiv(p.D, kTileA16) * kTileA16 * (size_t)p.wt_band_ks * 16 * 2);
     if (pick.wt) {
       p.use_wt = true;
       p.off_WT = take(wt);
@@ -247,7 +269,7 @@ grpo_status grpo_plan_info(const grpo_shape* shape, int64_t num_seqs, int with_b
   grpo::Plan p;
   const grpo_status st = grpo::make_plan(shape, num_seqs, with_backward != 0, &p, with_backward == 2);
   if (st != GRPO_OK) return st;
-  info[0] = p.use_wt ? 1 : 0;
+  info[0] = p.use_wt ? 1 : p.wt_bands;
   info[1] = p.use_wf ? 1 : 0;
   info[2] = p.bwd_rows;
   info[3] = (int64_t)p.total;

@@ -149,10 +149,14 @@ struct GemmArgs {
   const float* zy;        // [b_rows]: target logits (the softcap's W[y] factor)
   float* zy_out;          // LSE / LSES (bf16): [b_rows] target logits captured from the tile
   float* dw;              // DW: [V, D] fp32, offset to the band's first vocabulary row
-  int accumulate;         // DW: add to dw (later chunks) instead of overwriting it
+  int accumulate;         // DW: add to dw (later chunks) instead of overwriting it; DHT with part_out:
+                          // add to the partials (the later bands of a banded W^T)
   const int32_t* targets; // [b_rows]
   void* dh;               // [b_rows, D] (ksplit == 1)
-  float* part;            // [ksplit][b_rows][D] (ksplit > 1)
+  float* part;            // [ksplit][b_rows][D] (ksplit > 1, or part_out)
+  int part_out;           // DHT: write the fp32 partials even with ksplit == 1 (banded W^T)
+  int k_base;             // DHT: first k of this launch's reduction (a band's first vocabulary entry)
+  int a_koff;             // bf16 DHT: k steps subtracted from k / 16 to index the A copy (a band's start)
   int D;
   int ksplit;
   int dh_f32;         // DH / DHT unsplit: dH is written as fp32
@@ -419,16 +423,20 @@ struct DmaFragA {
   uint32_t lane_off;  // 16 l
   int w;              // wave index (uniform)
   int wrap;           // k step at which the operand's k index starts again at 0 (0: never)
-  __device__ __forceinline__ void init(const void* Af, int ks_count, int tile, int tid, int wrap_ks = 0) {
+  int koff;           // k steps before the copy's first (a band of W^T)
+  __device__ __forceinline__ void init(const void* Af, int ks_count, int tile, int tid, int wrap_ks = 0,
+                                       int koff_ks = 0) {
     const int64_t bytes = (int64_t)ks_count * kFA * 1024;
     rsrc = make_rsrc(reinterpret_cast<const char*>(Af) + (int64_t)tile * bytes, bytes);
     w = __builtin_amdgcn_readfirstlane(tid >> 6);
     lane_off = (uint32_t)((tid & 63) * 16);
     wrap = wrap_ks;
+    koff = koff_ks;
   }
   __device__ __forceinline__ void issue(char* lds_stage, int k0, int kend) const {
     const uint32_t v = k0 < kend ? lane_off : kOOB;
-    const int ks = (wrap > 0 && (k0 >> 4) >= wrap) ? (k0 >> 4) - wrap : (k0 >> 4);
+    const int kr = (k0 >> 4) - koff;
+    const int ks = (wrap > 0 && kr >= wrap) ? kr - wrap : kr;
     const uint32_t base = (uint32_t)ks * (kFA * 1024);
 #pragma unroll
     for (int j = 0; j < kDmaA; ++j)
@@ -843,7 +851,7 @@ void gemm_kernel(const GemmArgs g) {
 // W read as zero), so the logits epilogues need no masks: they add nothing to the max, their
 // exp is 0, and with a softcap they stay -inf.  Groups of 8 rows (32 i + 8 q + 0..7 of the
 // tile) past the stored width are skipped by uniform scalar tests.
-template <int KIND, bool kSplit, bool kCap, bool kOut32>
+template <int KIND, bool kSplit, bool kCap, bool kOut32, bool kAcc>
 __device__ __forceinline__ void gemm16_epi(const GemmArgs& g, floatx16 (&acc)[kFA][kFBW], int ks, int tile_a,
                                            int tb) {
   const int tid = threadIdx.x;
@@ -1014,9 +1022,19 @@ __device__ __forceinline__ void gemm16_epi(const GemmArgs& g, floatx16 (&acc)[kF
           for (int q = 0; q < 4; ++q) {
             if (__builtin_expect(32 * i + 8 * q >= drem, 0)) continue;
             const int d0 = row_a0 + 32 * i + 8 * q + 4 * hi;
-            const float4 o =
+            float4 o =
                 make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-            if (ok) *reinterpret_cast<float4*>(dst + d0) = o;
+            if (ok) {
+              float4* pp = reinterpret_cast<float4*>(dst + d0);
+              if constexpr (kAcc) {  // a later band of a banded W^T
+                const float4 x = *pp;
+                o.x = x.x + o.x;
+                o.y = x.y + o.y;
+                o.z = x.z + o.z;
+                o.w = x.w + o.w;
+              }
+              *pp = o;
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -1059,10 +1077,11 @@ __device__ __forceinline__ void gemm16_epi(const GemmArgs& g, floatx16 (&acc)[kF
   }
 }
 
-// One kernel holds one tile body: the softcap (kCap), the A operand's layout (kFragA) and a
-// split vocabulary (kSplit, dH) are chosen on the host, so register allocation covers a
-// single main loop and epilogue.
-template <int KIND, bool kSplit, bool kCap, bool kFragA, bool kOut32>
+// One kernel holds one tile body: the softcap (kCap), the A operand's layout (kFragA), a
+// split vocabulary (kSplit, dH: fp32 partials), fp32 dH (kOut32) and partials added to
+// instead of written (kAcc: the later bands of a banded W^T) are chosen on the host, so
+// register allocation covers a single main loop and epilogue.
+template <int KIND, bool kSplit, bool kCap, bool kFragA, bool kOut32, bool kAcc>
 __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int ks, int tile_a, int tb) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1070,7 +1089,7 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
   constexpr bool kTrans = KIND == KIND_DH;  // A transposed in registers
   const int row_a0 = tile_a * kTA;
   const int row_b0 = tb * kTB;
-  const int k_begin = ks * g.k_len;
+  const int k_begin = g.k_base + ks * g.k_len;
   const int k_end = min(g.K, k_begin + g.k_len);
   const int nk = k_end > k_begin ? (k_end - k_begin + kBK16 - 1) / kBK16 : 0;
 
@@ -1104,7 +1123,7 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
                                           typename std::conditional<kFragA, DmaFragA, DmaTileA>::type>::type;
   ATile at;
   if constexpr (kTrans) at.init(A, g.lda, row_a0, tid);
-  else if constexpr (kFragA) at.init(g.a, g.a_ks > 0 ? g.a_ks : g.b_ks, tile_a, tid, g.a_wrap);
+  else if constexpr (kFragA) at.init(g.a, g.a_ks > 0 ? g.a_ks : g.b_ks, tile_a, tid, g.a_wrap, g.a_koff);
   else at.init(A, g.lda, row_a0, g.a_rows, tid);
   auto afr = [&](const char* As, int kk, bf16x8 (&a)[kFA]) {
     if constexpr (kFragA) a_frags_f(As, kk, lane, a);
@@ -1205,10 +1224,10 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
     __builtin_amdgcn_s_barrier();
   }
 
-  gemm16_epi<KIND, kSplit, kCap, kOut32>(g, acc, ks, tile_a, tb);
+  gemm16_epi<KIND, kSplit, kCap, kOut32, kAcc>(g, acc, ks, tile_a, tb);
 }
 
-template <int KIND, bool kSplit, bool kCap, bool kFragA, bool kOut32 = false>
+template <int KIND, bool kSplit, bool kCap, bool kFragA, bool kOut32 = false, bool kAcc = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm16_kernel(const GemmArgs g) {
   __shared__ __attribute__((aligned(16))) char smem[kStagesA * kAStageBytes];
@@ -1219,7 +1238,7 @@ void gemm16_kernel(const GemmArgs g) {
     ks = ta / g.tiles_a_base;
     tile_a = ta - ks * g.tiles_a_base;
   }
-  gemm16_tile<KIND, kSplit, kCap, kFragA, kOut32>(g, smem, ks, tile_a, tb);
+  gemm16_tile<KIND, kSplit, kCap, kFragA, kOut32, kAcc>(g, smem, ks, tile_a, tb);
 }
 
 // Fragment-major copy of `rows` rows of a row-major bf16 matrix [rows, K] (ld = K), rows
@@ -1257,17 +1276,31 @@ __global__ __launch_bounds__(256) void frag_copy_kernel(const __bf16* __restrict
   }
 }
 
+// W [V, D] (rows V of a band) into the fragment-major W^T (rows = hidden units, k = vocabulary,
+// ks_v k steps).  A block takes 256 vocabulary rows x 64 hidden units: each thread reads 8 rows
+// x 8 units (16-byte row pieces, 128 contiguous bytes per 8 lanes), transposes that 8 x 8 block
+// with byte permutes into 8 output units (8 vocabulary entries of one hidden unit), and puts
+// them at their place in the block's 32 KB of output, staged in LDS; the block then writes
+// 16 runs of 2 KB (one k step x the two 32-unit row groups), one contiguous kilobyte per wave
+// instruction.  LDS slot s holds unit s ^ ((s >> 4) & 15) of the image, which spreads both the
+// scattered unit writes and the consecutive reads over the banks.  Vocabulary rows past V and
+// hidden units past D are zeros; k steps at or past ks_v are not written.
 __global__ __launch_bounds__(256) void transpose_w_kernel(const __bf16* __restrict__ W, int V, int D, int ks_v,
                                                           char* __restrict__ WTf) {
-  const int lane = threadIdx.x & 63;
-  const int v0 = blockIdx.x * 256 + (threadIdx.x >> 6) * 64 + 8 * (lane >> 3);
-  const int d0 = blockIdx.y * 64 + 8 * (lane & 7);
-  if (v0 >= 16 * ks_v || d0 >= (D + kTA - 1) / kTA * kTA) return;
+  __shared__ uint4 img[2048];  // [k step 16][row group 2][unit 64]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int vl = (tid >> 6) * 64 + 8 * (lane >> 3);  // block-relative vocabulary row
+  const int dl = 8 * (lane & 7);                       // block-relative hidden unit
+  const int v0 = blockIdx.x * 256 + vl;
+  const int d0 = blockIdx.y * 64 + dl;
+  const bool live = v0 < 16 * ks_v;
   uint4 r[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    r[i] = v0 + i < V && d0 < D ? *reinterpret_cast<const uint4*>(W + (int64_t)(v0 + i) * D + d0)
-                                : make_uint4(0, 0, 0, 0);
+    r[i] = live && v0 + i < V && d0 < D ? *reinterpret_cast<const uint4*>(W + (int64_t)(v0 + i) * D + d0)
+                                        : make_uint4(0, 0, 0, 0);
+  auto slot = [](int u) { return u ^ ((u >> 4) & 15); };
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     uint32_t o[4];
@@ -1276,7 +1309,19 @@ __global__ __launch_bounds__(256) void transpose_w_kernel(const __bf16* __restri
       const uint32_t a = u4get(r[2 * m], j >> 1), b = u4get(r[2 * m + 1], j >> 1);
       o[m] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
     }
-    *reinterpret_cast<uint4*>(WTf + frag_off(d0 + j, v0, ks_v)) = make_uint4(o[0], o[1], o[2], o[3]);
+    const int d = dl + j;
+    const int u = ((vl >> 4) * 2 + (d >> 5)) * 64 + (d & 31) + 32 * ((vl >> 3) & 1);
+    img[slot(u)] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  __syncthreads();
+  const int dt = blockIdx.y >> 2, rg0 = 2 * (blockIdx.y & 3);  // 256-row tile of W^T, first row group
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int u = i * 256 + tid;
+    const int ks = blockIdx.x * 16 + (u >> 7);
+    if (ks >= ks_v) continue;
+    const int64_t frag = ((int64_t)dt * ks_v + ks) * kFB + rg0 + ((u >> 6) & 1);
+    *reinterpret_cast<uint4*>(WTf + frag * 1024 + (u & 63) * 16) = img[slot(u)];
   }
 }
 
@@ -1729,11 +1774,17 @@ __global__ __launch_bounds__(256) void dh_reduce_kernel(const float* __restrict_
   const int y = targets[tok];
   float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   if (gt != 0.0f && y >= 0 && y < V) {
+    // all of the token's partials in flight at once, then summed in split order
+    float4 pk[kMaxKSplit];
+#pragma unroll
+    for (int k = 0; k < kMaxKSplit; ++k)
+      if (k < ksplit) pk[k] = *reinterpret_cast<const float4*>(part + ((int64_t)k * rows + tok) * D + d0);
     float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int k = 0; k < ksplit; ++k) {
-      const float4 p = *reinterpret_cast<const float4*>(part + ((int64_t)k * rows + tok) * D + d0);
-      s[0] += p.x; s[1] += p.y; s[2] += p.z; s[3] += p.w;
-    }
+#pragma unroll
+    for (int k = 0; k < kMaxKSplit; ++k)
+      if (k < ksplit) {
+        s[0] += pk[k].x; s[1] += pk[k].y; s[2] += pk[k].z; s[3] += pk[k].w;
+      }
     const float nc = -gt * dscale;
 #pragma unroll
     for (int u = 0; u < 4; ++u) o[u] = nc * s[u];
@@ -1795,7 +1846,11 @@ template <int KIND>
 void (*gemm16_pick(const GemmArgs& g))(const GemmArgs) {
   if constexpr (KIND == KIND_DH || KIND == KIND_DHT) {
     constexpr bool kFrag = KIND == KIND_DHT;
-    if (g.ksplit > 1) return gemm16_kernel<KIND, true, false, kFrag>;
+    if (g.ksplit > 1 || g.part_out) {
+      if constexpr (kFrag)  // the partials of a banded W^T's later bands are accumulated
+        if (g.accumulate) return gemm16_kernel<KIND, true, false, kFrag, false, true>;
+      return gemm16_kernel<KIND, true, false, kFrag>;
+    }
     return g.dh_f32 ? gemm16_kernel<KIND, false, false, kFrag, true> : gemm16_kernel<KIND, false, false, kFrag>;
   } else if constexpr (KIND == KIND_DW) {
     return gemm16_kernel<KIND, false, false, true>;
@@ -1841,6 +1896,9 @@ template <typename T>
 struct WCopies {
   const T* WT = nullptr;
   const char* Wf = nullptr;
+  char* WTb = nullptr;   // room for one band of W^T (banded form), else nullptr
+  int band_resident = -1;  // the band of W^T now in WTb
+  int64_t passes = 0;      // backward passes so far (their parity sets the band order)
 };
 
 template <typename T>
@@ -1856,6 +1914,7 @@ WCopies<T> prepare_w(Launcher& L, const Plan& p, const T* W, char* ws) {
                            (int)p.ks_v, ws + p.off_WT);
       });
     }
+    if (p.wt_bands >= 2) c.WTb = ws + p.off_WTb;
     if (p.use_wf) {
       c.Wf = ws + p.off_Wf;
       L.run(GRPO_K_W_COPY, [&] {
@@ -1962,7 +2021,7 @@ grpo_status logp_impl(const Plan& p, const grpo_shape* shape, const T* H, const 
 // dH_c: [rows, D] of T, or fp32 when the plan writes fp32 dH for bf16 inputs (the
 // probabilities then as hi + lo pairs, the dH GEMM's reduction over both halves).
 template <typename T>
-void backward_chunk(Launcher& L, const Plan& p, const T* W, const WCopies<T>& wc, const T* Hc, char* Hf, int rows,
+void backward_chunk(Launcher& L, const Plan& p, const T* W, WCopies<T>& wc, const T* Hc, char* Hf, int rows,
                     int64_t k, const float* lse_c, const float* g_c, const int32_t* targets_c, void* dH_c, T* P,
                     float* part, const LogitMap& lm, const float* zy_c, bool probs_ready, float* dW,
                     char* Qt) {
@@ -2040,16 +2099,61 @@ void backward_chunk(Launcher& L, const Plan& p, const T* W, const WCopies<T>& wc
     gd.V = (int)p.V;
     gd.D = (int)p.D;
     gd.ksplit = ksplit;
-    if (wc.WT) launch_gemm<T, KIND_DHT>(L, GRPO_K_DH_GEMM, gd);
-    else launch_gemm<T, KIND_DH>(L, GRPO_K_DH_GEMM, gd);
-    if (ksplit > 1) {
+    bool reduce = ksplit > 1;
+    if constexpr (sizeof(T) == 2) {
+      if (wc.WTb) {
+        // Banded W^T: band by band of the vocabulary, the band's rows of W transposed into the
+        // workspace, then the dH GEMM over the band (split ks_plan ways; a split past the band's
+        // end adds zeros), its fp32 partials written by the first band and accumulated by the
+        // others.  Consecutive passes walk the bands in opposite orders, so each pass after the
+        // first starts on the band that is already in place.
+        const int nb = (int)p.wt_bands;
+        const bool down = (wc.passes & 1) != 0;
+        const int64_t band = p.wt_band_ks * 16;
+        const int64_t dpad = cdiv(p.D, kTileA16) * kTileA16;
+        gd.a = wc.WTb;
+        gd.a_ks = (int)p.wt_band_ks;
+        gd.part_out = 1;
+        gd.ksplit = ks_plan;
+        gd.tiles_a = gd.tiles_a_base * ks_plan;
+        for (int i = 0; i < nb; ++i) {
+          const int b = down ? nb - 1 - i : i;
+          const int64_t v0 = b * band;
+          const int64_t vn = p.V - v0 < band ? p.V - v0 : band;
+          if (b != wc.band_resident) {
+            L.run(GRPO_K_TRANSPOSE_W, [&] {
+              hipLaunchKernelGGL(transpose_w_kernel, dim3(grid1(band, 256), grid1(dpad, 64)), dim3(256), 0, L.stream,
+                                 reinterpret_cast<const __bf16*>(W) + v0 * p.D, (int)vn, (int)p.D,
+                                 (int)p.wt_band_ks, wc.WTb);
+            });
+            wc.band_resident = b;
+          }
+          gd.k_base = (int)v0;
+          gd.K = (int)(v0 + vn);
+          gd.k_len = (int)(cdiv(cdiv(vn, ks_plan), kBK16) * kBK16);
+          gd.a_koff = (int)(v0 / 16);
+          gd.accumulate = i > 0;
+          launch_gemm<T, KIND_DHT>(L, GRPO_K_DH_GEMM, gd);
+        }
+        reduce = true;
+      } else if (wc.WT) {
+        launch_gemm<T, KIND_DHT>(L, GRPO_K_DH_GEMM, gd);
+      } else {
+        launch_gemm<T, KIND_DH>(L, GRPO_K_DH_GEMM, gd);
+      }
+    } else {
+      launch_gemm<T, KIND_DH>(L, GRPO_K_DH_GEMM, gd);
+    }
+    ++wc.passes;
+    if (reduce) {
+      const int nsplit = gd.ksplit;
       L.run(GRPO_K_DH_REDUCE, [&] {
         const dim3 grid(grid1((int64_t)sr * (p.D / 4), 256));
         if (out32)
-          hipLaunchKernelGGL((dh_reduce_kernel<float>), grid, dim3(256), 0, L.stream, part, ksplit, sr, (int)p.D,
+          hipLaunchKernelGGL((dh_reduce_kernel<float>), grid, dim3(256), 0, L.stream, part, nsplit, sr, (int)p.D,
                              (int)p.V, lm.dscale, g_s, targets_s, reinterpret_cast<float*>(dH_s));
         else
-          hipLaunchKernelGGL((dh_reduce_kernel<T>), grid, dim3(256), 0, L.stream, part, ksplit, sr, (int)p.D,
+          hipLaunchKernelGGL((dh_reduce_kernel<T>), grid, dim3(256), 0, L.stream, part, nsplit, sr, (int)p.D,
                              (int)p.V, lm.dscale, g_s, targets_s, reinterpret_cast<T*>(dH_s));
       });
     }
@@ -2149,7 +2253,7 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, int mode, const gr
   });
   // bf16: the logits GEMM captures the target logits in its epilogue; fp32: a row dot product
   if constexpr (sizeof(T) != 2) launch_target_logits<T>(L, p, H, W, targets, lm, zy);
-  const WCopies<T> wc = prepare_w<T>(L, p, W, ws);
+  WCopies<T> wc = prepare_w<T>(L, p, W, ws);
   for (int64_t k = 0; k < p.nchunks; ++k) {
     const int64_t t0 = k * p.C;
     const int rows = (int)(p.T - t0 < p.C ? p.T - t0 : p.C);
@@ -2236,7 +2340,7 @@ grpo_status logp_bwd_impl(const Plan& p, const grpo_shape* shape, const T* H, co
   const int64_t dh_esize = p.dh32 ? 4 : (int64_t)sizeof(T);
   // the target logits: the exact target entry of Q (and the softcap factor there)
   launch_target_logits<T>(L, p, H, W, targets, lm, zy);
-  const WCopies<T> wc = prepare_w<T>(L, p, W, ws);
+  WCopies<T> wc = prepare_w<T>(L, p, W, ws);
   for (int64_t k = 0; k < p.nchunks; ++k) {
     const int64_t t0 = k * p.C;
     const int rows = (int)(p.T - t0 < p.C ? p.T - t0 : p.C);

@@ -19,6 +19,11 @@ constexpr int kTileB16 = 256;
 constexpr int kNumCUs = 256;
 constexpr int kMaxKSplit = 8;
 constexpr size_t kAlign = 256;
+// Banded W^T for the dH GEMM: used for chunks of at least this many tokens (below, the
+// transposes of W in every backward pass cost more than the faster GEMM saves) and bands of
+// at least this many k steps of 16 vocabulary entries.
+constexpr int64_t kBandMinRows = 2048;
+constexpr int64_t kBandMinKs = 64;
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
@@ -43,10 +48,13 @@ struct Plan {
   bool dh32 = false;      // bf16 backward writing fp32 dH: the probabilities as bf16 hi + lo pairs
   int64_t ks_q = 0;       // bf16: k steps per row of the probability buffer (ks_v, or 2 ks_lo with dh32)
   int64_t ks_lo = 0;      // bf16 with dh32: first k step of the lo half (ks_v rounded up to even)
+  int64_t wt_band_ks = 0; // bf16 without room for the whole W^T copy: k steps (vocabulary / 16) per band
+                          // of W^T transposed in each backward pass (even); 0: no bands
+  int64_t wt_bands = 0;   // number of such bands (>= 2 when used)
   bool backward = false;
   size_t off_zy = 0, off_lse = 0, off_pm = 0, off_ps = 0;
   size_t off_g = 0, off_wl = 0, off_seq = 0, off_cu = 0, off_cnt = 0, off_wseq = 0;
-  size_t off_P = 0, off_part = 0, off_Hf = 0, off_WT = 0, off_Wf = 0, off_Qt = 0;
+  size_t off_P = 0, off_part = 0, off_Hf = 0, off_WT = 0, off_Wf = 0, off_Qt = 0, off_WTb = 0;
   size_t total = 0;
 };
 

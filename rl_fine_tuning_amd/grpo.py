@@ -194,7 +194,8 @@ def grpo_plan_info(T, D, V, chunk_tokens, dtype=GRPO_BF16, temperature=1.0, num_
     info = (ctypes.c_int64 * 4)()
     st = lib().grpo_plan_info(ctypes.byref(shape), int(num_seqs), _bwd_mode(with_backward, with_dW), info)
     _check(st, "grpo_plan_info")
-    return dict(w_transposed_copy=bool(info[0]), w_copy=bool(info[1]), backward_slice_tokens=int(info[2]),
+    return dict(w_transposed_copy=int(info[0]) == 1, w_transposed_bands=int(info[0]) if info[0] >= 2 else 0,
+                w_copy=bool(info[1]), backward_slice_tokens=int(info[2]),
                 workspace_bytes=int(info[3]))
 
 

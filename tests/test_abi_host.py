@@ -72,8 +72,13 @@ def test_plan_layouts():
     assert info["w_transposed_copy"] and not info["w_copy"] and info["backward_slice_tokens"] == 8192
     info = B.grpo_plan_info(40960, 1536, 151936, 4096, num_seqs=64)       # both copies, whole chunks
     assert info["w_transposed_copy"] and info["w_copy"] and info["backward_slice_tokens"] == 4096
-    info = B.grpo_plan_info(20480, 4096, 128256, 2048, num_seqs=4)        # no room for either copy
+    info = B.grpo_plan_info(20480, 4096, 128256, 2048, num_seqs=4)        # no room for either copy:
     assert not info["w_transposed_copy"] and not info["w_copy"] and info["backward_slice_tokens"] == 2048
+    assert info["w_transposed_bands"] == 3 and info["workspace_bytes"] <= 2048 * 128256 * 4  # W^T in 3 bands
+    for kw in (dict(with_dW=True), dict(dh_fp32=True)):                    # no bands with dW or fp32 dH,
+        assert B.grpo_plan_info(20480, 4096, 128256, 2048, num_seqs=4, **kw)["w_transposed_bands"] == 0
+    assert B.grpo_plan_info(20480, 4096, 128256, 1024, num_seqs=4)["w_transposed_bands"] == 0  # nor below 2048
+    assert B.grpo_plan_info(2600, 2048, 40000, 2048, num_seqs=2)["w_transposed_bands"] == 2
     info = B.grpo_plan_info(380000, 2880, 201088, 8192, num_seqs=4)
     assert info["w_transposed_copy"] and info["w_copy"] and info["backward_slice_tokens"] == 8192
     # the forward alone keeps the copy of W when it fits; fp32 inputs keep no copies

@@ -116,8 +116,8 @@ def test_guards_random_shapes(i):
     assert not bad, bad
 
 
-@pytest.mark.parametrize("cfg,keep,dW", [(3, False, False), (3, True, False), (3, False, True), (4, False, False),
-                                         (4, False, True)])
+@pytest.mark.parametrize("cfg,keep,dW", [(2, False, False), (2, True, False), (3, False, False), (3, True, False),
+                                         (3, False, True), (4, False, False), (4, False, True)])
 def test_guards_full_size(cfg, keep, dW):
     c = make_config(cfg)
     say(f"guards full size config {cfg}: T={c.T} D={c.D} V={c.V} chunk={c.chunk} keep={keep} dW={dW}")

@@ -180,6 +180,31 @@ def test_dh_gemm_both_operand_paths(V, chunk, expect_wt):
     say(f"  logp err {r['logp_err']:.2e} dH rel {r['dH_rel']:.2e}")
 
 
+@pytest.mark.parametrize("keep", [False, True])
+def test_dh_gemm_banded_wt(keep):
+    # No room for the whole W^T copy (it alone is half of one chunk's fp32 logits here) but
+    # room for half of it: each backward pass transposes W in two vocabulary bands and the dH
+    # GEMM accumulates its fp32 partials over them; the second pass walks the bands the other
+    # way and starts on the band already in place (3 transposes for 2 passes).
+    from rl_fine_tuning_amd import Timer
+    D, V, chunk = 2048, 40000, 2048
+    k = case(37, D=D, V=V, lengths=[1300, 1300], G=2, chunk=chunk, old_std=0.3, ref_std=0.3, mask_frac=0.1,
+             bad_targets=(7,))
+    npass, info = backward_passes(k["T"], D, V, chunk, num_seqs=2, keep=keep)
+    say(f"loss banded W^T keep={keep}: plan {info}, backward passes {npass}")
+    assert info["w_transposed_bands"] == 2 and npass == 2
+    d = to_device(k)
+    tm = Timer(256)
+    got = grpo_loss_fwd_bwd(d["H"], d["W"], d["targets"], k["c"].cu, d["old"], d["ref"], d["adv"], chunk,
+                            temperature=k["tau"], mask=d["mask"], keep_chunk_logits=keep, timer=tm, **k["prm"])
+    torch.cuda.synchronize()
+    assert tm.read("transpose_w")[1] == 3
+    assert tm.read("dh_gemm")[1] == 4 and tm.read("dh_reduce")[1] == 2
+    tm.close()
+    r = check_loss_outputs(k, got)
+    say(f"  logp err {r['logp_err']:.2e} dH rel {r['dH_rel']:.2e}")
+
+
 def test_confident_tokens_dH():
     # Softmax concentrated on the target (p_y near 1): dH = (g/tau)(W[y] - sum p W) is a
     # small difference of large terms; the target entry is formed in fp32 before rounding.

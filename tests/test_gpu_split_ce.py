@@ -27,6 +27,7 @@ def _inputs(seed, D, V, lengths, dtype="bf16", bad=()):
     ("bf16", 256, 10000, [300, 400, 324], 512, 0.7, 1),   # W^T copy, split vocabulary
     ("bf16", 264, 999, [700, 1], 128, 1.0, 0),           # in-register W^T, ragged tail
     ("bf16", 1024, 32000, [1500, 548], 4096, 1.0, 1),    # one chunk, several tiles each way
+    ("bf16", 2048, 40000, [1500, 1100], 2048, 1.0, 3),   # W^T in 2 bands per pass, 2 passes
     ("f32", 68, 333, [90, 40, 70], 50, 0.7, 0),
 ])
 def test_logp_bwd_matches_oracle(dtype, D, V, lengths, chunk, tau, expect_wt):
