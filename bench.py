@@ -390,7 +390,7 @@ def main():
     import torch
 
     from rl_fine_tuning_amd import (Timer, grpo_advantages, grpo_ce_loss_fwd_bwd, grpo_logp_bwd, grpo_logp_fwd,
-                                    grpo_loss_fwd_bwd, grpo_workspace_bytes)
+                                    grpo_loss_fwd_bwd, grpo_workspace_bytes, grpo_plan_info)
     from synth import CONFIGS, make_config
 
     cfg = args.config
@@ -457,6 +457,10 @@ def main():
         "w_copy": V * D * esz + ntv * 256 * ks_d * 32,
         "transpose_w": V * D * esz + -(-D // 256) * 256 * ks_v * 32,
     }
+    bands = grpo_plan_info(T, D, V, C, 0 if case.dtype == "bf16" else 1, num_seqs=S)["w_transposed_bands"]
+    if bands and kernels["transpose_w"]["launches"]:
+        # W^T made band by band in every backward pass: each launch moves one band (V / bands rows)
+        stream_bytes["transpose_w"] *= kernels["transpose_w"]["launches"] / args.steps / bands
     streaming = {}
     for k, b in stream_bytes.items():
         kk = kernels[k]
