@@ -1216,13 +1216,21 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
       }
       __builtin_amdgcn_sched_barrier(0);
     };
-    // four B register buffers rotate, so the loop runs in groups of four stages; the
-    // stages past the end of K read zeros
-    for (int kt = 0; kt < nk; kt += 4) {
+    // four B register buffers rotate, so the loop runs in groups of four stages, then the
+    // remaining one to three (their prefetches past the end of K read zeros)
+    int kt = 0;
+    for (; kt + 4 <= nk; kt += 4) {
       step(kt, bb0, bb3);
       step(kt + 1, bb1, bb0);
       step(kt + 2, bb2, bb1);
       step(kt + 3, bb3, bb2);
+    }
+    if (kt < nk) {
+      step(kt, bb0, bb3);
+      if (kt + 1 < nk) {
+        step(kt + 1, bb1, bb0);
+        if (kt + 2 < nk) step(kt + 2, bb2, bb1);
+      }
     }
     __builtin_amdgcn_s_waitcnt(kWaitAll);
     __builtin_amdgcn_s_barrier();
