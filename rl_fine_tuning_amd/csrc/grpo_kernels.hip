@@ -1216,20 +1216,25 @@ __device__ __forceinline__ void gemm16_tile(const GemmArgs& g, char* smem, int k
       }
       __builtin_amdgcn_sched_barrier(0);
     };
-    // four B register buffers rotate, so the loop runs in groups of four stages, then the
-    // remaining one to three (their prefetches past the end of K read zeros)
+    // four B register buffers rotate, so the loop runs in groups of four stages.  The logits
+    // GEMMs (K = D: tens of stages per tile) then run the remaining one to three as single
+    // steps; the dH and dW GEMMs (thousands of stages per tile, where the extra code costs
+    // registers) run a last padded group whose stages past the end of K read zeros.
+    constexpr bool kExactTail = KIND == KIND_LSE || KIND == KIND_PROBS || KIND == KIND_LSES;
     int kt = 0;
-    for (; kt + 4 <= nk; kt += 4) {
+    for (; kExactTail ? kt + 4 <= nk : kt < nk; kt += 4) {
       step(kt, bb0, bb3);
       step(kt + 1, bb1, bb0);
       step(kt + 2, bb2, bb1);
       step(kt + 3, bb3, bb2);
     }
-    if (kt < nk) {
-      step(kt, bb0, bb3);
-      if (kt + 1 < nk) {
-        step(kt + 1, bb1, bb0);
-        if (kt + 2 < nk) step(kt + 2, bb2, bb1);
+    if constexpr (kExactTail) {
+      if (kt < nk) {
+        step(kt, bb0, bb3);
+        if (kt + 1 < nk) {
+          step(kt + 1, bb1, bb0);
+          if (kt + 2 < nk) step(kt + 2, bb2, bb1);
+        }
       }
     }
     __builtin_amdgcn_s_waitcnt(kWaitAll);
