@@ -142,10 +142,15 @@ typedef enum {
 
 typedef struct grpo_timer grpo_timer; /* opaque, owned by the caller */
 
+/* with_backward flag of grpo_workspace_bytes / grpo_plan_info: the backward reads H from
+ * pinned host memory (grpo_logp_bwd_offload), with 1 (no dW) or 2 (dW). */
+#define GRPO_WS_HOST_H 4
+
 /* Bytes of workspace that grpo_logp_fwd (with_backward = 0), the backward entry points
  * (with_backward = 1) or the backward entry points given a dW output (with_backward = 2)
- * need for this shape and num_seqs sequences.  Returns 0 for an
- * invalid shape.  Bounded by chunk_tokens * V * 4 (one chunk's fp32 logits) plus
+ * need for this shape and num_seqs sequences; 1 | GRPO_WS_HOST_H and 2 | GRPO_WS_HOST_H:
+ * grpo_logp_bwd_offload, whose workspace also holds two buffers of chunk_tokens rows of H.
+ * Returns 0 for an invalid shape or with_backward.  Bounded by chunk_tokens * V * 4 (one chunk's fp32 logits) plus
  * O(T + chunk_tokens * (V / 128 + D)) bytes of per-token state.  For bf16 the workspace
  * may also hold fragment-major copies of W^T (for the dH GEMM) and of W (for the logits
  * GEMMs), about D * V * 2 bytes each, and the backward may run over slices of a chunk's
@@ -165,8 +170,8 @@ size_t grpo_workspace_bytes(const grpo_shape* shape, int64_t num_seqs, int with_
  * that is already in place); info[1] = 1 if
  * the logits GEMMs read a fragment-major copy of W, info[2] = tokens per backward slice
  * (>= the chunk's tokens when the backward of a chunk runs in one pass; 0 without the
- * backward), info[3] = workspace bytes.  GRPO_E_NULL if info is NULL; the shape errors of
- * grpo_workspace_bytes otherwise (info untouched). */
+ * backward), info[3] = workspace bytes.  GRPO_E_NULL if info is NULL, GRPO_E_VALUE for an
+ * invalid with_backward; the shape errors of grpo_workspace_bytes otherwise (info untouched). */
 grpo_status grpo_plan_info(const grpo_shape* shape, int64_t num_seqs, int with_backward, int64_t info[4]);
 
 /* Per-token log-probabilities of the targets ([P4]: chunked hidden-state selective
@@ -260,6 +265,42 @@ grpo_status grpo_loss_fwd_bwd_static(const grpo_shape* shape, const grpo_loss_pa
 grpo_status grpo_logp_bwd(const grpo_shape* shape, const void* H, const void* W, const int32_t* targets,
                           const float* lse, const float* grad_logp, void* dH, float* dW,
                           void* workspace, size_t workspace_bytes, void* stream, grpo_timer* timer);
+
+/* Host offload of the hidden states that the split forward / backward keeps ([P4]
+ * "Auslagern von Aktivierungen fuer Log-Softmax": the activations of the chunked log-softmax
+ * are moved off the GPU outside the model's forward, and the hint there: this pays only when
+ * the hidden states are processed in pieces, as here, chunk by chunk).  grpo_logp_fwd_offload
+ * copies H into pinned host memory while its logits GEMMs run; grpo_logp_bwd_offload reads H
+ * back from there one chunk at a time, so the backward holds two chunks of H on the GPU
+ * instead of all of it.  The copies run on a stream of the offload context, ordered against
+ * `stream` by its events; a context serves one call at a time.
+ *   grpo_offload_create: a copy stream (default priority) and events on the current device;
+ *     *out owned by the caller.  grpo_offload_destroy: waits for the context's copies, then
+ *     releases it (GRPO_E_NULL for NULL). */
+typedef struct grpo_offload grpo_offload; /* opaque, owned by the caller */
+grpo_status grpo_offload_create(grpo_offload** out);
+grpo_status grpo_offload_destroy(grpo_offload* offload);
+
+/* grpo_logp_fwd, and H [T, D] copied to H_host [host, pinned: hipHostMalloc or equivalent,
+ * T * D elements of shape->dtype] on the context's copy stream, which starts after the work
+ * enqueued on `stream` before this call (that produced H) and runs beside the call's GEMMs;
+ * `stream` then waits for the copy, so H_host is complete when the call's work on `stream` is
+ * (H may be freed after that).  GRPO_E_VALUE if H_host is not pinned host memory. */
+grpo_status grpo_logp_fwd_offload(const grpo_shape* shape, const void* H, const void* W,
+                                  const int32_t* targets, float* logp, float* lse, void* H_host,
+                                  void* workspace, size_t workspace_bytes, void* stream,
+                                  grpo_timer* timer, grpo_offload* offload);
+
+/* grpo_logp_bwd with H in pinned host memory: before each chunk's backward its rows are copied
+ * into one of two workspace buffers on the context's copy stream (the next chunk's copy runs
+ * while this chunk's GEMMs read the other buffer); results bitwise equal to grpo_logp_bwd's.
+ *   H_host [host, pinned] [T, D] of shape->dtype; the rest as for grpo_logp_bwd; workspace of
+ *   grpo_workspace_bytes(shape, 1, 1 | GRPO_WS_HOST_H) bytes (2 | GRPO_WS_HOST_H with dW).
+ *   GRPO_E_VALUE if H_host is not pinned host memory. */
+grpo_status grpo_logp_bwd_offload(const grpo_shape* shape, const void* H_host, const void* W,
+                                  const int32_t* targets, const float* lse, const float* grad_logp,
+                                  void* dH, float* dW, void* workspace, size_t workspace_bytes,
+                                  void* stream, grpo_timer* timer, grpo_offload* offload);
 
 /* Chunked cross-entropy, forward and backward ([P2] "Unsloth internals", the fused, chunked
  * cross-entropy: the loss over the vocabulary without the [T, V] logits or their gradient):

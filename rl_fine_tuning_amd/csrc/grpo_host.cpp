@@ -98,7 +98,17 @@ int dh_ksplit(int64_t chunk_rows, int64_t D, int64_t V, int32_t dtype) {
   return best;
 }
 
-grpo_status make_plan(const grpo_shape* s, int64_t S, bool backward, Plan* out, bool dW) {
+bool decode_ws_mode(int with_backward, bool* backward, bool* dW, bool* host_h) {
+  const int base = with_backward & ~GRPO_WS_HOST_H;
+  if (base < 0 || base > 2) return false;
+  *host_h = (with_backward & GRPO_WS_HOST_H) != 0;
+  if (*host_h && base == 0) return false;  // the forward reads H from the device
+  *backward = base != 0;
+  *dW = base == 2;
+  return true;
+}
+
+grpo_status make_plan(const grpo_shape* s, int64_t S, bool backward, Plan* out, bool dW, bool host_h) {
   grpo_status st = validate_shape(s);
   if (st != GRPO_OK) return st;
   if (backward && (S < 1 || S > INT32_MAX - 1)) return GRPO_E_SHAPE;
@@ -133,6 +143,13 @@ grpo_status make_plan(const grpo_shape* s, int64_t S, bool backward, Plan* out, 
     return o;
   };
   const size_t T = (size_t)p.T, C = (size_t)p.C;
+  // backward from host memory: two buffers of one chunk's rows of H (chunk k + 1 is copied into
+  // one while chunk k's GEMMs read the other)
+  p.host_h = backward && host_h;
+  if (p.host_h && p.nchunks > 0) {
+    p.hs_bytes = align_up(C * (size_t)p.D * p.esize);
+    p.off_Hs = take(2 * p.hs_bytes);
+  }
   p.off_zy = take(T * 4);
   p.off_lse = take(T * 4);
   p.off_pm = take((size_t)p.ntiles_v * C * 4);
@@ -260,14 +277,18 @@ extern "C" {
 
 size_t grpo_workspace_bytes(const grpo_shape* shape, int64_t num_seqs, int with_backward) {
   grpo::Plan p;
-  if (grpo::make_plan(shape, num_seqs, with_backward != 0, &p, with_backward == 2) != GRPO_OK) return 0;
+  bool bwd, dW, host_h;
+  if (!grpo::decode_ws_mode(with_backward, &bwd, &dW, &host_h)) return 0;
+  if (grpo::make_plan(shape, num_seqs, bwd, &p, dW, host_h) != GRPO_OK) return 0;
   return p.total;
 }
 
 grpo_status grpo_plan_info(const grpo_shape* shape, int64_t num_seqs, int with_backward, int64_t info[4]) {
   if (!info) return GRPO_E_NULL;
   grpo::Plan p;
-  const grpo_status st = grpo::make_plan(shape, num_seqs, with_backward != 0, &p, with_backward == 2);
+  bool bwd, dW, host_h;
+  if (!grpo::decode_ws_mode(with_backward, &bwd, &dW, &host_h)) return GRPO_E_VALUE;
+  const grpo_status st = grpo::make_plan(shape, num_seqs, bwd, &p, dW, host_h);
   if (st != GRPO_OK) return st;
   info[0] = p.use_wt ? 1 : p.wt_bands;
   info[1] = p.use_wf ? 1 : 0;

@@ -54,6 +54,16 @@ struct grpo_timer {
   std::vector<int32_t> kid;
 };
 
+// Host offload of the hidden states: a copy stream beside the caller's and the events that
+// order the two.
+struct grpo_offload {
+  hipStream_t copy = nullptr;
+  hipEvent_t ev_in = nullptr;     // recorded on the call's stream when the call starts
+  hipEvent_t ev_done = nullptr;   // forward: the copy of H to the host has finished
+  hipEvent_t ev_ready[2] = {};    // backward: staging buffer b holds its chunk
+  hipEvent_t ev_free[2] = {};     // backward: the chunk in staging buffer b has been used
+};
+
 namespace grpo {
 namespace {
 
@@ -1989,8 +1999,17 @@ GemmArgs logits_args(const Plan& p, const T* W, const char* Wf, const T* Hc, con
 
 template <typename T>
 grpo_status logp_impl(const Plan& p, const grpo_shape* shape, const T* H, const T* W, const int32_t* targets,
-                      float* logp, float* lse_out, char* ws, Launcher& L) {
+                      float* logp, float* lse_out, char* ws, Launcher& L, void* H_host = nullptr,
+                      grpo_offload* off = nullptr) {
   const LogitMap lm = make_logit_map(shape);
+  if (off) {
+    // H to the host on the copy stream, after what `stream` did before this call, beside the GEMMs
+    if (hipEventRecord(off->ev_in, L.stream) != hipSuccess ||
+        hipStreamWaitEvent(off->copy, off->ev_in, 0) != hipSuccess ||
+        hipMemcpyAsync(H_host, H, (size_t)p.T * p.D * sizeof(T), hipMemcpyDeviceToHost, off->copy) != hipSuccess ||
+        hipEventRecord(off->ev_done, off->copy) != hipSuccess)
+      return GRPO_E_HIP;
+  }
   float* zy = reinterpret_cast<float*>(ws + p.off_zy);
   float* lse = lse_out ? lse_out : reinterpret_cast<float*>(ws + p.off_lse);
   float* pm = reinterpret_cast<float*>(ws + p.off_pm);
@@ -2026,6 +2045,7 @@ grpo_status logp_impl(const Plan& p, const grpo_shape* shape, const T* H, const 
       hipLaunchKernelGGL(merge_kernel, dim3(grid1(rows, 4)), dim3(256), 0, L.stream, m);
     });
   }
+  if (off && hipStreamWaitEvent(L.stream, off->ev_done, 0) != hipSuccess) return GRPO_E_HIP;
   return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_E_HIP;
 }
 
@@ -2346,26 +2366,49 @@ grpo_status loss_impl(const Plan& p, const grpo_shape* shape, int mode, const gr
 }
 
 // Backward of grpo_logp_fwd: dH = (grad / tau) (W[y] - P W) per chunk, from the forward's lse.
+// With `off` (p.host_h), H is in pinned host memory: chunk k's rows are copied on the copy
+// stream into staging buffer k % 2 of the workspace, after the chunk two before has been used
+// from it, and `stream` waits for that copy; so chunk k + 1's copy runs during chunk k's work.
 template <typename T>
 grpo_status logp_bwd_impl(const Plan& p, const grpo_shape* shape, const T* H, const T* W, const int32_t* targets,
-                          const float* lse, const float* grad, void* dH, float* dW, char* ws, Launcher& L) {
+                          const float* lse, const float* grad, void* dH, float* dW, char* ws, Launcher& L,
+                          grpo_offload* off = nullptr) {
   const LogitMap lm = make_logit_map(shape);
   T* P = reinterpret_cast<T*>(ws + p.off_P);
   char* Hf = ws + p.off_Hf;
   float* part = reinterpret_cast<float*>(ws + p.off_part);
   float* zy = reinterpret_cast<float*>(ws + p.off_zy);
   const int64_t dh_esize = p.dh32 ? 4 : (int64_t)sizeof(T);
-  // the target logits: the exact target entry of Q (and the softcap factor there)
-  launch_target_logits<T>(L, p, H, W, targets, lm, zy);
+  const bool host = off != nullptr;
+  // the target logits: the exact target entry of Q (and the softcap factor there); per chunk
+  // from the staged rows when H is on the host
+  if (!host) launch_target_logits<T>(L, p, H, W, targets, lm, zy);
   WCopies<T> wc = prepare_w<T>(L, p, W, ws);
+  if (host && (hipEventRecord(off->ev_in, L.stream) != hipSuccess ||
+               hipStreamWaitEvent(off->copy, off->ev_in, 0) != hipSuccess))
+    return GRPO_E_HIP;
   for (int64_t k = 0; k < p.nchunks; ++k) {
     const int64_t t0 = k * p.C;
     const int rows = (int)(p.T - t0 < p.C ? p.T - t0 : p.C);
     const T* Hc = H + t0 * p.D;
+    const int b = (int)(k & 1);
+    if (host) {
+      T* stage = reinterpret_cast<T*>(ws + p.off_Hs + b * p.hs_bytes);
+      if ((k >= 2 && hipStreamWaitEvent(off->copy, off->ev_free[b], 0) != hipSuccess) ||
+          hipMemcpyAsync(stage, Hc, (size_t)rows * p.D * sizeof(T), hipMemcpyHostToDevice, off->copy) != hipSuccess ||
+          hipEventRecord(off->ev_ready[b], off->copy) != hipSuccess ||
+          hipStreamWaitEvent(L.stream, off->ev_ready[b], 0) != hipSuccess)
+        return GRPO_E_HIP;
+      Hc = stage;
+      Plan pc = p;  // the chunk's rows only
+      pc.T = rows;
+      launch_target_logits<T>(L, pc, Hc, W, targets + t0, lm, zy + t0);
+    }
     if constexpr (sizeof(T) == 2) enqueue_frag_copy(L, p, Hc, rows, Hf);
     backward_chunk<T>(L, p, W, wc, Hc, Hf, rows, k, lse + t0, grad + t0, targets + t0,
                       reinterpret_cast<char*>(dH) + t0 * p.D * dh_esize, P, part, lm, zy + t0, false, dW,
                       ws + p.off_Qt);
+    if (host && hipEventRecord(off->ev_free[b], L.stream) != hipSuccess) return GRPO_E_HIP;
   }
   return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_E_HIP;
 }
@@ -2523,6 +2566,103 @@ grpo_status grpo_logp_bwd(const grpo_shape* shape, const void* H, const void* W,
                                  dH, dW, ws, L);
   return logp_bwd_impl<float>(p, shape, (const float*)H, (const float*)W, targets, lse, grad_logp, dH,
                               nullptr, ws, L);
+}
+
+grpo_status grpo_offload_create(grpo_offload** out) {
+  if (!out) return GRPO_E_NULL;
+  grpo_offload* o = new grpo_offload();
+  bool ok = hipStreamCreateWithFlags(&o->copy, hipStreamNonBlocking) == hipSuccess;
+  for (hipEvent_t* e : {&o->ev_in, &o->ev_done, &o->ev_ready[0], &o->ev_ready[1], &o->ev_free[0], &o->ev_free[1]})
+    ok = ok && hipEventCreateWithFlags(e, hipEventDisableTiming) == hipSuccess;
+  if (!ok) {
+    grpo_offload_destroy(o);
+    return GRPO_E_HIP;
+  }
+  *out = o;
+  return GRPO_OK;
+}
+
+grpo_status grpo_offload_destroy(grpo_offload* o) {
+  if (!o) return GRPO_E_NULL;
+  if (o->copy) (void)hipStreamSynchronize(o->copy);
+  for (hipEvent_t e : {o->ev_in, o->ev_done, o->ev_ready[0], o->ev_ready[1], o->ev_free[0], o->ev_free[1]})
+    if (e) (void)hipEventDestroy(e);
+  if (o->copy) (void)hipStreamDestroy(o->copy);
+  delete o;
+  return GRPO_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// [T, D] elements of `esize` bytes at p, all in pinned (page-locked) host memory
+bool pinned_host(const void* p, int64_t T, int64_t D, int esize) {
+  if (!p) return false;
+  const char* first = static_cast<const char*>(p);
+  const char* last = first + (T * D * esize > 0 ? T * D * esize - 1 : 0);
+  for (const char* q : {first, last}) {
+    hipPointerAttribute_t a;
+    if (hipPointerGetAttributes(&a, q) != hipSuccess) {
+      (void)hipGetLastError();
+      return false;
+    }
+    if (a.type != hipMemoryTypeHost) return false;
+  }
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+grpo_status grpo_logp_fwd_offload(const grpo_shape* shape, const void* H, const void* W, const int32_t* targets,
+                                  float* logp, float* lse, void* H_host, void* workspace, size_t workspace_bytes,
+                                  void* stream, grpo_timer* timer, grpo_offload* offload) {
+  Plan p;
+  grpo_status st = make_plan(shape, 1, false, &p);
+  if (st != GRPO_OK) return st;
+  if (!W || !offload) return GRPO_E_NULL;
+  if (p.T > 0 && (!H || !targets || !logp || !H_host)) return GRPO_E_NULL;
+  if (!aligned16(H) || !aligned16(W)) return GRPO_E_UNSUPPORTED;
+  if (!ws_ok(p, workspace, workspace_bytes)) return GRPO_E_WORKSPACE;
+  if (p.T == 0) return GRPO_OK;
+  if (!pinned_host(H_host, p.T, p.D, p.esize)) return GRPO_E_VALUE;
+  (void)hipGetLastError();
+  Launcher L{reinterpret_cast<hipStream_t>(stream), timer};
+  char* ws = reinterpret_cast<char*>(workspace);
+  if (p.dtype == GRPO_BF16)
+    return logp_impl<__bf16>(p, shape, (const __bf16*)H, (const __bf16*)W, targets, logp, lse, ws, L, H_host,
+                             offload);
+  return logp_impl<float>(p, shape, (const float*)H, (const float*)W, targets, logp, lse, ws, L, H_host, offload);
+}
+
+grpo_status grpo_logp_bwd_offload(const grpo_shape* shape, const void* H_host, const void* W,
+                                  const int32_t* targets, const float* lse, const float* grad_logp, void* dH,
+                                  float* dW, void* workspace, size_t workspace_bytes, void* stream,
+                                  grpo_timer* timer, grpo_offload* offload) {
+  Plan p;
+  grpo_status st = make_plan(shape, 1, true, &p, dW != nullptr, true);
+  if (st != GRPO_OK) return st;
+  if (!W || !offload) return GRPO_E_NULL;
+  if (p.T > 0 && (!H_host || !targets || !lse || !grad_logp || !dH)) return GRPO_E_NULL;
+  if (!aligned16(H_host) || !aligned16(W) || !aligned16(dH)) return GRPO_E_UNSUPPORTED;
+  if (dW && (shape->dtype != GRPO_BF16 || !aligned16(dW))) return GRPO_E_UNSUPPORTED;
+  if (!ws_ok(p, workspace, workspace_bytes)) return GRPO_E_WORKSPACE;
+  if (p.T == 0 && !dW) return GRPO_OK;
+  if (p.T > 0 && !pinned_host(H_host, p.T, p.D, p.esize)) return GRPO_E_VALUE;
+  (void)hipGetLastError();
+  Launcher L{reinterpret_cast<hipStream_t>(stream), timer};
+  if (p.T == 0) {  // no tokens: the gradient of W is 0
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(1024), dim3(256), 0, L.stream, dW, (int64_t)p.V * p.D);
+    return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_E_HIP;
+  }
+  char* ws = reinterpret_cast<char*>(workspace);
+  if (p.dtype == GRPO_BF16)
+    return logp_bwd_impl<__bf16>(p, shape, (const __bf16*)H_host, (const __bf16*)W, targets, lse, grad_logp, dH,
+                                 dW, ws, L, offload);
+  return logp_bwd_impl<float>(p, shape, (const float*)H_host, (const float*)W, targets, lse, grad_logp, dH,
+                              nullptr, ws, L, offload);
 }
 
 grpo_status grpo_ce_loss_fwd_bwd(const grpo_shape* shape, const void* H, const void* W, const int32_t* targets,

@@ -52,6 +52,9 @@ struct Plan {
                           // of W^T transposed in each backward pass (even); 0: no bands
   int64_t wt_bands = 0;   // number of such bands (>= 2 when used)
   bool backward = false;
+  bool host_h = false;    // backward from hidden states in pinned host memory: chunks staged in the workspace
+  size_t off_Hs = 0;      // host_h: two staging buffers of one chunk's rows of H
+  size_t hs_bytes = 0;    // host_h: bytes of one staging buffer
   size_t off_zy = 0, off_lse = 0, off_pm = 0, off_ps = 0;
   size_t off_g = 0, off_wl = 0, off_seq = 0, off_cu = 0, off_cnt = 0, off_wseq = 0;
   size_t off_P = 0, off_part = 0, off_Hf = 0, off_WT = 0, off_Wf = 0, off_Qt = 0, off_WTb = 0;
@@ -73,7 +76,9 @@ int dh_ksplit(int64_t rows, int64_t D, int64_t V, int32_t dtype);
 grpo_status validate_shape(const grpo_shape* s);
 grpo_status validate_loss_params(const grpo_loss_params* p);
 grpo_status validate_cu(const int32_t* cu, int64_t S, int64_t T);
-grpo_status make_plan(const grpo_shape* s, int64_t S, bool backward, Plan* out, bool dW = false);
+grpo_status make_plan(const grpo_shape* s, int64_t S, bool backward, Plan* out, bool dW = false, bool host_h = false);
+// with_backward of grpo_workspace_bytes / grpo_plan_info: 0, 1, 2, and 1 or 2 plus GRPO_WS_HOST_H
+bool decode_ws_mode(int with_backward, bool* backward, bool* dW, bool* host_h);
 int dh_ksplit(int64_t chunk_rows, int64_t D, int64_t V, int32_t dtype);
 bool aligned16(const void* p);
 

@@ -87,6 +87,14 @@ def lib() -> ctypes.CDLL:
         L.grpo_timer_read.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64),
                                       ctypes.POINTER(i64)]
         L.grpo_timer_read.restype = ctypes.c_int
+        L.grpo_offload_create.argtypes = [ctypes.POINTER(vp)]
+        L.grpo_offload_create.restype = ctypes.c_int
+        L.grpo_offload_destroy.argtypes = [vp]
+        L.grpo_offload_destroy.restype = ctypes.c_int
+        L.grpo_logp_fwd_offload.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+        L.grpo_logp_fwd_offload.restype = ctypes.c_int
+        L.grpo_logp_bwd_offload.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+        L.grpo_logp_bwd_offload.restype = ctypes.c_int
         L.grpo_version.argtypes = []
         L.grpo_version.restype = ctypes.c_char_p
         _lib = L
@@ -173,26 +181,33 @@ def _dh_dtype(H, dh_fp32):
     return torch.float32 if dh_fp32 else H.dtype
 
 
-def _bwd_mode(with_backward, with_dW):
-    return 2 if with_dW else int(bool(with_backward))
+GRPO_WS_HOST_H = 4
+
+
+def _bwd_mode(with_backward, with_dW, host_h=False):
+    mode = 2 if with_dW else int(bool(with_backward))
+    return mode | (GRPO_WS_HOST_H if host_h else 0)
 
 
 def grpo_workspace_bytes(T, D, V, chunk_tokens, dtype=GRPO_BF16, temperature=1.0, num_seqs=1,
                          with_backward=True, logit_softcapping=0.0, keep_chunk_logits=False,
-                         with_dW=False, dh_fp32=False) -> int:
+                         with_dW=False, dh_fp32=False, host_h=False) -> int:
+    """host_h: the workspace of grpo_logp_bwd_offload (H in pinned host memory)."""
     shape = make_shape(T, D, V, chunk_tokens, dtype, temperature, logit_softcapping=logit_softcapping,
                        keep_chunk_logits=keep_chunk_logits, dh_fp32=dh_fp32)
-    return int(lib().grpo_workspace_bytes(ctypes.byref(shape), int(num_seqs), _bwd_mode(with_backward, with_dW)))
+    return int(lib().grpo_workspace_bytes(ctypes.byref(shape), int(num_seqs),
+                                          _bwd_mode(with_backward, with_dW, host_h)))
 
 
 def grpo_plan_info(T, D, V, chunk_tokens, dtype=GRPO_BF16, temperature=1.0, num_seqs=1, with_backward=True,
-                   logit_softcapping=0.0, keep_chunk_logits=False, with_dW=False, dh_fp32=False) -> dict:
+                   logit_softcapping=0.0, keep_chunk_logits=False, with_dW=False, dh_fp32=False,
+                   host_h=False) -> dict:
     """The library's workspace layout for a call: which fragment-major copies of W it keeps,
     the tokens per backward slice and the workspace bytes."""
     shape = make_shape(T, D, V, chunk_tokens, dtype, temperature, logit_softcapping=logit_softcapping,
                        keep_chunk_logits=keep_chunk_logits, dh_fp32=dh_fp32)
     info = (ctypes.c_int64 * 4)()
-    st = lib().grpo_plan_info(ctypes.byref(shape), int(num_seqs), _bwd_mode(with_backward, with_dW), info)
+    st = lib().grpo_plan_info(ctypes.byref(shape), int(num_seqs), _bwd_mode(with_backward, with_dW, host_h), info)
     _check(st, "grpo_plan_info")
     return dict(w_transposed_copy=int(info[0]) == 1, w_transposed_bands=int(info[0]) if info[0] >= 2 else 0,
                 w_copy=bool(info[1]), backward_slice_tokens=int(info[2]),
@@ -301,6 +316,99 @@ def grpo_logp_bwd(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: 
         st = lib().grpo_logp_bwd(ctypes.byref(shape), _ptr(H), _ptr(W), _ptr(targets), _ptr(lse), _ptr(grad_logp),
                                  _ptr(dH), _ptr(dW), _ptr(ws), wsn, _stream(stream), timer.handle if timer else None)
     _check(st, "grpo_logp_bwd")
+    return (dH, dW) if dW is not None else dH
+
+
+class Offload:
+    """A host-offload context (grpo_offload_* in grpo.h): a copy stream and its events on the
+    current device.  One call at a time."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        _check(lib().grpo_offload_create(ctypes.byref(h)), "grpo_offload_create")
+        self.handle = h
+
+    def close(self):
+        if self.handle:
+            lib().grpo_offload_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _pinned(t, name, dtype, shape):
+    """A pinned host tensor (torch.empty(..., pin_memory=True)) of dtype and shape."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.is_cuda or not t.is_pinned():
+        raise ValueError(f"{name} must be a pinned host tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def grpo_logp_fwd_offload(H: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, chunk_tokens: int,
+                          offload: Offload, temperature: float = 1.0, *, H_host=None, logit_scale_multiply=0.0,
+                          logit_scale_divide=0.0, logit_softcapping=0.0, out=None, lse=None, workspace=None,
+                          stream=None, timer: Timer | None = None):
+    """grpo_logp_fwd, and H copied to pinned host memory beside the GEMMs (H_host: a pinned
+    tensor like H, or None to allocate one).  Returns (logp, lse, H_host)."""
+    T, D, V = _hw(H, W, targets)
+    dev = H.device
+    if H_host is None:
+        H_host = torch.empty((T, D), dtype=H.dtype, pin_memory=True)
+    _pinned(H_host, "H_host", H.dtype, (T, D))
+    shape = make_shape(T, D, V, chunk_tokens, _dtype_code(H), temperature, logit_scale_multiply,
+                       logit_scale_divide, logit_softcapping)
+    nbytes = int(lib().grpo_workspace_bytes(ctypes.byref(shape), 1, 0))
+    with _on(stream):
+        ws, wsn = _workspace(nbytes, workspace, dev)
+        logp = _out(out, "out", dev, torch.float32, (T,))
+        lse = _out(lse, "lse", dev, torch.float32, (T,))
+        st = lib().grpo_logp_fwd_offload(ctypes.byref(shape), _ptr(H), _ptr(W), _ptr(targets), _ptr(logp),
+                                         _ptr(lse), _ptr(H_host), _ptr(ws), wsn, _stream(stream),
+                                         timer.handle if timer else None, offload.handle)
+    _check(st, "grpo_logp_fwd_offload")
+    return logp, lse, H_host
+
+
+def grpo_logp_bwd_offload(H_host: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: torch.Tensor,
+                          grad_logp: torch.Tensor, chunk_tokens: int, offload: Offload, temperature: float = 1.0, *,
+                          logit_scale_multiply=0.0, logit_scale_divide=0.0, logit_softcapping=0.0, dh_fp32=False,
+                          dH=None, dW=None, workspace=None, stream=None, timer: Timer | None = None):
+    """grpo_logp_bwd with H in pinned host memory (H_host [T, D], W's dtype): each chunk's rows
+    are brought to the GPU during the previous chunk's work.  Returns dH, or (dH, dW)."""
+    _dev(W, "W", dtype=(torch.bfloat16, torch.float32))
+    if W.dim() != 2:
+        raise ValueError(f"W must be [V, D], got shape {tuple(W.shape)}")
+    V, D = int(W.shape[0]), int(W.shape[1])
+    if not isinstance(H_host, torch.Tensor) or H_host.dim() != 2 or H_host.shape[1] != D:
+        raise ValueError(f"H_host must be a [T, {D}] tensor")
+    T = int(H_host.shape[0])
+    _pinned(H_host, "H_host", W.dtype, (T, D))
+    dev = W.device
+    _dev(targets, "targets", dev, torch.int32, (T,))
+    _dev(lse, "lse", dev, torch.float32, (T,))
+    _dev(grad_logp, "grad_logp", dev, torch.float32, (T,))
+    shape = make_shape(T, D, V, chunk_tokens, _dtype_code(W), temperature, logit_scale_multiply,
+                       logit_scale_divide, logit_softcapping, dh_fp32=dh_fp32)
+    with _on(stream):
+        dW = _want_dW(dW, V, D, dev)
+        nbytes = int(lib().grpo_workspace_bytes(ctypes.byref(shape), 1,
+                                                _bwd_mode(True, dW is not None, host_h=True)))
+        ws, wsn = _workspace(nbytes, workspace, dev)
+        dH = _out(dH, "dH", dev, torch.float32 if dh_fp32 else W.dtype, (T, D))
+        st = lib().grpo_logp_bwd_offload(ctypes.byref(shape), _ptr(H_host), _ptr(W), _ptr(targets), _ptr(lse),
+                                         _ptr(grad_logp), _ptr(dH), _ptr(dW), _ptr(ws), wsn, _stream(stream),
+                                         timer.handle if timer else None, offload.handle)
+    _check(st, "grpo_logp_bwd_offload")
     return (dH, dW) if dW is not None else dH
 
 

@@ -7,6 +7,7 @@ import re
 
 import numpy as np
 import pytest
+import torch
 
 from rl_fine_tuning_amd import grpo as B
 
@@ -374,3 +375,42 @@ def test_dh_fp32_validation_and_plan():
     assert i["backward_slice_tokens"] == 4096 and i["workspace_bytes"] <= 8192 * 151936 * 4
     assert B.grpo_plan_info(110000, 4096, 151936, 8192, num_seqs=2) == \
         B.grpo_plan_info(110000, 4096, 151936, 8192, num_seqs=2, dh_fp32=False)
+
+
+E_NULL, E_VALUE, E_WORKSPACE, E_UNSUPPORTED = 1, 3, 4, 5  # grpo_status in include/grpo.h
+
+
+def test_offload_workspace_and_validation():
+    # grpo_logp_bwd_offload's workspace: the backward's plus two staging buffers of one chunk's
+    # rows of H; the flag goes only with a backward mode
+    for (T, D, V, C, dt) in [(110000, 4096, 151936, 8192, 0), (20480, 4096, 128256, 2048, 0), (700, 68, 333, 50, 1)]:
+        base = B.grpo_workspace_bytes(T, D, V, C, dt)
+        host = B.grpo_workspace_bytes(T, D, V, C, dt, host_h=True)
+        stage = -(-C * D * (2 if dt == 0 else 4) // 256) * 256
+        assert base < host <= base + 2 * stage + 256, (T, D, V, C, base, host)
+        assert host <= C * V * 4 + 64 * T + 64 * 2 ** 20 + 8 * C * (V // 256 + 1) + 32 * C * D
+        assert B.grpo_workspace_bytes(T, D, V, C, dt, with_dW=dt == 0, host_h=True) > 0
+    lib = B.lib()
+    s = shape()
+    for mode in (3, 4, 7, 8, -1):
+        assert lib.grpo_workspace_bytes(ctypes.byref(s), 1, mode) == 0, mode
+        info = (ctypes.c_int64 * 4)()
+        assert lib.grpo_plan_info(ctypes.byref(s), 1, mode, info) == E_VALUE, mode
+    # host-checkable errors come before any HIP call (no GPU needed): a missing context,
+    # misalignment, a short workspace
+    off = ctypes.c_void_p(0)
+    fake, ws = FAKE, ctypes.c_void_p(1 << 21)
+    # grpo_logp_fwd_offload(shape, H, W, targets, logp, lse, H_host, ws, ws_bytes, stream, timer, offload)
+    assert lib.grpo_logp_fwd_offload(ctypes.byref(s), fake, fake, fake, fake, fake, fake, ws, 1 << 30, None, None,
+                                     off) == E_NULL
+    # grpo_logp_bwd_offload(shape, H_host, W, targets, lse, grad, dH, dW, ws, ws_bytes, stream, timer, offload)
+    assert lib.grpo_logp_bwd_offload(ctypes.byref(s), fake, fake, fake, fake, fake, fake, None, ws, 1 << 30, None,
+                                     None, off) == E_NULL
+    ctx = ctypes.c_void_p(1 << 22)  # never dereferenced: the checks below fail first
+    assert lib.grpo_logp_bwd_offload(ctypes.byref(s), ctypes.c_void_p((1 << 20) + 8), fake, fake, fake, fake, fake,
+                                     None, ws, 1 << 30, None, None, ctx) == E_UNSUPPORTED
+    assert lib.grpo_logp_bwd_offload(ctypes.byref(s), fake, fake, fake, fake, fake, fake, None, ws, 16, None, None,
+                                     ctx) == E_WORKSPACE
+    with pytest.raises(ValueError):
+        B.grpo_logp_bwd_offload(torch.zeros(4, 8, dtype=torch.bfloat16), torch.zeros(3, 8, dtype=torch.bfloat16),
+                                     torch.zeros(4, dtype=torch.int32), torch.zeros(4), torch.zeros(4), 4, None)
