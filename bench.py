@@ -389,8 +389,9 @@ def main():
     import numpy as np
     import torch
 
-    from rl_fine_tuning_amd import (Timer, grpo_advantages, grpo_ce_loss_fwd_bwd, grpo_logp_bwd, grpo_logp_fwd,
-                                    grpo_loss_fwd_bwd, grpo_workspace_bytes, grpo_plan_info)
+    from rl_fine_tuning_amd import (Offload, Timer, grpo_advantages, grpo_ce_loss_fwd_bwd, grpo_logp_bwd,
+                                    grpo_logp_bwd_offload, grpo_logp_fwd, grpo_logp_fwd_offload, grpo_loss_fwd_bwd,
+                                    grpo_plan_info, grpo_workspace_bytes)
     from synth import CONFIGS, make_config
 
     cfg = args.config
@@ -558,15 +559,27 @@ def main():
             dw_tf = gemm_flops["dh_gemm"] * calls / (ms_k * 1e-3) / 1e12 if ms_k else None
             tmw.close()
             del dW
+        # the split forward / backward with the hidden states offloaded to pinned host memory in
+        # between (PCIe-inclusive: the forward's copy to the host and the backward's copies back)
+        off = Offload()
+        H_host = torch.empty((T, D), dtype=H.dtype, pin_memory=True)
+        ws_h = torch.empty(grpo_workspace_bytes(T, D, V, C, 0 if case.dtype == "bf16" else 1, host_h=True),
+                           dtype=torch.uint8, device=dev)
+        ms_fo = timed(lambda: grpo_logp_fwd_offload(H, W, targets, C, off, H_host=H_host, out=lp_out, lse=lse,
+                                                    workspace=ws_f))
+        ms_bo = timed(lambda: grpo_logp_bwd_offload(H_host, W, targets, lse, grad, C, off, dH=dH, workspace=ws_h))
+        off.close()
+        del ws_h, H_host
         per = lambda ms, k: {"tokens_per_s": T / (ms * 1e-3), "ms": ms,
                              "mfma_frac": k * T * D * V / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)}
         result["entry_points"] = {"grpo_logp_fwd": per(ms_f, 2.0), "grpo_logp_bwd": per(ms_b, 4.0),
                                   "grpo_ce_loss_fwd_bwd": per(ms_ce, 6.0),
                                   "grpo_loss_fwd_bwd_with_dW": dict(per(ms_dw, 8.0), dw_gemm_tflops=dw_tf)
                                   if ms_dw else None,
-                                  "grpo_advantages": {"us": 1e3 * ms_adv, "sequences": S}}
+                                  "grpo_advantages": {"us": 1e3 * ms_adv, "sequences": S},
+                                  "grpo_logp_fwd_offload": per(ms_fo, 2.0), "grpo_logp_bwd_offload": per(ms_bo, 4.0)}
         log(f"entry points: logp_fwd {ms_f:.1f} ms, logp_bwd {ms_b:.1f} ms, ce {ms_ce:.1f} ms, "
-            f"advantages {1e3 * ms_adv:.1f} us")
+            f"advantages {1e3 * ms_adv:.1f} us, logp_fwd_offload {ms_fo:.1f} ms, logp_bwd_offload {ms_bo:.1f} ms")
     result["provenance"] = provenance(torch)
     others = [int(x) for x in args.other_configs.split(",") if x.strip() and int(x) != cfg]
     if others:
