@@ -276,7 +276,8 @@ grpo_status grpo_logp_bwd(const grpo_shape* shape, const void* H, const void* W,
  * `stream` by its events; a context serves one call at a time.
  *   grpo_offload_create: a copy stream (default priority) and events on the current device;
  *     *out owned by the caller.  grpo_offload_destroy: waits for the context's copies, then
- *     releases it (GRPO_E_NULL for NULL). */
+ *     releases it (GRPO_E_NULL for NULL); the caller first lets the work of the calls that used
+ *     it complete (the events they recorded on their streams belong to the context). */
 typedef struct grpo_offload grpo_offload; /* opaque, owned by the caller */
 grpo_status grpo_offload_create(grpo_offload** out);
 grpo_status grpo_offload_destroy(grpo_offload* offload);
