@@ -504,3 +504,42 @@ def test_dW_cross_entropy_matches_torch_autograd():
     np.testing.assert_allclose(out["dW"], Wt.grad.numpy(), rtol=0, atol=1e-15)
     dH, dW = oracle.logp_backward(H, W, y, out["g"], tau, with_dW=True)
     np.testing.assert_allclose(dW, out["dW"], rtol=0, atol=0)
+
+
+@pytest.mark.parametrize("agg,cap", [("seq_mean", 0.0), ("token_mean", 0.0), ("seq_mean", 2.5)])
+def test_full_grpo_gradient_matches_torch_autograd(agg, cap):
+    # The whole objective written with torch's own operators in float64 on the CPU (softcapped
+    # logits, log_softmax, gather, ratio, clamp, min, k3, the aggregation's weights), and its
+    # autograd gradient with respect to H and W: an independent derivative of every term the
+    # oracle differentiates by hand (the clipped branch, the KL term, temperature, softcap).
+    torch = pytest.importorskip("torch")
+    H, W, y, cu, mask, old, ref, adv, tau = _case(23, lengths=(4, 6, 3, 5), D=7, V=19)
+    eps_lo, eps_hi, beta = 0.15, 0.25, 0.1
+    out = oracle.grpo_loss_and_grad(H, W, y, cu, mask, old, ref, adv, tau, clip_eps_low=eps_lo,
+                                    clip_eps_high=eps_hi, beta=beta, agg=agg, softcap=cap, with_dW=True)
+    rho = np.exp(out["logp"] - old)
+    assert np.any(rho > 1 + eps_hi) and np.any(rho < 1 - eps_lo)  # both clip sides present
+    assert np.all(np.abs(rho - (1 + eps_hi)) > 1e-6) and np.all(np.abs(rho - (1 - eps_lo)) > 1e-6)
+    T, S = len(y), len(cu) - 1
+    seq = np.searchsorted(cu, np.arange(T), side="right") - 1
+    m = torch.tensor(mask, dtype=torch.float64)
+    if agg == "seq_mean":
+        lens = torch.zeros(S, dtype=torch.float64).index_add_(0, torch.tensor(seq), m)
+        w = m / (S * lens[torch.tensor(seq)])
+    else:
+        w = m / m.sum()
+    Ht = torch.tensor(H, requires_grad=True)
+    Wt = torch.tensor(W, requires_grad=True)
+    x = Ht @ Wt.T
+    z = (cap * torch.tanh(x / cap) if cap else x) / tau
+    lp = torch.log_softmax(z, dim=1).gather(1, torch.tensor(y)[:, None])[:, 0]
+    A = torch.tensor(adv)[torch.tensor(seq)]
+    ratio = torch.exp(lp - torch.tensor(old))
+    surr = torch.minimum(ratio * A, torch.clamp(ratio, 1 - eps_lo, 1 + eps_hi) * A)
+    d = torch.tensor(ref) - lp
+    k3 = torch.exp(d) - d - 1
+    L = (w * -(surr - beta * k3)).sum()
+    L.backward()
+    np.testing.assert_allclose(out["loss"], L.item(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(out["dH"], Ht.grad.numpy(), rtol=0, atol=1e-12 * np.abs(Ht.grad.numpy()).max())
+    np.testing.assert_allclose(out["dW"], Wt.grad.numpy(), rtol=0, atol=1e-12 * np.abs(Wt.grad.numpy()).max())
