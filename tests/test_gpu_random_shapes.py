@@ -14,7 +14,7 @@ from gpu_cases import DH_REL_L2, case, check_loss_outputs, check_rows, say, to_d
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 48
+N_CASES = 128
 
 
 def params(i):
