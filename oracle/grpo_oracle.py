@@ -41,7 +41,11 @@ every per-token quantity depends on its own row only.
 All arithmetic is float64.  bf16 inputs are widened exactly from their bit
 patterns, so comparisons measure kernel error and not input rounding.
 
-Parity pins: every function here is pinned in tests/test_oracle_pins.py.
+Parity pins: every function here is pinned in tests/test_oracle_pins.py.  Parity
+unpinned against the pages for the readings they leave open (the std estimator, where
+eps enters, the per-sequence-mean aggregation, and the order of logit scale, softcap
+and temperature): the pages fix none of them, so the pins check each chosen reading's
+own closed forms, limits and derivatives, not a value the pages print.
 """
 from __future__ import annotations
 
