@@ -30,7 +30,7 @@
  *  - Pointers are device pointers unless marked [host].  `stream` is a
  *    hipStream_t passed as void* (NULL = the null stream).  Every call only
  *    enqueues work on `stream`; none synchronizes the host (except the timer
- *    read-out), none allocates device memory, and none keeps a pointer after it
+ *    read-out and grpo_offload_destroy), none allocates device memory, and none keeps a pointer after it
  *    returns ([host] arrays are read during the call, into kernel arguments).
  *    The caller owns every buffer, including the workspace.
  *  - Row-major layouts: H[T, D], W[V, D] (the nn.Linear [out, in] layout), dH[T, D].
@@ -286,7 +286,8 @@ grpo_status grpo_offload_destroy(grpo_offload* offload);
  * T * D elements of shape->dtype] on the context's copy stream, which starts after the work
  * enqueued on `stream` before this call (that produced H) and runs beside the call's GEMMs;
  * `stream` then waits for the copy, so H_host is complete when the call's work on `stream` is
- * (H may be freed after that).  GRPO_E_VALUE if H_host is not pinned host memory. */
+ * (H may be freed after that).  offload: a context of grpo_offload_create (GRPO_E_NULL if
+ * NULL).  GRPO_E_VALUE if H_host is not pinned host memory. */
 grpo_status grpo_logp_fwd_offload(const grpo_shape* shape, const void* H, const void* W,
                                   const int32_t* targets, float* logp, float* lse, void* H_host,
                                   void* workspace, size_t workspace_bytes, void* stream,
@@ -296,8 +297,8 @@ grpo_status grpo_logp_fwd_offload(const grpo_shape* shape, const void* H, const 
  * into one of two workspace buffers on the context's copy stream (the next chunk's copy runs
  * while this chunk's GEMMs read the other buffer); results bitwise equal to grpo_logp_bwd's.
  *   H_host [host, pinned] [T, D] of shape->dtype; the rest as for grpo_logp_bwd; workspace of
- *   grpo_workspace_bytes(shape, 1, 1 | GRPO_WS_HOST_H) bytes (2 | GRPO_WS_HOST_H with dW).
- *   GRPO_E_VALUE if H_host is not pinned host memory. */
+ *   grpo_workspace_bytes(shape, 1, 1 | GRPO_WS_HOST_H) bytes (2 | GRPO_WS_HOST_H with dW);
+ *   offload as for grpo_logp_fwd_offload.  GRPO_E_VALUE if H_host is not pinned host memory. */
 grpo_status grpo_logp_bwd_offload(const grpo_shape* shape, const void* H_host, const void* W,
                                   const int32_t* targets, const float* lse, const float* grad_logp,
                                   void* dH, float* dW, void* workspace, size_t workspace_bytes,
