@@ -30,8 +30,10 @@
  *  - Pointers are device pointers unless marked [host].  `stream` is a
  *    hipStream_t passed as void* (NULL = the null stream).  Every call only
  *    enqueues work on `stream`; none synchronizes the host (except the timer
- *    read-out and grpo_offload_destroy), none allocates device memory, and none keeps a pointer after it
- *    returns ([host] arrays are read during the call, into kernel arguments).
+ *    read-out and grpo_offload_destroy), none allocates device memory, and none keeps a
+ *    pointer after it returns ([host] arrays are read during the call, into kernel
+ *    arguments; the pinned H_host of the offload calls is the exception: the GPU's copies
+ *    read or write it asynchronously, like device memory, so it lives until their work is done).
  *    The caller owns every buffer, including the workspace.
  *  - Row-major layouts: H[T, D], W[V, D] (the nn.Linear [out, in] layout), dH[T, D].
  *    Row t of H predicts targets[t]; the caller applies any causal shift.
